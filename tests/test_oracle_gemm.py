@@ -1,0 +1,104 @@
+"""Pins for the oracle's GEMM references and their per-element bound.
+
+Method passages: "Zenbit" page, *What's inside*, ``zenbit.pallas_nf4`` bullet
+(fused dequant+matmul forward; fused backward forming dL/dX only);
+"bitsandbytes" page, quantized-GEMM paragraph (float32 multiply and output).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _bf16(rng, shape, std=1.0):
+    return O.bf16_bits_to_f32(O.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32)))
+
+
+def test_fwd_and_bwd_against_exact_rationals():
+    rng = np.random.default_rng(0)
+    M, N, K = 3, 5, 64
+    x = _bf16(rng, (M, K))
+    w = _bf16(rng, (N, K), 0.02)
+    dy = _bf16(rng, (M, N))
+    y = O.matmul_fwd(x, w)
+    dx = O.matmul_bwd_dx(dy, w)
+    for i in range(M):
+        for j in range(N):
+            exact = sum(Fraction(float(x[i, k])) * Fraction(float(w[j, k])) for k in range(K))
+            assert abs(Fraction(float(y[i, j])) - exact) <= Fraction(K) * Fraction(2) ** -52 * \
+                sum(abs(Fraction(float(x[i, k])) * Fraction(float(w[j, k]))) for k in range(K))
+    for i in range(M):
+        for k in range(K):
+            exact = sum(Fraction(float(dy[i, j])) * Fraction(float(w[j, k])) for j in range(N))
+            mag = sum(abs(Fraction(float(dy[i, j])) * Fraction(float(w[j, k]))) for j in range(N))
+            assert abs(Fraction(float(dx[i, k])) - exact) <= Fraction(N) * Fraction(2) ** -52 * mag
+
+
+def test_identity_special_cases_are_exact():
+    rng = np.random.default_rng(1)
+    q = O.quantize((rng.standard_normal(256 * 256) * 0.02).astype(np.float32))
+    wh = O.bf16_bits_to_f32(O.dequantize(q)).reshape(256, 256)
+    assert np.array_equal(O.matmul_fwd(np.eye(256, dtype=np.float32), wh), wh.T.astype(np.float64))
+    assert np.array_equal(O.matmul_bwd_dx(np.eye(256, dtype=np.float32), wh), wh.astype(np.float64))
+
+
+def test_bound_accepts_fp32_accumulation_and_rejects_mistakes():
+    rng = np.random.default_rng(2)
+    M, N, K = 16, 96, 4096
+    x = _bf16(rng, (M, K))
+    w = _bf16(rng, (N, K), 0.02)
+    ref = O.matmul_fwd(x, w)
+    bound = O.fwd_bound(x, w)
+    # an fp32 accumulation in a different order passes
+    acc = np.zeros((M, N), np.float32)
+    for k0 in range(0, K, 64):
+        acc += (x[:, k0:k0 + 64] @ w[:, k0:k0 + 64].T).astype(np.float32)
+    assert O.gemm_violations(acc, ref, bound) == 0
+    # a dropped K slice, a sign error, a transposed-operand mistake all fail
+    acc_drop = acc - (x[:, :64] @ w[:, :64].T).astype(np.float32)
+    assert O.gemm_violations(acc_drop, ref, bound) > 0
+    assert O.gemm_violations(-acc, ref, bound) > 0
+    wt = w.reshape(N, 64, K // 64).transpose(0, 2, 1).reshape(N, K)
+    assert O.gemm_violations(O.matmul_fwd(x, wt), ref, bound) > 0
+
+
+def test_bf16_rounded_outputs_would_break_the_bound():
+    """Why the GEMM outputs are fp32: bf16 rounding of Y exceeds 1e-4 * |X||W|."""
+    rng = np.random.default_rng(3)
+    M, N, K = 8, 256, 4096
+    x = _bf16(rng, (M, K))
+    w = _bf16(rng, (N, K), 0.02)
+    ref = O.matmul_fwd(x, w)
+    y_bf16 = O.bf16_bits_to_f32(O.f32_to_bf16_bits(ref.astype(np.float32)))
+    assert O.gemm_violations(y_bf16, ref, O.fwd_bound(x, w)) > 0
+
+
+def test_zero_magnitude_requires_exact_zero():
+    x = np.zeros((2, 64), np.float32)
+    w = np.ones((3, 64), np.float32)
+    ref = O.matmul_fwd(x, w)
+    b = O.fwd_bound(x, w)
+    assert O.gemm_violations(np.zeros((2, 3)), ref, b) == 0
+    assert O.gemm_violations(np.full((2, 3), 1e-30), ref, b) == 6
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_tiny_workload_end_to_end(dq):
+    """The tiny workload through the whole oracle: shapes, sizes, bound self-consistency."""
+    import synth
+    t = synth.tiny()
+    w = t["W"].numpy()
+    q = O.quantize(w, double_quant_on=dq)
+    assert q["packed"].size == 256 * 256 // 2 and q["absmax"].size == 1024
+    if dq:
+        assert q["absmax_q"].size == 1024 and q["scale"].size == 4
+    wh = O.bf16_bits_to_f32(O.dequantize(q)).reshape(256, 256)
+    x = t["X"].float().numpy()
+    dy = t["dY"].float().numpy()
+    y = O.matmul_fwd(x, wh)
+    dx = O.matmul_bwd_dx(dy, wh)
+    assert y.shape == (8, 256) and dx.shape == (8, 256)
+    assert O.gemm_violations(y.astype(np.float32), y, O.fwd_bound(x, wh)) == 0
+    assert O.gemm_violations(dx.astype(np.float32), dx, O.bwd_dx_bound(dy, wh)) == 0
