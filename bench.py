@@ -1,0 +1,282 @@
+"""Benchmark of the NF4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one training-layer pass of the prefill workload (X [4096,4096]
+bf16, weight [11008,4096] bf16 N(0,0.02), dY [4096,11008] bf16 N(0,0.01)):
+NF4 quantization with double quantization of the weight, the fused forward
+Y = X W^T and the fused backward dX = dY W^, all through the C ABI of
+libnf4.so on torch's current stream, inputs and outputs resident in HBM.
+
+``value`` is the step's GEMM throughput, 2 * 2*M*N*K flops per step over the
+step time (quantization included in the time).  The same JSON line carries
+per-kernel timings (HIP events around every launch of the timed steps), the
+dequantizer and the decode-shape forward (M = 1, 4, 16 on a rotating pool of
+64 quantized 4096x4096 weights, replayed from a HIP graph so launch overhead
+does not count), a roofline entry for the dominant kernel and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NF4 dequant-GEMM TFLOP/s + GB/s (fwd, bwd-dX) and % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PF dense)
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+
+
+def wq_bytes(rows, cols):
+    numel = rows * cols
+    nb = -(-numel // 64)
+    return -(-numel // 2) + nb + 4 * (-(-nb // 256)) + 4
+
+
+def time_events(fn, reps, stream=None):
+    """Average milliseconds of ``fn`` over ``reps`` calls between two HIP events."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def bench_prefill(dg, steps, warmup):
+    import synth
+    d = torch.device("cuda:0")
+    M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
+    W = synth.prefill_weight().to(d)
+    X = synth.prefill_x().to(d)
+    dY = synth.prefill_dy().to(d)
+    q = dg.empty_qtensor(N, K, True, d)
+    ws = torch.empty(dg.nf4_sizes(N, K)["workspace_bytes"], dtype=torch.uint8, device=d)
+    Y = torch.empty((M, N), dtype=torch.float32, device=d)
+    dX = torch.empty((M, K), dtype=torch.float32, device=d)
+
+    ops = ("quantize", "fwd", "bwd_dx")
+    ev = {o: [] for o in ops}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            marks[0].record()
+        dg.nf4_quantize(W, out=q, workspace=ws)
+        if record:
+            marks[1].record()
+        dg.nf4_matmul_fwd(X, q, out=Y)
+        if record:
+            marks[2].record()
+        dg.nf4_matmul_bwd_dx(dY, q, out=dX)
+        if record:
+            marks[3].record()
+        return marks
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    rec = [step(True) for _ in range(steps)]
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    for marks in rec:
+        for i, o in enumerate(ops):
+            ev[o].append(marks[i].elapsed_time(marks[i + 1]))
+    per = {o: float(np.mean(v)) for o, v in ev.items()}
+    flop = 2.0 * M * N * K
+    bytes_fwd = M * K * 2 + wq_bytes(N, K) + M * N * 4
+    bytes_bwd = M * N * 2 + wq_bytes(N, K) + M * K * 4
+    bytes_q = N * K * 2 + wq_bytes(N, K)
+    res = {
+        "ms_per_step": ms_step,
+        "tflops_step": 2 * flop / (ms_step * 1e-3) / 1e12,
+        "ops": {
+            "quantize": {"ms": per["quantize"], "GB/s": bytes_q / (per["quantize"] * 1e-3) / 1e9},
+            "fwd": {"ms": per["fwd"], "TFLOP/s": flop / (per["fwd"] * 1e-3) / 1e12,
+                    "GB/s": bytes_fwd / (per["fwd"] * 1e-3) / 1e9},
+            "bwd_dx": {"ms": per["bwd_dx"], "TFLOP/s": flop / (per["bwd_dx"] * 1e-3) / 1e12,
+                       "GB/s": bytes_bwd / (per["bwd_dx"] * 1e-3) / 1e9},
+        },
+        "flop_per_gemm": flop,
+    }
+    for o in ("fwd", "bwd_dx"):
+        res["ops"][o]["frac_mfma"] = res["ops"][o]["TFLOP/s"] / PEAK_BF16_TFLOPS
+    res["ops"]["quantize"]["frac_hbm"] = res["ops"]["quantize"]["GB/s"] / PEAK_HBM_GBPS
+
+    # dequantize (context: the unfused path's first half)
+    Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
+    ms_dq = time_events(lambda: dg.nf4_dequantize(q, out=Wh), 20)
+    bdq = wq_bytes(N, K) + N * K * 2
+    res["ops"]["dequantize"] = {"ms": ms_dq, "GB/s": bdq / (ms_dq * 1e-3) / 1e9,
+                                "frac_hbm": bdq / (ms_dq * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    # the naive dequantize-then-multiply the pages compare against, for context
+    Xf = X
+    ms_naive = time_events(lambda: (dg.nf4_dequantize(q, out=Wh), torch.matmul(Xf, Wh.t())), 10)
+    res["ops"]["naive_dequant_then_matmul_fwd"] = {"ms": ms_naive, "TFLOP/s": flop / (ms_naive * 1e-3) / 1e12}
+    del W, X, dY, Y, dX, Wh, ws
+    return res
+
+
+def bench_decode(dg, pool=64, reps=20):
+    import synth
+    d = torch.device("cuda:0")
+    K, N = synth.DECODE_K, synth.DECODE_N
+    # a pool of 64 independently seeded quantized weights (554 MB, more than
+    # twice the 256 MB last-level cache), rotated call by call
+    qs = []
+    for lo in range(0, pool, 16):
+        for Wp in synth.parallel(synth.decode_weight, range(lo, min(pool, lo + 16))):
+            qs.append(dg.nf4_quantize(Wp.to(d)))
+    torch.cuda.synchronize()
+    out = {}
+    for M in synth.DECODE_MS:
+        X = synth.decode_x(M).to(d)
+        Y = torch.empty((M, N), dtype=torch.float32, device=d)
+        for qq in qs:
+            dg.nf4_matmul_fwd(X, qq, out=Y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for qq in qs:
+                dg.nf4_matmul_fwd(X, qq, out=Y)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_events(g.replay, reps) / pool
+        b = M * K * 2 + wq_bytes(N, K) + M * N * 4
+        out[f"decode_m{M}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
+                               "frac_hbm": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                               "TFLOP/s": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+        del g
+    return out
+
+
+def cpu_baseline(target_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the prefill workload."""
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    K, N = synth.PREFILL_K, synth.PREFILL_N
+    W = synth.prefill_weight()
+    rows_w = 1024                      # quantize 1024 of the 11008 weight rows
+    t = time.perf_counter()
+    qo = O.quantize(W[:rows_w].float().numpy())
+    t_q = time.perf_counter() - t
+    wh = O.bf16_bits_to_f32(O.dequantize(qo)).reshape(rows_w, K)
+    # fwd and bwd on a slice of rows against that weight slice; scale the row count to the time budget
+    X = synth.prefill_x()
+    dY = synth.prefill_dy()
+    m = 64
+    while True:
+        t = time.perf_counter()
+        O.matmul_fwd(X[:m].float().numpy(), wh)
+        O.matmul_bwd_dx(dY[:m, :rows_w].float().numpy(), wh)
+        dt = time.perf_counter() - t
+        if dt > 2.0 or m >= 4096:
+            break
+        m *= 2
+    reps = max(1, int(target_s / max(dt, 1e-3)))
+    t = time.perf_counter()
+    for _ in range(reps):
+        O.matmul_fwd(X[:m].float().numpy(), wh)
+        O.matmul_bwd_dx(dY[:m, :rows_w].float().numpy(), wh)
+    t_g = (time.perf_counter() - t) / reps
+    flop = 2 * (2.0 * m * rows_w * K)
+    # per-weight-element time of the quantizer scaled to the full weight, once per step
+    t_q_full = t_q * (N / rows_w)
+    t_g_full = t_g * (synth.PREFILL_M / m) * (N / rows_w)
+    step_flop = 2 * 2.0 * synth.PREFILL_M * N * K
+    return {
+        "value": step_flop / (t_q_full + t_g_full) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"prefill workload: oracle quantize of {rows_w} of {N} weight rows (1 process), "
+                   f"fp64 fwd+bwd of {m} rows x {rows_w} weight rows (numpy BLAS, {blas_threads} threads), "
+                   f"{reps} reps; scaled linearly to one full step"),
+        "seconds": {"quantize_sample": t_q, "gemm_sample": t_g},
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the NF4 path here is built and timed on a single "
+              "MI355X (no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    import dequant_gemm_amd as dg
+    dg.lib()
+    torch.cuda.synchronize()
+
+    pre = bench_prefill(dg, a.steps, a.warmup)
+    ops = pre["ops"]
+    if not a.no_decode:
+        ops.update(bench_decode(dg))
+    dom = "fwd" if ops["fwd"]["ms"] >= ops["bwd_dx"]["ms"] else "bwd_dx"
+    ach = ops[dom]["TFLOP/s"]
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tflops_step"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill: M=4096 (8x512 tokens), K=4096, N=11008, NF4 blocksize 64 "
+                               "double-quant; step = quantize + fwd + bwd-dX",
+                   "M": 4096, "K": 4096, "N": 11008, "blocksize": 64, "double_quant": True},
+        "roofline": {"kernel": "fwd_large_kernel" if dom == "fwd" else "bwd_dx_kernel",
+                     "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "ops": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                for k, v in ops.items()},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

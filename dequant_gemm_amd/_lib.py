@@ -1,0 +1,238 @@
+"""ctypes binding of libnf4.so (the C ABI in include/nf4.h).
+
+Argument marshalling only: every step of quantization, dequantization and the
+GEMMs runs in the library's HIP kernels.  torch supplies device memory
+(``data_ptr()``) and the current HIP stream; nothing else.  There is no CPU
+fallback: if the library is missing or a call fails, a ``RuntimeError`` is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnf4.so")
+
+NF4_OK = 0
+NF4_F32 = 0
+NF4_BF16 = 1
+BLOCKSIZE = 64
+DQ_GROUP = 256
+
+STATUS_NAMES = {
+    0: "NF4_OK", 1: "NF4_ERR_NULL", 2: "NF4_ERR_SHAPE", 3: "NF4_ERR_BLOCKSIZE", 4: "NF4_ERR_DTYPE",
+    5: "NF4_ERR_ALIGN", 6: "NF4_ERR_WORKSPACE", 7: "NF4_ERR_UNSUPPORTED", 8: "NF4_ERR_HIP",
+}
+
+EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_thresholds", "nf4_sizes", "nf4_quantize",
+           "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx")
+
+
+class QTensorStruct(ctypes.Structure):
+    """Mirror of ``nf4_qtensor``."""
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32), ("double_quant", ctypes.c_int32),
+        ("packed", ctypes.c_void_p), ("absmax", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
+        ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libnf4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dequant_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.nf4_status_string.argtypes = [i32]
+        L.nf4_status_string.restype = ctypes.c_char_p
+        L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+        L.nf4_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
+        L.nf4_sizes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                ctypes.POINTER(i64), ctypes.POINTER(sz)]
+        L.nf4_quantize.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(QTensorStruct), vp, sz, vp, vp]
+        L.nf4_dequantize.argtypes = [ctypes.POINTER(QTensorStruct), vp, i32, vp]
+        L.nf4_matmul_fwd.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
+        L.nf4_matmul_bwd_dx.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
+        for name in EXPORTS[1:]:
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().nf4_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != NF4_OK:
+        raise NF4Error(status, where)
+
+
+def _dtype_enum(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return NF4_F32
+    if dt == torch.bfloat16:
+        return NF4_BF16
+    raise TypeError(f"unsupported dtype {dt}; use torch.float32 or torch.bfloat16")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require_device(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class QTensor:
+    """An NF4-quantized weight [rows, cols] (the QuantState analogue).
+
+    Device buffers: ``packed`` (uint8, ceil(numel/2)); without double
+    quantization ``absmax`` (fp32 per 64-block); with it ``absmax_q`` (int8 per
+    block), ``absmax_scale`` (fp32 per 256 blocks) and ``absmax_mean`` (fp32 [1]).
+    """
+    rows: int
+    cols: int
+    double_quant: bool
+    packed: torch.Tensor
+    absmax: Optional[torch.Tensor] = None
+    absmax_q: Optional[torch.Tensor] = None
+    absmax_scale: Optional[torch.Tensor] = None
+    absmax_mean: Optional[torch.Tensor] = None
+    blocksize: int = BLOCKSIZE
+
+    @property
+    def shape(self):
+        return (self.rows, self.cols)
+
+    @property
+    def device(self):
+        return self.packed.device
+
+    def struct(self) -> QTensorStruct:
+        return QTensorStruct(self.rows, self.cols, self.blocksize, int(self.double_quant),
+                             _ptr(self.packed), _ptr(self.absmax), _ptr(self.absmax_q),
+                             _ptr(self.absmax_scale), _ptr(self.absmax_mean))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.packed, self.absmax, self.absmax_q, self.absmax_scale, self.absmax_mean) if t is not None)
+
+
+# ------------------------------------------------------------------ the C ABI, by name
+
+def nf4_codebook() -> torch.Tensor:
+    out = (ctypes.c_float * 16)()
+    _check(lib().nf4_codebook(out), "nf4_codebook")
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def nf4_thresholds() -> torch.Tensor:
+    out = (ctypes.c_float * 15)()
+    _check(lib().nf4_thresholds(out), "nf4_thresholds")
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def nf4_sizes(rows: int, cols: int, blocksize: int = BLOCKSIZE, double_quant: bool = True) -> dict:
+    pb, nb, ng = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    ws = ctypes.c_size_t()
+    _check(lib().nf4_sizes(rows, cols, blocksize, int(double_quant), ctypes.byref(pb), ctypes.byref(nb),
+                           ctypes.byref(ng), ctypes.byref(ws)), "nf4_sizes")
+    return {"packed_bytes": pb.value, "nblocks": nb.value, "ngroups": ng.value, "workspace_bytes": ws.value}
+
+
+def empty_qtensor(rows: int, cols: int, double_quant: bool = True, device="cuda") -> QTensor:
+    s = nf4_sizes(rows, cols, BLOCKSIZE, double_quant)
+    dev = torch.device(device)
+    q = QTensor(rows, cols, double_quant, torch.empty(s["packed_bytes"], dtype=torch.uint8, device=dev))
+    if double_quant:
+        q.absmax_q = torch.empty(s["nblocks"], dtype=torch.int8, device=dev)
+        q.absmax_scale = torch.empty(s["ngroups"], dtype=torch.float32, device=dev)
+        q.absmax_mean = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        q.absmax = torch.empty(s["nblocks"], dtype=torch.float32, device=dev)
+    return q
+
+
+def nf4_quantize(W: torch.Tensor, blocksize: int = BLOCKSIZE, double_quant: bool = True,
+                 out: Optional[QTensor] = None, workspace: Optional[torch.Tensor] = None,
+                 status: Optional[torch.Tensor] = None) -> QTensor:
+    """NF4-quantize a 2-D bf16/fp32 device tensor (row-major flattening)."""
+    _require_device(W, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows, cols]")
+    rows, cols = W.shape
+    q = out if out is not None else empty_qtensor(rows, cols, double_quant, W.device)
+    s = nf4_sizes(rows, cols, blocksize, double_quant)
+    if workspace is None and s["workspace_bytes"]:
+        workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=W.device)
+    st = q.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nf4_quantize(W.data_ptr(), _dtype_enum(W.dtype), rows, cols, blocksize, int(double_quant),
+                              ctypes.byref(st), _ptr(workspace), ws_bytes, _ptr(status), _stream(W.device)),
+           "nf4_quantize")
+    return q
+
+
+def nf4_dequantize(q: QTensor, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.device)
+    _require_device(out, "out")
+    st = q.struct()
+    _check(lib().nf4_dequantize(ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype), _stream(q.device)),
+           "nf4_dequantize")
+    return out
+
+
+def nf4_matmul_fwd(X: torch.Tensor, q: QTensor, out_dtype: torch.dtype = torch.float32,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X W^T with W^ dequantized on chip.  X: bf16 [M, K] (K = q.cols)."""
+    _require_device(X, "X")
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or X.shape[1] != q.cols:
+        raise ValueError("X must be bf16 [M, q.cols]")
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, q.rows), dtype=out_dtype, device=X.device)
+    _require_device(out, "out")
+    st = q.struct()
+    _check(lib().nf4_matmul_fwd(X.data_ptr(), M, ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype),
+                                _stream(X.device)), "nf4_matmul_fwd")
+    return out
+
+
+def nf4_matmul_bwd_dx(dY: torch.Tensor, q: QTensor, out_dtype: torch.dtype = torch.float32,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX = dY W^ (gradient of Y = X W^T with respect to X).  dY: bf16 [M, N] (N = q.rows)."""
+    _require_device(dY, "dY")
+    if dY.dtype != torch.bfloat16 or dY.dim() != 2 or dY.shape[1] != q.rows:
+        raise ValueError("dY must be bf16 [M, q.rows]")
+    M = dY.shape[0]
+    if out is None:
+        out = torch.empty((M, q.cols), dtype=out_dtype, device=dY.device)
+    _require_device(out, "out")
+    st = q.struct()
+    _check(lib().nf4_matmul_bwd_dx(dY.data_ptr(), M, ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype),
+                                   _stream(dY.device)), "nf4_matmul_bwd_dx")
+    return out

@@ -1,0 +1,170 @@
+// nf4_api.hip -- the C ABI declared in include/nf4.h: argument validation,
+// buffer-size arithmetic and kernel dispatch.  Validation touches no HIP API,
+// so every error path can be exercised on a machine without a GPU.
+#include "../../include/nf4.h"
+#include "nf4_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == NF4_F32 || d == NF4_BF16; }
+
+int check_shape(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return NF4_ERR_SHAPE;
+  if (rows > NF4_MAX_NUMEL / cols) return NF4_ERR_SHAPE;
+  return NF4_OK;
+}
+
+int64_t nblocks_of(int64_t numel) { return (numel + NF4_BLOCKSIZE - 1) / NF4_BLOCKSIZE; }
+int64_t ngroups_of(int64_t nblocks) { return (nblocks + NF4_DQ_GROUP - 1) / NF4_DQ_GROUP; }
+
+// Checks a quantized tensor descriptor and its buffers.
+int check_qtensor(const nf4_qtensor *q) {
+  if (!q) return NF4_ERR_NULL;
+  if (q->blocksize != NF4_BLOCKSIZE) return NF4_ERR_BLOCKSIZE;
+  int st = check_shape(q->rows, q->cols);
+  if (st) return st;
+  if (q->double_quant != 0 && q->double_quant != 1) return NF4_ERR_UNSUPPORTED;
+  if (!q->packed) return NF4_ERR_NULL;
+  if (!aligned16(q->packed)) return NF4_ERR_ALIGN;
+  if (q->double_quant) {
+    if (!q->absmax_q || !q->absmax_scale || !q->absmax_mean) return NF4_ERR_NULL;
+    if (!aligned16(q->absmax_q) || !aligned16(q->absmax_scale) || !aligned16(q->absmax_mean))
+      return NF4_ERR_ALIGN;
+  } else {
+    if (!q->absmax) return NF4_ERR_NULL;
+    if (!aligned16(q->absmax)) return NF4_ERR_ALIGN;
+  }
+  return NF4_OK;
+}
+
+nf4::AbsmaxSrc absmax_src(const nf4_qtensor *q) {
+  nf4::AbsmaxSrc s;
+  s.absmax = q->absmax;
+  s.q = q->absmax_q;
+  s.scale = q->absmax_scale;
+  s.mean = q->absmax_mean;
+  s.dq = q->double_quant;
+  return s;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *nf4_status_string(int status) {
+  switch (status) {
+    case NF4_OK: return "ok";
+    case NF4_ERR_NULL: return "a required pointer is NULL";
+    case NF4_ERR_SHAPE: return "a size is out of range or does not match";
+    case NF4_ERR_BLOCKSIZE: return "blocksize must be 64";
+    case NF4_ERR_DTYPE: return "unknown dtype";
+    case NF4_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case NF4_ERR_WORKSPACE: return "workspace too small";
+    case NF4_ERR_UNSUPPORTED: return "unsupported (e.g. GEMM needs cols % 64 == 0)";
+    case NF4_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int nf4_codebook(float *levels16) {
+  if (!levels16) return NF4_ERR_NULL;
+  for (int i = 0; i < 16; ++i) levels16[i] = nf4::level(i);
+  return NF4_OK;
+}
+
+int nf4_thresholds(float *thresholds15) {
+  if (!thresholds15) return NF4_ERR_NULL;
+  for (int i = 0; i < 15; ++i) thresholds15[i] = nf4::threshold(i);
+  return NF4_OK;
+}
+
+int nf4_sizes(int64_t rows, int64_t cols, int blocksize, int double_quant, int64_t *packed_bytes,
+              int64_t *nblocks, int64_t *ngroups, size_t *workspace_bytes) {
+  if (blocksize != NF4_BLOCKSIZE) return NF4_ERR_BLOCKSIZE;
+  int st = check_shape(rows, cols);
+  if (st) return st;
+  if (double_quant != 0 && double_quant != 1) return NF4_ERR_UNSUPPORTED;
+  const int64_t numel = rows * cols;
+  const int64_t nb = nblocks_of(numel);
+  if (packed_bytes) *packed_bytes = (numel + 1) / 2;
+  if (nblocks) *nblocks = nb;
+  if (ngroups) *ngroups = ngroups_of(nb);
+  if (workspace_bytes) *workspace_bytes = double_quant ? nf4::quant_workspace_bytes(nb) : 0;
+  return NF4_OK;
+}
+
+int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blocksize,
+                 int double_quant, const nf4_qtensor *out, void *workspace, size_t workspace_bytes,
+                 uint32_t *d_status, void *stream) {
+  if (blocksize != NF4_BLOCKSIZE) return NF4_ERR_BLOCKSIZE;
+  if (!W || !out) return NF4_ERR_NULL;
+  if (!valid_dtype(w_dtype)) return NF4_ERR_DTYPE;
+  int st = check_shape(rows, cols);
+  if (st) return st;
+  if (double_quant != 0 && double_quant != 1) return NF4_ERR_UNSUPPORTED;
+  if (!aligned16(W)) return NF4_ERR_ALIGN;
+  st = check_qtensor(out);
+  if (st) return st;
+  if (out->rows != rows || out->cols != cols || out->double_quant != double_quant) return NF4_ERR_SHAPE;
+  if (d_status && !aligned16(d_status)) return NF4_ERR_ALIGN;
+  const int64_t numel = rows * cols;
+  const int64_t nb = nblocks_of(numel);
+  unsigned long long *buckets = nullptr;
+  float *absmax = out->absmax;
+  if (double_quant) {
+    const size_t need = nf4::quant_workspace_bytes(nb);
+    if (workspace_bytes < need) return NF4_ERR_WORKSPACE;
+    if (!workspace) return NF4_ERR_NULL;
+    if (!aligned16(workspace)) return NF4_ERR_ALIGN;
+    buckets = reinterpret_cast<unsigned long long *>(workspace);
+    absmax = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + nf4::absmax_ws_offset());
+  }
+  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, out->packed, absmax, buckets,
+                                         d_status, double_quant, out->absmax_q, out->absmax_scale,
+                                         out->absmax_mean, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int nf4_dequantize(const nf4_qtensor *q, void *out, int out_dtype, void *stream) {
+  int st = check_qtensor(q);
+  if (st) return st;
+  if (!out) return NF4_ERR_NULL;
+  if (!valid_dtype(out_dtype)) return NF4_ERR_DTYPE;
+  if (!aligned16(out)) return NF4_ERR_ALIGN;
+  return hip_status(nf4::launch_dequantize(q->packed, absmax_src(q), q->rows * q->cols, out,
+                                           out_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+static int check_gemm(const void *A, int64_t M, const nf4_qtensor *q, void *C, int c_dtype) {
+  int st = check_qtensor(q);
+  if (st) return st;
+  if (M < 0 || M > kMaxDim) return NF4_ERR_SHAPE;
+  if (!valid_dtype(c_dtype)) return NF4_ERR_DTYPE;
+  if (q->cols % NF4_BLOCKSIZE != 0) return NF4_ERR_UNSUPPORTED;
+  if (M == 0) return NF4_OK;
+  if (!A || !C) return NF4_ERR_NULL;
+  if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+int nf4_matmul_fwd(const void *X, int64_t M, const nf4_qtensor *q, void *Y, int y_dtype, void *stream) {
+  int st = check_gemm(X, M, q, Y, y_dtype);
+  if (st || M == 0) return st;
+  return hip_status(nf4::launch_fwd(X, M, q->rows, q->cols, q->packed, absmax_src(q), Y,
+                                    y_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int nf4_matmul_bwd_dx(const void *dY, int64_t M, const nf4_qtensor *q, void *dX, int dx_dtype,
+                      void *stream) {
+  int st = check_gemm(dY, M, q, dX, dx_dtype);
+  if (st || M == 0) return st;
+  return hip_status(nf4::launch_bwd_dx(dY, M, q->rows, q->cols, q->packed, absmax_src(q), dX,
+                                       dx_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// nf4_common.h -- device-side constants and helpers shared by the libnf4 kernels.
+//
+// NF4 levels: "bitsandbytes" page, NF4 data-type paragraph (16 levels from the
+// inverse normal CDF, denser near zero).  The values are QLoRA's asymmetric
+// construction (8 positive and 7 negative standard-normal quantiles, offset
+// 0.9677083, plus 0, normalised by the largest) rounded once to fp32; they are
+// stored here as bit patterns.  The decision thresholds are derived from the
+// levels: t_i is the smallest fp32 strictly above the midpoint of levels i and
+// i+1, so code(n) = #{i : n >= t_i} is the nearest level with ties going to
+// the lower index.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBlock = 64;     // weights per absmax block
+constexpr int kGroup = 256;    // absmax values per double-quantization scale
+
+constexpr uint32_t kLevelBits[16] = {
+    0xbf800000u, 0xbf3239b3u, 0xbf066b30u, 0xbeca32a0u, 0xbe91a24cu, 0xbe3d353fu,
+    0xbdba786bu, 0x00000000u, 0x3da2fb03u, 0x3e24cae1u, 0x3e7c04dcu, 0x3ead0338u,
+    0x3ee1a4b7u, 0x3f1007aau, 0x3f3913b1u, 0x3f800000u};
+
+constexpr uint32_t kThresholdBits[15] = {
+    0xbf591cd9u, 0xbf1c5271u, 0xbeeb847fu, 0xbeadea75u, 0xbe703cebu, 0xbe0d38bau,
+    0xbd3a786au, 0x3d22fb04u, 0x3df64863u, 0x3e5067dfu, 0x3e9582d4u, 0x3ec753f8u,
+    0x3f006d03u, 0x3f248daeu, 0x3f5c89d9u};
+
+__host__ __device__ constexpr float level(int i) { return __builtin_bit_cast(float, kLevelBits[i]); }
+__host__ __device__ constexpr float threshold(int i) { return __builtin_bit_cast(float, kThresholdBits[i]); }
+
+// ------------------------------------------------------------------ small helpers
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  // Byte permute of the 8-byte value {hi, lo}: selector bytes 0-3 pick bytes of
+  // `lo`, 4-7 bytes of `hi`, 12 gives 0x00 and 13 or more gives 0xFF.
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b) {
+  return (mask & a) | (~mask & b);
+}
+
+// Two fp32 values rounded to bf16 (nearest-even), packed low then high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Dequantized block absmax: a^ = fp32(fp32(q * s) + mu) with double
+// quantization ("bitsandbytes" page, double-quantization paragraph: the scale
+// factors are dequantized first), else the stored fp32 absmax.
+struct AbsmaxSrc {
+  const float *absmax;        // fp32 per block (no double quantization)
+  const int8_t *q;            // int8 per block
+  const float *scale;         // fp32 per group of 256 blocks
+  const float *mean;          // one fp32
+  int dq;
+};
+
+__device__ __forceinline__ float block_ahat(const AbsmaxSrc &s, int64_t blk, float mu) {
+  if (!s.dq) return s.absmax[blk];
+  float qs = __fmul_rn((float)s.q[blk], s.scale[blk >> 8]);
+  return __fadd_rn(qs, mu);
+}
+
+// ------------------------------------------------------------------ register LUT dequant
+//
+// For one block, the 16 possible dequantized values bf16(level_i * a^) are
+// computed once and held as byte planes: lo[q] holds the low bytes of entries
+// 4q..4q+3, hi[q] the high bytes.  A byte-permute then looks up four codes at
+// a time; bit 3 of each code picks the upper or lower half of the table.
+
+struct Lut {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+__device__ __forceinline__ Lut make_lut(float ahat) {
+  uint32_t p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    p[j] = pack_bf16x2(__fmul_rn(level(2 * j), ahat), __fmul_rn(level(2 * j + 1), ahat));
+  Lut t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = perm(p[2 * q + 1], p[2 * q], 0x06040200u);
+    t.hi[q] = perm(p[2 * q + 1], p[2 * q], 0x07050301u);
+  }
+  return t;
+}
+
+// Four codes (one per byte of `sel`, values 0..15) -> low and high bytes of
+// their bf16 values.
+__device__ __forceinline__ void lut_lookup4(uint32_t sel, const Lut &t, uint32_t &lo, uint32_t &hi) {
+  const uint32_t s7 = sel & 0x07070707u;
+  const uint32_t upper = perm(0u, 0u, sel + 0x05050505u);  // 0xFF in bytes whose code >= 8
+  lo = bitsel(upper, perm(t.lo[3], t.lo[2], s7), perm(t.lo[1], t.lo[0], s7));
+  hi = bitsel(upper, perm(t.hi[3], t.hi[2], s7), perm(t.hi[1], t.hi[0], s7));
+}
+
+// Eight packed codes (element 2j in the low nibble of byte j) -> eight bf16
+// values in element order, as four bf16x2 words.
+__device__ __forceinline__ void dequant8(uint32_t d, const Lut &t, uint32_t out[4]) {
+  const uint32_t even = d & 0x0f0f0f0fu;          // codes of elements 0, 2, 4, 6
+  const uint32_t odd = (d >> 4) & 0x0f0f0f0fu;    // codes of elements 1, 3, 5, 7
+  const uint32_t sa = perm(odd, even, 0x05010400u);  // codes 0, 1, 2, 3
+  const uint32_t sb = perm(odd, even, 0x07030602u);  // codes 4, 5, 6, 7
+  uint32_t lo, hi;
+  lut_lookup4(sa, t, lo, hi);
+  out[0] = perm(hi, lo, 0x05010400u);
+  out[1] = perm(hi, lo, 0x07030602u);
+  lut_lookup4(sb, t, lo, hi);
+  out[2] = perm(hi, lo, 0x05010400u);
+  out[3] = perm(hi, lo, 0x07030602u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t w[4]) {
+  uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace nf4

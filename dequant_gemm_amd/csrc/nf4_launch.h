@@ -1,0 +1,35 @@
+// nf4_launch.h -- host-side launchers implemented by the kernel sources and
+// called by the C ABI in nf4_api.hip.  All arguments are validated by the
+// caller; launchers only configure grids and enqueue on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4_common.h"
+
+namespace nf4 {
+
+// Workspace layout for quantization with double quantization.
+constexpr size_t kBucketBytes = 256 * sizeof(unsigned long long);
+inline size_t absmax_ws_offset() { return kBucketBytes; }
+inline size_t quant_workspace_bytes(int64_t nblocks) {
+  size_t b = kBucketBytes + (size_t)nblocks * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t *packed,
+                           float *absmax_out, unsigned long long *buckets, uint32_t *status,
+                           int dq, int8_t *q_out, float *scale_out, float *mean_out,
+                           hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t *packed, const AbsmaxSrc &src, int64_t numel,
+                             void *out, int out_is_bf16, hipStream_t stream);
+
+hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
+                      const AbsmaxSrc &src, void *y, int y_is_bf16, hipStream_t stream);
+
+hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
+                         const AbsmaxSrc &src, void *dx, int dx_is_bf16, hipStream_t stream);
+
+}  // namespace nf4

@@ -1,0 +1,198 @@
+/*
+ * nf4.h -- C ABI of libnf4 (package dequant_gemm_amd): NF4 blockwise weight
+ * quantization with double quantization, and the fused NF4-dequant GEMMs,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute (sources cited by page title and passage):
+ *
+ *  - "Zenbit" (PyPI project page), section "What's inside", bullet zenbit.nf4:
+ *    NF4 blockwise quantization with double quantization of the scale
+ *    factors, QLoRA-style.  Bullet zenbit.pallas_nf4: a fused NF4
+ *    dequant+matmul whose weight streams compressed and is dequantized on
+ *    chip, never materialised at full precision in device memory; a fused
+ *    backward that forms dL/dX without materialising the weight, and no dL/dW
+ *    (the quantized base weight is frozen).
+ *  - "bitsandbytes" (unfragile.ai artifact page), NF4 data-type paragraph:
+ *    16 levels from the inverse normal CDF, more of them near zero; weights
+ *    map to levels through lookup tables after per-block scaling.
+ *    Double-quantization paragraph: one absmax per 64-weight block, the absmax
+ *    values themselves quantized to 8 bits with their own meta-scales; the
+ *    scales are dequantized first, then used to dequantize the weights.
+ *    Quantized-GEMM paragraph: weights dequantized on the fly, float32
+ *    multiply, float32 outputs.  QuantState paragraph: the quantized data,
+ *    absmax and shape travel together (here: nf4_qtensor).
+ *
+ * Exact semantics (the readings where the pages are silent):
+ *  - weight W is logical [rows, cols] row-major, flattened e = r*cols + c;
+ *    block b holds elements 64b .. 64b+63 (the last block may be partial);
+ *  - a_b = max|x| over the block (fp32); n = fp32(x / a_b) (IEEE division);
+ *    code = index of the nearest NF4 level, ties to the lower index; an
+ *    all-zero block codes every element 7 (the level 0.0);
+ *  - packed byte j = code[2j] | code[2j+1] << 4 (odd count: high nibble 0);
+ *  - double quantization: mu = exact mean of all a_b rounded once to fp32;
+ *    a'_b = fp32(a_b - mu); per group of 256 consecutive blocks
+ *    s_g = fp32(max|a'| / 127); q_b = clamp(rint_even(fp32(a'_b / s_g)),
+ *    -127, 127) as int8; an all-zero group has s_g = 0 and q = 0;
+ *  - dequantized absmax a^_b = fp32(fp32(q_b * s_g) + mu) with double
+ *    quantization (two roundings, no fused multiply-add), else a^_b = a_b;
+ *  - W^_e = bf16_rne(fp32(level[code_e] * a^_b)); the fp32 variant returns
+ *    fp32(level * a^) unrounded;
+ *  - GEMMs: Y = X W^T and dX = dY W^ with bf16 operands, fp32 accumulation
+ *    and fp32 (or, on request, bf16-rounded) outputs; W^ is formed on chip.
+ *
+ * Conventions for every call:
+ *  - Device pointers point to memory of the current HIP device; every device
+ *    pointer must be 16-byte aligned (NF4_ERR_ALIGN otherwise).
+ *  - The caller owns and frees every buffer.  The library never allocates or
+ *    frees device memory and never synchronises; work is queued on `stream`
+ *    (a hipStream_t; NULL means the default stream) and outputs are valid once
+ *    the stream has reached that point.  No global mutable state.
+ *  - Every problem the host can see (NULL pointer, bad size, bad blocksize,
+ *    bad dtype enum, misalignment, short workspace, unsupported shape) is
+ *    returned before anything is launched, and outputs are left untouched.
+ *    A failed launch returns NF4_ERR_HIP.
+ *  - Non-finite weights are outside the method's domain (precondition); if
+ *    `d_status` is given, the quantizer ORs bit 0 into it when it sees a
+ *    non-finite block absmax.
+ *  - Dense tensors are row-major and contiguous: X [M,K], Y [M,N],
+ *    dY [M,N], dX [M,K], where the weight is [N,K] (nn.Linear's [out,in]).
+ */
+#ifndef NF4_H_
+#define NF4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nf4_status {
+  NF4_OK = 0,
+  NF4_ERR_NULL = 1,         /* a required pointer is NULL */
+  NF4_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or too large */
+  NF4_ERR_BLOCKSIZE = 3,    /* blocksize is not 64 */
+  NF4_ERR_DTYPE = 4,        /* unknown nf4_dtype value */
+  NF4_ERR_ALIGN = 5,        /* a device pointer is not 16-byte aligned */
+  NF4_ERR_WORKSPACE = 6,    /* workspace smaller than nf4_sizes reports */
+  NF4_ERR_UNSUPPORTED = 7,  /* valid but not supported, e.g. a GEMM with cols % 64 != 0 */
+  NF4_ERR_HIP = 8           /* a HIP launch failed */
+};
+
+enum nf4_dtype {
+  NF4_F32 = 0,
+  NF4_BF16 = 1
+};
+
+/* Largest element count a quantized tensor may hold (2^37). */
+#define NF4_MAX_NUMEL ((int64_t)1 << 37)
+/* The only supported block size. */
+#define NF4_BLOCKSIZE 64
+/* Absmax values per double-quantization group. */
+#define NF4_DQ_GROUP 256
+
+/*
+ * A quantized weight: host struct, device buffers (the QuantState analogue).
+ * Sizes for rows x cols (numel = rows*cols, nblocks = ceil(numel/64),
+ * ngroups = ceil(nblocks/256)):
+ *   packed        ceil(numel/2) bytes
+ *   absmax        nblocks fp32     (double_quant == 0; NULL otherwise)
+ *   absmax_q      nblocks int8     (double_quant == 1)
+ *   absmax_scale  ngroups fp32     (double_quant == 1)
+ *   absmax_mean   1 fp32           (double_quant == 1)
+ * The struct is read during a call only; the library keeps no pointer to it.
+ */
+typedef struct nf4_qtensor {
+  int64_t rows;
+  int64_t cols;
+  int32_t blocksize;
+  int32_t double_quant;
+  uint8_t *packed;
+  float *absmax;
+  int8_t *absmax_q;
+  float *absmax_scale;
+  float *absmax_mean;
+} nf4_qtensor;
+
+/* A short English description of a status code (static storage). */
+const char *nf4_status_string(int status);
+
+/*
+ * Copies the 16 NF4 levels, ascending (level 0 = -1, level 7 = 0,
+ * level 15 = +1), into host memory `levels16`.  Source: "bitsandbytes" page,
+ * NF4 data-type paragraph (levels from the inverse normal CDF); construction:
+ * QLoRA's 8 positive / 7 negative normal quantiles with offset 0.9677083,
+ * normalised by the largest, rounded once to fp32.
+ */
+int nf4_codebook(float *levels16);
+
+/*
+ * Copies into host memory `thresholds15` the 15 decision thresholds the
+ * quantizer uses: t_i is the smallest fp32 n that codes to i+1, so that
+ * code(n) = #{i : n >= t_i} equals the nearest level with ties to the lower
+ * index.  Exposed so the derivation can be checked against an independent
+ * nearest-level search.
+ */
+int nf4_thresholds(float *thresholds15);
+
+/*
+ * Buffer sizes for a rows x cols weight.  Any output pointer may be NULL.
+ * workspace_bytes is the device workspace nf4_quantize needs (0 without
+ * double quantization).  Errors: NF4_ERR_SHAPE (rows or cols < 1, or
+ * numel > NF4_MAX_NUMEL), NF4_ERR_BLOCKSIZE.
+ */
+int nf4_sizes(int64_t rows, int64_t cols, int blocksize, int double_quant,
+              int64_t *packed_bytes, int64_t *nblocks, int64_t *ngroups,
+              size_t *workspace_bytes);
+
+/*
+ * Quantizes W (device, [rows, cols] row-major, dtype w_dtype = NF4_F32 or
+ * NF4_BF16) into `out`, whose rows/cols/blocksize/double_quant must match the
+ * arguments and whose buffers are sized per nf4_sizes.  "Zenbit" page,
+ * zenbit.nf4 bullet; "bitsandbytes" page, NF4 and double-quantization
+ * paragraphs.  `workspace` (device, >= workspace_bytes from nf4_sizes, may be
+ * NULL when that is 0) is scratch for the fp32 absmax and the exact-mean
+ * accumulators; its contents on entry do not matter.  `d_status` (device
+ * uint32, may be NULL): bit 0 is ORed in if a block absmax is non-finite.
+ * Bit-exact and deterministic: the mean is formed from integer sums, so the
+ * result does not depend on launch order.
+ */
+int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
+                 int blocksize, int double_quant, const nf4_qtensor *out,
+                 void *workspace, size_t workspace_bytes, uint32_t *d_status,
+                 void *stream);
+
+/*
+ * Writes the dequantized weight W^ (device, [rows, cols] row-major) in
+ * out_dtype: NF4_BF16 gives bf16_rne(level * a^) (the operand the GEMMs
+ * use), NF4_F32 gives fp32(level * a^).  "bitsandbytes" page,
+ * double-quantization paragraph: absmax first, then the weights.
+ */
+int nf4_dequantize(const nf4_qtensor *q, void *out, int out_dtype, void *stream);
+
+/*
+ * Y = X W^T.  X: device bf16 [M, K] with K = q->cols; Y: device [M, N] with
+ * N = q->rows, in y_dtype (NF4_F32, or NF4_BF16 = one rounding of the fp32
+ * accumulator).  W^ is dequantized on chip to bf16 and never written to
+ * memory.  Requires K % 64 == 0 (NF4_ERR_UNSUPPORTED otherwise).  M == 0 is
+ * a successful no-op.  "Zenbit" page, zenbit.pallas_nf4 bullet (fused
+ * forward); "bitsandbytes" page, quantized-GEMM paragraph (fp32 output).
+ */
+int nf4_matmul_fwd(const void *X, int64_t M, const nf4_qtensor *q, void *Y,
+                   int y_dtype, void *stream);
+
+/*
+ * dX = dY W^ (the backward pass with respect to the input of Y = X W^T; no
+ * gradient for the frozen weight).  dY: device bf16 [M, N] with N = q->rows;
+ * dX: device [M, K] with K = q->cols, in dx_dtype (NF4_F32 or NF4_BF16).
+ * Requires K % 64 == 0.  M == 0 is a successful no-op.  "Zenbit" page,
+ * zenbit.pallas_nf4 bullet (fused backward, dL/dX only).
+ */
+int nf4_matmul_bwd_dx(const void *dY, int64_t M, const nf4_qtensor *q, void *dX,
+                      int dx_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4_H_ */

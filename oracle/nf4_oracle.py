@@ -100,10 +100,14 @@ def f32_to_bf16_bits(x) -> np.ndarray:
 
     bfloat16 keeps the top 16 bits of the float32 encoding; rounding adds half
     an ulp of the kept part (0x7FFF, plus 1 when the kept part is odd, so ties
-    go to even) before truncating.  Finite inputs only.
+    go to even) before truncating.  Finite inputs only (no overflow of the
+    32-bit sum is then possible).
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -147,7 +151,7 @@ def normalize(x: np.ndarray, a: np.ndarray) -> np.ndarray:
         return (np.asarray(x, np.float32) / np.asarray(a, np.float32)).astype(np.float32)
 
 
-def nearest_code(n: np.ndarray, c: np.ndarray | None = None, chunk: int = 1 << 20) -> np.ndarray:
+def nearest_code(n: np.ndarray, c: np.ndarray | None = None, chunk: int = 1 << 16) -> np.ndarray:
     """argmin_i |n - c_i| with ties to the lower index (R3).
 
     The distances are taken in float64: a tie can only happen where n lies
@@ -161,9 +165,13 @@ def nearest_code(n: np.ndarray, c: np.ndarray | None = None, chunk: int = 1 << 2
     c64 = np.asarray(c, np.float64)[None, :]
     n = np.asarray(n, np.float32).ravel()
     out = np.empty(n.size, dtype=np.uint8)
+    dist = np.empty((min(chunk, n.size), c64.size), np.float64)
     for lo in range(0, n.size, chunk):
         seg = n[lo:lo + chunk].astype(np.float64)[:, None]
-        out[lo:lo + chunk] = np.argmin(np.abs(seg - c64), axis=1)
+        d = dist[: seg.shape[0]]
+        np.subtract(seg, c64, out=d)
+        np.abs(d, out=d)
+        out[lo:lo + chunk] = np.argmin(d, axis=1)
     return out
 
 
@@ -285,16 +293,21 @@ def dq_absmax(q: np.ndarray, s: np.ndarray, mu: np.float32, group: int = DQ_GROU
 
 
 def dequantize_codes(codes: np.ndarray, ahat: np.ndarray, blocksize: int = BLOCKSIZE,
-                     out: str = "bf16", c: np.ndarray | None = None) -> np.ndarray:
+                     out: str = "bf16", c: np.ndarray | None = None, chunk: int = 1 << 20) -> np.ndarray:
     """W^_e = bf16_rne(fl(c[code_e] * a^_b)) (R5); ``out='f32'`` returns fl(c * a^) unrounded."""
     if c is None:
         c = codebook()
+    c = np.asarray(c, np.float32)
     codes = np.asarray(codes, np.uint8).ravel()
-    ab = np.repeat(np.asarray(ahat, np.float32), blocksize)[: codes.size]
-    prod = (np.asarray(c, np.float32)[codes] * ab).astype(np.float32)
-    if out == "f32":
-        return prod
-    return f32_to_bf16_bits(prod)
+    ahat = np.asarray(ahat, np.float32)
+    res = np.empty(codes.size, np.uint16 if out == "bf16" else np.float32)
+    step = chunk - chunk % blocksize
+    for lo in range(0, codes.size, step):
+        cc = codes[lo:lo + step]
+        ab = np.repeat(ahat[lo // blocksize: (lo + cc.size + blocksize - 1) // blocksize], blocksize)[: cc.size]
+        prod = (c[cc] * ab).astype(np.float32)
+        res[lo:lo + cc.size] = prod if out == "f32" else f32_to_bf16_bits(prod)
+    return res
 
 
 def quantize(w: np.ndarray, blocksize: int = BLOCKSIZE, double_quant_on: bool = True) -> dict:

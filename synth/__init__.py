@@ -9,9 +9,9 @@ Recipe (every tensor):
   * ``standard_normal`` in float64 times the standard deviation, or
     ``standard_t(nu)`` times a scale, drawn in chunks of ``_CHUNK`` values in
     row-major order (the chunking does not change the stream);
-  * rounded to float32 by numpy's ``astype`` (round-to-nearest-even), and from
-    there to bfloat16 by torch's conversion (round-to-nearest-even) where the
-    workload calls for bf16.
+  * the float64 product rounded to float32 (round-to-nearest-even, numpy's
+    unsafe cast on output), and from there to bfloat16 by torch's conversion
+    (round-to-nearest-even) where the workload calls for bf16.
 
 Workloads and seeds (``N(0, s)`` means standard deviation ``s``):
   tiny     W [256,256] f32 N(0,0.02) seed 0; X [8,256] bf16 N(0,1) seed 1;
@@ -34,7 +34,7 @@ import os
 import numpy as np
 import torch
 
-_CHUNK = 1 << 22
+_CHUNK = 1 << 20
 
 BULK_LAYERS = 32
 BULK_D = 4096
@@ -45,15 +45,17 @@ BULK_NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 def _draw(kind: str, n: int, seed: int, scale: float, df: float = 4.0) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     out = np.empty(n, dtype=np.float32)
+    tmp = np.empty(min(_CHUNK, n), dtype=np.float64)
     for lo in range(0, n, _CHUNK):
         m = min(_CHUNK, n - lo)
         if kind == "normal":
-            v = rng.standard_normal(m)
+            v = rng.standard_normal(out=tmp[:m])
         elif kind == "t":
             v = rng.standard_t(df, m)
         else:
             raise ValueError(kind)
-        out[lo:lo + m] = (v * scale).astype(np.float32)
+        # float64 product rounded to float32 (nearest-even) on the way out
+        np.multiply(v, scale, out=out[lo:lo + m], casting="unsafe")
     return out
 
 
@@ -145,14 +147,16 @@ def bulk_weight(layer: int, j: int) -> torch.Tensor:
     return normal(bulk_shape(j), 0.02, 3000 + 7 * layer + j)
 
 
-def bulk_weights_parallel(keys, workers: int | None = None):
-    """Draw several bulk matrices at once (numpy's generators release the GIL).
-
-    ``keys`` is an iterable of (layer, j); returns a dict keyed the same way.
-    """
-    keys = list(keys)
+def parallel(fn, args, workers: int | None = None):
+    """[fn(a) for a in args], drawn on a thread pool (numpy's generators release the GIL)."""
+    args = list(args)
     if workers is None:
         workers = min(16, len(os.sched_getaffinity(0)))
     with _cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
-        vals = list(ex.map(lambda k: bulk_weight(*k), keys))
-    return dict(zip(keys, vals))
+        return list(ex.map(fn, args))
+
+
+def bulk_weights_parallel(keys, workers: int | None = None):
+    """Several bulk matrices at once; ``keys`` are (layer, j); returns a dict keyed the same way."""
+    keys = list(keys)
+    return dict(zip(keys, parallel(lambda k: bulk_weight(*k), keys, workers)))

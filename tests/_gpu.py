@@ -1,0 +1,73 @@
+"""Shared helpers of the GPU parity tests: device checks and oracle comparisons.
+
+Expected values always come from ``oracle`` run on the same seeded inputs;
+nothing here derives an expected value from the HIP path.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a HIP device")
+    return torch.device("cuda:0")
+
+
+def lib():
+    import dequant_gemm_amd as dg
+    dg.lib()  # raises if libnf4.so is missing: no fallback
+    return dg
+
+
+def note(msg: str):
+    """Progress line that pytest's capture does not swallow."""
+    sys.__stderr__.write(msg + "\n")
+    sys.__stderr__.flush()
+
+
+def u32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int32).numpy().view(np.uint32)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_quantize(w_cpu: torch.Tensor, dq: bool) -> dict:
+    return O.quantize(w_cpu.float().numpy(), double_quant_on=dq)
+
+
+def assert_quant_equal(qg, qo: dict, where: str = ""):
+    """Codes (packed bytes) and the absmax state, bit for bit."""
+    pk = qg.packed.cpu().numpy()
+    bad = np.nonzero(pk != qo["packed"])[0]
+    assert bad.size == 0, f"{where}: {bad.size} packed bytes differ, first at {bad[0]}"
+    if qo["double_quant"]:
+        assert u32(qg.absmax_mean)[0] == np.float32(qo["mean"]).view(np.uint32), f"{where}: mean"
+        q = qg.absmax_q.cpu().numpy()
+        bad = np.nonzero(q != qo["absmax_q"])[0]
+        assert bad.size == 0, f"{where}: {bad.size} int8 absmax differ, first at {bad[0]}"
+        s = u32(qg.absmax_scale)
+        assert np.array_equal(s, qo["scale"].view(np.uint32)), f"{where}: scales"
+    else:
+        a = u32(qg.absmax)
+        bad = np.nonzero(a != qo["absmax"].view(np.uint32))[0]
+        assert bad.size == 0, f"{where}: {bad.size} fp32 absmax differ, first at {bad[0]}"
+
+
+def assert_gemm_within_bound(out: torch.Tensor, ref: np.ndarray, bound: np.ndarray, where: str = ""):
+    o = out.detach().float().cpu().numpy().astype(np.float64)
+    assert o.shape == ref.shape
+    assert np.all(np.isfinite(o)), f"{where}: non-finite output"
+    err = np.abs(o - ref)
+    bad = ~(err <= bound)
+    n = int(bad.sum())
+    if n:
+        i = np.argwhere(bad)[0]
+        pytest.fail(f"{where}: {n} elements outside 1e-4*(|A||B|); first {tuple(i)}: "
+                    f"got {o[tuple(i)]!r} want {ref[tuple(i)]!r} bound {bound[tuple(i)]!r}")

@@ -1,0 +1,157 @@
+"""The C ABI on the CPU: the library loads, exports every call include/nf4.h
+declares, its constants agree with the oracle, sizes follow the closed forms,
+and every host-detectable error is returned before any HIP call.
+
+No compute call is made here (no GPU); the error paths never reach HIP.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests._exact import exact_argmin_code
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4.h")
+
+dg = pytest.importorskip("dequant_gemm_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dg.LIB_PATH):
+        pytest.fail("libnf4.so is not built (run `python -m dequant_gemm_amd.build`)")
+    return dg.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nf4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    declared = _declared_functions()
+    assert set(declared) == set(dg.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (nf4_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared) <= exported, set(declared) - exported
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_codebook_matches_oracle_bit_for_bit(L):
+    got = dg.nf4_codebook().numpy()
+    assert got.view(np.uint32).tolist() == O.codebook().view(np.uint32).tolist()
+
+
+def test_thresholds_are_the_exact_decision_boundaries(L):
+    """Each t_i is the smallest fp32 whose exact nearest level is i+1 (ties to the lower)."""
+    c = O.codebook()
+    t = dg.nf4_thresholds().numpy()
+    assert np.all(np.diff(t.astype(np.float64)) > 0)
+    for i, ti in enumerate(t):
+        below = np.nextafter(np.float32(ti), np.float32(-2))
+        assert exact_argmin_code(np.float32(ti), c) == i + 1
+        assert exact_argmin_code(below, c) == i
+
+
+@pytest.mark.parametrize("rows,cols,dq", [(256, 256, True), (4096, 4096, True), (11008, 4096, True),
+                                          (28672, 8192, True), (3, 37, False), (1, 1, True)])
+def test_sizes_closed_forms(L, rows, cols, dq):
+    s = dg.nf4_sizes(rows, cols, 64, dq)
+    numel = rows * cols
+    nb = -(-numel // 64)
+    assert s["packed_bytes"] == -(-numel // 2)
+    assert s["nblocks"] == nb
+    assert s["ngroups"] == -(-nb // 256)
+    if dq:
+        assert s["workspace_bytes"] >= 2048 + 4 * nb
+    else:
+        assert s["workspace_bytes"] == 0
+
+
+def test_appendix_quantized_bytes():
+    """Wq = packed + int8 absmax + fp32 scales + mu at the workload sizes (4.127 bits/weight)."""
+    expect = {(256, 256): 33812, (4096, 4096): 8654852, (11008, 4096): 23259908, (28672, 8192): 121167876}
+    for (r, c), wq in expect.items():
+        s = dg.nf4_sizes(r, c, 64, True)
+        assert s["packed_bytes"] + s["nblocks"] + 4 * s["ngroups"] + 4 == wq
+
+
+def _status(name, L):
+    return getattr(dg._lib, "NF4_" + name) if hasattr(dg._lib, "NF4_" + name) else None
+
+
+P = 1 << 20  # a fake, 16-byte aligned "device" address; never dereferenced on the error paths
+
+
+def _qt(rows=64, cols=64, dq=1, packed=P, absmax=P, q=P, scale=P, mean=P, bs=64):
+    return dg.QTensorStruct(rows, cols, bs, dq, packed, absmax, q, scale, mean)
+
+
+def test_sizes_errors(L):
+    i64 = ctypes.c_int64
+    assert L.nf4_sizes(0, 64, 64, 1, None, None, None, None) == 2
+    assert L.nf4_sizes(64, -1, 64, 1, None, None, None, None) == 2
+    assert L.nf4_sizes(1 << 20, 1 << 20, 64, 1, None, None, None, None) == 2  # beyond 2^37 elements
+    assert L.nf4_sizes(64, 64, 128, 1, None, None, None, None) == 3
+    assert L.nf4_sizes(64, 64, 64, 2, None, None, None, None) == 7
+    assert L.nf4_codebook(None) == 1
+
+
+def test_quantize_errors(L):
+    q = _qt()
+    ws = dg.nf4_sizes(64, 64, 64, True)["workspace_bytes"]
+    call = lambda **k: L.nf4_quantize(k.get("W", P), k.get("dt", 1), k.get("rows", 64), k.get("cols", 64),
+                                      k.get("bs", 64), k.get("dq", 1), ctypes.byref(k.get("q", q)),
+                                      k.get("ws", P), k.get("wsb", ws), k.get("status", None), None)
+    assert call(W=None) == 1
+    assert call(dt=7) == 4
+    assert call(bs=32) == 3
+    assert call(rows=0) == 2
+    assert call(W=P + 2) == 5
+    assert call(wsb=ws - 1) == 6
+    assert call(ws=None) == 1
+    assert call(ws=P + 8) == 5
+    assert call(q=_qt(rows=32)) == 2                 # descriptor does not match the shape
+    assert call(q=_qt(dq=0), dq=1) == 2
+    assert call(q=_qt(packed=None)) == 1
+    assert call(q=_qt(q=None)) == 1
+    assert call(q=_qt(mean=P + 4)) == 5
+    assert call(status=P + 4) == 5
+    assert L.nf4_quantize(P, 1, 64, 64, 64, 1, None, P, ws, None, None) == 1
+
+
+def test_dequantize_errors(L):
+    assert L.nf4_dequantize(None, P, 1, None) == 1
+    assert L.nf4_dequantize(ctypes.byref(_qt()), None, 1, None) == 1
+    assert L.nf4_dequantize(ctypes.byref(_qt()), P, 5, None) == 4
+    assert L.nf4_dequantize(ctypes.byref(_qt()), P + 2, 1, None) == 5
+    assert L.nf4_dequantize(ctypes.byref(_qt(bs=128)), P, 1, None) == 3
+    assert L.nf4_dequantize(ctypes.byref(_qt(dq=0, absmax=None)), P, 1, None) == 1
+
+
+@pytest.mark.parametrize("fn", ["nf4_matmul_fwd", "nf4_matmul_bwd_dx"])
+def test_gemm_errors(L, fn):
+    f = getattr(L, fn)
+    q = _qt(rows=128, cols=256)
+    assert f(P, 4, None, P, 0, None) == 1
+    assert f(None, 4, ctypes.byref(q), P, 0, None) == 1
+    assert f(P, 4, ctypes.byref(q), None, 0, None) == 1
+    assert f(P, -1, ctypes.byref(q), P, 0, None) == 2
+    assert f(P, 4, ctypes.byref(q), P, 9, None) == 4
+    assert f(P + 4, 4, ctypes.byref(q), P, 0, None) == 5
+    assert f(P, 4, ctypes.byref(_qt(rows=128, cols=96)), P, 0, None) == 7   # K % 64 != 0
+    # M == 0 is a successful no-op that launches nothing
+    assert f(None, 0, ctypes.byref(q), None, 0, None) == 0
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert L.nf4_status_string(s)
+    assert L.nf4_status_string(99) == b"unknown status"

@@ -1,0 +1,228 @@
+"""GPU parity: the fused NF4-dequant GEMMs against the CPU oracle.
+
+Forward Y = X W^T and backward dX = dY W^ ("Zenbit" page, zenbit.pallas_nf4
+bullet: fused forward and a fused backward forming dL/dX only).  The oracle
+quantizes the same seeded weight itself, rounds W^ to bf16 the same way and
+accumulates in float64; every checked element must satisfy
+|err| <= 1e-4 * (|A| |B|) element by element (1e-4 is the stated tolerance).
+Identity inputs make the product a copy of W^, which must then be exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._gpu import assert_gemm_within_bound, bf16_bits, dev, lib, note, oracle_quantize
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_what(W_cpu, dq=True):
+    qo = oracle_quantize(W_cpu, dq)
+    return O.bf16_bits_to_f32(O.dequantize(qo)).reshape(W_cpu.shape)
+
+
+def _run(M, N, K, seed, dq=True, out_dtype=torch.float32, wdtype=torch.bfloat16):
+    dg = lib()
+    d = dev()
+    W = synth.normal((N, K), 0.02, seed, wdtype)
+    X = synth.normal((M, K), 1.0, seed + 1)
+    dY = synth.normal((M, N), 1.0, seed + 2)
+    q = dg.nf4_quantize(W.to(d), double_quant=dq)
+    Y = dg.nf4_matmul_fwd(X.to(d), q, out_dtype)
+    dX = dg.nf4_matmul_bwd_dx(dY.to(d), q, out_dtype)
+    torch.cuda.synchronize()
+    wh = _oracle_what(W, dq)
+    x = X.float().numpy()
+    dy = dY.float().numpy()
+    return Y, dX, x, dy, wh
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 256, 256), (4, 256, 256), (8, 256, 256), (16, 256, 256),    # small-M kernel
+    (1, 300, 320), (5, 17, 64), (16, 1000, 192), (3, 4096, 4096),
+    (17, 300, 256), (100, 513, 128), (256, 256, 256), (300, 700, 512),  # large-M kernel, ragged tiles
+    (513, 129, 64), (1000, 64, 1024),
+])
+def test_fwd_bwd_ragged(M, N, K):
+    Y, dX, x, dy, wh = _run(M, N, K, 7 * M + N + K)
+    assert_gemm_within_bound(Y, O.matmul_fwd(x, wh), O.fwd_bound(x, wh), f"fwd {M}x{N}x{K}")
+    assert_gemm_within_bound(dX, O.matmul_bwd_dx(dy, wh), O.bwd_dx_bound(dy, wh), f"bwd {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_tiny_workload(dq):
+    dg = lib()
+    d = dev()
+    t = synth.tiny()
+    q = dg.nf4_quantize(t["W"].to(d), double_quant=dq)
+    Y = dg.nf4_matmul_fwd(t["X"].to(d), q)
+    dX = dg.nf4_matmul_bwd_dx(t["dY"].to(d), q)
+    torch.cuda.synchronize()
+    wh = _oracle_what(t["W"], dq)
+    x, dy = t["X"].float().numpy(), t["dY"].float().numpy()
+    assert_gemm_within_bound(Y, O.matmul_fwd(x, wh), O.fwd_bound(x, wh), "tiny fwd")
+    assert_gemm_within_bound(dX, O.matmul_bwd_dx(dy, wh), O.bwd_dx_bound(dy, wh), "tiny bwd")
+
+
+@pytest.mark.parametrize("n_rows,k_cols", [(256, 256), (320, 192)])
+def test_identity_inputs_reproduce_the_dequantized_weight(n_rows, k_cols):
+    """X = I gives Y = W^T, dY = I gives dX = W^: each output is one exact product."""
+    dg = lib()
+    d = dev()
+    W = synth.tiny()["W"] if (n_rows, k_cols) == (256, 256) else synth.normal((n_rows, k_cols), 0.02, 77, torch.float32)
+    wh = _oracle_what(W)
+    q = dg.nf4_quantize(W.to(d), double_quant=True)
+    for M in (k_cols,):
+        Y = dg.nf4_matmul_fwd(torch.eye(k_cols, dtype=torch.bfloat16, device=d), q)
+        assert np.array_equal(Y.cpu().numpy(), wh.T)
+    dX = dg.nf4_matmul_bwd_dx(torch.eye(n_rows, dtype=torch.bfloat16, device=d), q)
+    assert np.array_equal(dX.cpu().numpy(), wh)
+    # small-M kernel: unit rows pick single columns of W^
+    e = torch.zeros((4, k_cols), dtype=torch.bfloat16)
+    for r, kk in enumerate((0, 1, 63, k_cols - 1)):
+        e[r, kk] = 1
+    Ys = dg.nf4_matmul_fwd(e.to(d), q)
+    torch.cuda.synchronize()
+    assert np.array_equal(Ys.cpu().numpy(), wh[:, [0, 1, 63, k_cols - 1]].T)
+
+
+def test_bf16_outputs_are_one_rounding_of_fp32():
+    dg = lib()
+    d = dev()
+    W = synth.normal((384, 512), 0.02, 3, torch.bfloat16).to(d)
+    q = dg.nf4_quantize(W)
+    for M in (8, 300):
+        X = synth.normal((M, 512), 1.0, 4).to(d)
+        dY = synth.normal((M, 384), 1.0, 5).to(d)
+        y32 = dg.nf4_matmul_fwd(X, q, torch.float32)
+        y16 = dg.nf4_matmul_fwd(X, q, torch.bfloat16)
+        d32 = dg.nf4_matmul_bwd_dx(dY, q, torch.float32)
+        d16 = dg.nf4_matmul_bwd_dx(dY, q, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y16), O.f32_to_bf16_bits(y32.cpu().numpy()))
+        assert np.array_equal(bf16_bits(d16), O.f32_to_bf16_bits(d32.cpu().numpy()))
+
+
+def test_zero_rows_is_a_noop():
+    dg = lib()
+    d = dev()
+    q = dg.nf4_quantize(synth.normal((64, 64), 0.02, 1).to(d))
+    Y = dg.nf4_matmul_fwd(torch.empty((0, 64), dtype=torch.bfloat16, device=d), q)
+    dX = dg.nf4_matmul_bwd_dx(torch.empty((0, 64), dtype=torch.bfloat16, device=d), q)
+    assert Y.shape == (0, 64) and dX.shape == (0, 64)
+
+
+def test_deterministic_reruns():
+    dg = lib()
+    d = dev()
+    q = dg.nf4_quantize(synth.normal((1024, 1024), 0.02, 8).to(d))
+    for M in (4, 512):
+        X = synth.normal((M, 1024), 1.0, 9).to(d)
+        a = dg.nf4_matmul_fwd(X, q)
+        b = dg.nf4_matmul_fwd(X, q)
+        c = dg.nf4_matmul_bwd_dx(X, q)
+        e = dg.nf4_matmul_bwd_dx(X, q)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(c, e)
+
+
+@pytest.mark.parametrize("M", synth.DECODE_MS)
+def test_decode_full(M):
+    dg = lib()
+    d = dev()
+    W = synth.decode_weight(0)
+    X = synth.decode_x(M)
+    q = dg.nf4_quantize(W.to(d))
+    Y = dg.nf4_matmul_fwd(X.to(d), q)
+    torch.cuda.synchronize()
+    wh = _oracle_what(W)
+    x = X.float().numpy()
+    assert_gemm_within_bound(Y, O.matmul_fwd(x, wh), O.fwd_bound(x, wh), f"decode M={M}")
+
+
+def _sampled_rows(M, seed, n=48):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.integers(0, M, n), [0, M - 1]]))
+
+
+@pytest.fixture(scope="module")
+def prefill():
+    dg = lib()
+    d = dev()
+    note("prefill: drawing inputs, GPU quantize/fwd/bwd")
+    W = synth.prefill_weight()
+    X, dY = synth.prefill_x(), synth.prefill_dy()
+    q = dg.nf4_quantize(W.to(d))
+    Y = dg.nf4_matmul_fwd(X.to(d), q)
+    dX = dg.nf4_matmul_bwd_dx(dY.to(d), q)
+    torch.cuda.synchronize()
+    note("prefill: oracle W^")
+    return {"W": W, "X": X, "dY": dY, "Y": Y.cpu(), "dX": dX.cpu(), "wh": _oracle_what(W)}
+
+
+def test_prefill_fwd_sampled_rows(prefill):
+    rows = _sampled_rows(synth.PREFILL_M, 2001)
+    x = prefill["X"][rows].float().numpy()
+    wh = prefill["wh"]
+    assert_gemm_within_bound(prefill["Y"][rows], O.matmul_fwd(x, wh), O.fwd_bound(x, wh), "prefill fwd")
+
+
+def test_prefill_bwd_sampled_rows(prefill):
+    rows = _sampled_rows(synth.PREFILL_M, 2002)
+    dy = prefill["dY"][rows].float().numpy()
+    wh = prefill["wh"]
+    assert_gemm_within_bound(prefill["dX"][rows], O.matmul_bwd_dx(dy, wh), O.bwd_dx_bound(dy, wh), "prefill bwd")
+
+
+def test_prefill_all_elements_against_fp32_product(prefill):
+    """Every element, against an fp32 product of the oracle's W^ (bound widened by
+    the fp32 reference's own rounding, 2K * 2^-24 * |X||W^|)."""
+    dev()
+    wh = torch.from_numpy(prefill["wh"]).to("cuda:0")
+    X = prefill["X"].to("cuda:0").float()
+    ref = X @ wh.T
+    mag = X.abs() @ wh.abs().T
+    tol = (1e-4 + 2 * synth.PREFILL_K * 2.0 ** -24) * mag
+    err = (prefill["Y"].to("cuda:0") - ref).abs()
+    assert int((err > tol).sum()) == 0
+    dY = prefill["dY"].to("cuda:0").float()
+    ref = dY @ wh
+    mag = dY.abs() @ wh.abs()
+    tol = (1e-4 + 2 * synth.PREFILL_N * 2.0 ** -24) * mag
+    err = (prefill["dX"].to("cuda:0") - ref).abs()
+    assert int((err > tol).sum()) == 0
+
+
+@pytest.fixture(scope="module")
+def large():
+    dg = lib()
+    d = dev()
+    note("large: drawing inputs (W fp32 Student-t)")
+    W = synth.large_weight()
+    X, dY = synth.large_x(), synth.large_dy()
+    note("large: GPU quantize/fwd/bwd")
+    q = dg.nf4_quantize(W.to(d))
+    Y = dg.nf4_matmul_fwd(X.to(d), q)
+    dX = dg.nf4_matmul_bwd_dx(dY.to(d), q)
+    torch.cuda.synchronize()
+    rows_f = _sampled_rows(synth.LARGE_M, 4001, 24)
+    rows_b = _sampled_rows(synth.LARGE_M, 4002, 24)
+    out = {"X": X[rows_f].float().numpy(), "dY": dY[rows_b].float().numpy(),
+           "Y": Y[torch.from_numpy(rows_f).to(d)].cpu(), "dX": dX[torch.from_numpy(rows_b).to(d)].cpu()}
+    del Y, dX, q
+    note("large: oracle W^ (235M elements)")
+    out["wh"] = _oracle_what(W)
+    return out
+
+
+def test_large_fwd_sampled_rows(large):
+    wh = large["wh"]
+    assert_gemm_within_bound(large["Y"], O.matmul_fwd(large["X"], wh), O.fwd_bound(large["X"], wh), "large fwd")
+
+
+def test_large_bwd_sampled_rows(large):
+    wh = large["wh"]
+    assert_gemm_within_bound(large["dX"], O.matmul_bwd_dx(large["dY"], wh), O.bwd_dx_bound(large["dY"], wh),
+                             "large bwd")

@@ -1,0 +1,201 @@
+"""GPU parity: nf4_quantize and nf4_dequantize against the CPU oracle, bit for bit.
+
+Codes, packed bytes, fp32/int8 absmax, scales, mean and dequantized weights
+must equal the oracle's exactly ("Zenbit" page, zenbit.nf4 bullet;
+"bitsandbytes" page, NF4 and double-quantization paragraphs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._gpu import assert_quant_equal, bf16_bits, dev, lib, note, oracle_quantize, u32
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_roundtrip(W_cpu, dq, where):
+    dg = lib()
+    d = dev()
+    qo = oracle_quantize(W_cpu, dq)
+    qg = dg.nf4_quantize(W_cpu.to(d), double_quant=dq)
+    torch.cuda.synchronize()
+    assert_quant_equal(qg, qo, where)
+    wh = dg.nf4_dequantize(qg, torch.bfloat16)
+    want = O.dequantize(qo).reshape(W_cpu.shape)
+    got = bf16_bits(wh)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{where}: {bad[0].size} bf16 W^ differ"
+    wf = dg.nf4_dequantize(qg, torch.float32)
+    assert np.array_equal(u32(wf), O.dequantize(qo, out="f32").reshape(W_cpu.shape).view(np.uint32)), where
+    return qg, qo
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_tiny(dq):
+    _check_roundtrip(synth.tiny()["W"], dq, f"tiny dq={dq}")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 2), (3, 37), (5, 64), (1, 100), (7, 1000),
+                                       (33, 65), (2, 8191), (300, 777), (257, 256 * 64 + 8)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged_shapes(rows, cols, dtype):
+    W = synth.normal((rows, cols), 0.02, 17 + rows + cols, dtype)
+    for dq in (True, False):
+        _check_roundtrip(W, dq, f"{rows}x{cols} {dtype} dq={dq}")
+
+
+def _special_weight():
+    """Blocks that exercise every branch of the level search."""
+    rng = np.random.default_rng(99)
+    c = O.codebook()
+    blocks = []
+    blocks.append(np.zeros(64, np.float32))                                            # all zero
+    blocks.append((rng.standard_normal(64) * 1e-40).astype(np.float32))               # subnormal
+    blocks.append((rng.uniform(-1, 1, 64) * 2.0 ** -126).astype(np.float32))          # tiny normal
+    blocks.append((rng.uniform(-1, 1, 64) * 3.0e38).astype(np.float32))               # near overflow
+    # exact ties: absmax 1.0, so n = x exactly; the five exactly representable midpoints
+    mids = [(np.float64(c[i]) + np.float64(c[i + 1])) / 2 for i in range(15)]
+    exact = [np.float32(m) for m in mids if float(np.float32(m)) == m]
+    b = np.zeros(64, np.float32)
+    b[0] = 1.0
+    vals = []
+    for m in exact:
+        vals += [m, np.nextafter(m, np.float32(2)), np.nextafter(m, np.float32(-2))]
+    for m in mids:  # values within an ulp of every threshold
+        f = np.float32(m)
+        vals += [f, np.nextafter(f, np.float32(2)), np.nextafter(f, np.float32(-2))]
+    b[1:1 + min(63, len(vals))] = np.array(vals[:63], np.float32)
+    blocks.append(b)
+    b2 = b.copy()
+    b2[0] = -1.0
+    b2[1:] = -b2[1:]
+    blocks.append(b2)
+    rest = vals[63:]
+    b3 = np.zeros(64, np.float32)
+    b3[0] = 1.0
+    b3[1:1 + len(rest)] = np.array(rest[:63], np.float32)
+    blocks.append(b3)
+    # the same patterns scaled by an absmax that is not a power of two
+    s = np.float32(0.0371)
+    blocks.append((b * s).astype(np.float32))
+    blocks.append(np.full(64, np.float32(-0.5)))                                      # constant block
+    blocks.append((rng.standard_normal(64) * 0.02).astype(np.float32))
+    w = np.concatenate(blocks).reshape(-1, 64)
+    return torch.from_numpy(w)
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_special_blocks(dq):
+    _check_roundtrip(_special_weight(), dq, f"special dq={dq}")
+
+
+def test_nonfinite_input_sets_status_bit():
+    dg = lib()
+    d = dev()
+    W = synth.normal((4, 256), 0.02, 5, torch.float32)
+    W[2, 70] = float("inf")
+    status = torch.zeros(4, dtype=torch.int32, device=d)
+    dg.nf4_quantize(W.to(d), double_quant=True, status=status)
+    torch.cuda.synchronize()
+    assert int(status[0].item()) & 1 == 1
+    status.zero_()
+    dg.nf4_quantize(synth.normal((4, 256), 0.02, 5, torch.float32).to(d), double_quant=True, status=status)
+    torch.cuda.synchronize()
+    assert int(status[0].item()) == 0
+
+
+def test_deterministic_and_mean_is_order_free():
+    dg = lib()
+    d = dev()
+    W = synth.normal((2048, 512), 0.02, 41, torch.bfloat16).to(d)
+    a = dg.nf4_quantize(W)
+    b = dg.nf4_quantize(W)
+    torch.cuda.synchronize()
+    for name in ("packed", "absmax_q", "absmax_scale", "absmax_mean"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    # permuting rows permutes whole blocks: the exact mean cannot change
+    perm = torch.randperm(2048, generator=torch.Generator().manual_seed(0)).to(d)
+    c = dg.nf4_quantize(W[perm].contiguous())
+    torch.cuda.synchronize()
+    assert u32(c.absmax_mean)[0] == u32(a.absmax_mean)[0]
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_decode_weight_full(dq):
+    _check_roundtrip(synth.decode_weight(0), dq, f"decode dq={dq}")
+
+
+def test_prefill_weight_full():
+    note("prefill weight 11008x4096: oracle over every element")
+    _check_roundtrip(synth.prefill_weight(), True, "prefill")
+
+
+def test_large_outlier_weight():
+    """28672x8192 fp32 Student-t(4): exact absmax state everywhere, codes on sampled blocks."""
+    dg = lib()
+    d = dev()
+    note("large weight 28672x8192 fp32: drawing")
+    W = synth.large_weight()
+    w = W.numpy().ravel()
+    note("large weight: GPU quantize")
+    qg = dg.nf4_quantize(W.to(d), double_quant=True)
+    wh = dg.nf4_dequantize(qg, torch.bfloat16)
+    torch.cuda.synchronize()
+    note("large weight: oracle absmax, mean, int8 state")
+    a = O.block_absmax(w)
+    mu = O.exact_mean_f32(a)
+    q, s = O.double_quant(a, mu)
+    assert u32(qg.absmax_mean)[0] == np.float32(mu).view(np.uint32)
+    assert np.array_equal(qg.absmax_q.cpu().numpy(), q)
+    assert np.array_equal(u32(qg.absmax_scale), s.view(np.uint32))
+    ahat = O.dq_absmax(q, s, mu)
+    rng = np.random.default_rng(4000)
+    blocks = np.unique(np.concatenate([rng.integers(0, a.size, 8192), np.argsort(a)[-512:], np.argsort(a)[:64]]))
+    xb = w.reshape(-1, 64)[blocks]
+    codes = O.encode_blocks(xb, a[blocks])
+    pk = qg.packed.cpu().numpy().reshape(-1, 32)[blocks]
+    assert np.array_equal(pk, O.pack_codes(codes.ravel()).reshape(-1, 32))
+    want = O.dequantize_codes(codes.ravel(), ahat[blocks]).reshape(-1, 64)
+    got = bf16_bits(wh).reshape(-1, 64)[blocks]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("layers", [range(0, 8), range(8, 16), range(16, 24), range(24, 32)])
+def test_bulk_decoder_layers(layers):
+    """Bulk: every linear of a 32-layer decoder; exact int8 state everywhere, codes on samples.
+
+    Each matrix is quantized and dequantized on the GPU; the oracle recomputes
+    absmax, the exact mean, int8 absmax and scales of every block, and codes and
+    W^ of 256 random blocks per matrix.  The first layer is checked on every
+    element.
+    """
+    dg = lib()
+    d = dev()
+    for l in layers:
+        mats = synth.bulk_weights_parallel([(l, j) for j in range(7)])
+        for j in range(7):
+            W = mats[(l, j)]
+            if l == 0:
+                _check_roundtrip(W, True, f"bulk layer 0 {synth.BULK_NAMES[j]}")
+                continue
+            w = W.float().numpy().ravel()
+            qg = dg.nf4_quantize(W.to(d), double_quant=True)
+            wh = dg.nf4_dequantize(qg, torch.bfloat16)
+            torch.cuda.synchronize()
+            a = O.block_absmax(w)
+            mu = O.exact_mean_f32(a)
+            q, s = O.double_quant(a, mu)
+            where = f"bulk layer {l} {synth.BULK_NAMES[j]}"
+            assert u32(qg.absmax_mean)[0] == np.float32(mu).view(np.uint32), where
+            assert np.array_equal(qg.absmax_q.cpu().numpy(), q), where
+            assert np.array_equal(u32(qg.absmax_scale), s.view(np.uint32)), where
+            rng = np.random.default_rng(3000 + 7 * l + j)
+            blocks = np.unique(rng.integers(0, a.size, 256))
+            codes = O.encode_blocks(w.reshape(-1, 64)[blocks], a[blocks])
+            assert np.array_equal(qg.packed.cpu().numpy().reshape(-1, 32)[blocks],
+                                  O.pack_codes(codes.ravel()).reshape(-1, 32)), where
+            want = O.dequantize_codes(codes.ravel(), O.dq_absmax(q, s, mu)[blocks]).reshape(-1, 64)
+            assert np.array_equal(bf16_bits(wh).reshape(-1, 64)[blocks], want), where
+        note(f"bulk layer {l}: 7 matrices bit-exact")
