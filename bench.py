@@ -226,6 +226,49 @@ def _cpu_model():
     return "unknown"
 
 
+def run_single_op(dg, op, steps, warmup):
+    """One operation of the hot path repeated ``steps`` times (for profiler runs)."""
+    import synth
+    d = torch.device("cuda:0")
+    if op == "decode":
+        K, N = synth.DECODE_K, synth.DECODE_N
+        qs = [dg.nf4_quantize(w.to(d)) for w in synth.parallel(synth.decode_weight, range(16))]
+        X = synth.decode_x(16).to(d)
+        Y = torch.empty((16, N), dtype=torch.float32, device=d)
+        fn = lambda i: dg.nf4_matmul_fwd(X, qs[i % len(qs)], out=Y)
+    else:
+        M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
+        W = synth.prefill_weight().to(d)
+        q = dg.nf4_quantize(W)
+        if op == "fwd":
+            X = synth.prefill_x().to(d)
+            Y = torch.empty((M, N), dtype=torch.float32, device=d)
+            fn = lambda i: dg.nf4_matmul_fwd(X, q, out=Y)
+        elif op == "bwd_dx":
+            dY = synth.prefill_dy().to(d)
+            dX = torch.empty((M, K), dtype=torch.float32, device=d)
+            fn = lambda i: dg.nf4_matmul_bwd_dx(dY, q, out=dX)
+        elif op == "quantize":
+            ws = torch.empty(dg.nf4_sizes(N, K)["workspace_bytes"], dtype=torch.uint8, device=d)
+            fn = lambda i: dg.nf4_quantize(W, out=q, workspace=ws)
+        elif op == "dequantize":
+            Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
+            fn = lambda i: dg.nf4_dequantize(q, out=Wh)
+        else:
+            raise ValueError(op)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(i)
+    e.record()
+    e.synchronize()
+    print(json.dumps({"op": op, "steps": steps, "ms_per_call": s.elapsed_time(e) / steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +276,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--op", default=None, choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode"],
+                    help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the NF4 path here is built and timed on a single "
@@ -244,6 +289,9 @@ def main():
     import dequant_gemm_amd as dg
     dg.lib()
     torch.cuda.synchronize()
+    if a.op:
+        run_single_op(dg, a.op, a.steps, a.warmup)
+        return
 
     pre = bench_prefill(dg, a.steps, a.warmup)
     ops = pre["ops"]

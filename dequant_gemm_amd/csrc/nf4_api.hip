@@ -115,17 +115,17 @@ int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blo
   if (d_status && !aligned16(d_status)) return NF4_ERR_ALIGN;
   const int64_t numel = rows * cols;
   const int64_t nb = nblocks_of(numel);
-  unsigned long long *buckets = nullptr;
+  unsigned long long *partials = nullptr;
   float *absmax = out->absmax;
   if (double_quant) {
     const size_t need = nf4::quant_workspace_bytes(nb);
     if (workspace_bytes < need) return NF4_ERR_WORKSPACE;
     if (!workspace) return NF4_ERR_NULL;
     if (!aligned16(workspace)) return NF4_ERR_ALIGN;
-    buckets = reinterpret_cast<unsigned long long *>(workspace);
+    partials = reinterpret_cast<unsigned long long *>(workspace);
     absmax = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + nf4::absmax_ws_offset());
   }
-  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, out->packed, absmax, buckets,
+  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, out->packed, absmax, partials,
                                          d_status, double_quant, out->absmax_q, out->absmax_scale,
                                          out->absmax_mean, reinterpret_cast<hipStream_t>(stream)));
 }

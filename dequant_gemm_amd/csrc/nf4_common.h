@@ -75,6 +75,29 @@ __device__ __forceinline__ float block_ahat(const AbsmaxSrc &s, int64_t blk, flo
   return __fadd_rn(qs, mu);
 }
 
+// The raw per-block state, loaded early and turned into a^ only when used, so
+// that a prefetch does not force an early wait on its own loads.
+struct AbsmaxRaw {
+  float v;     // fp32 absmax (no double quantization) or the group scale
+  int q;       // int8 absmax (double quantization)
+};
+
+__device__ __forceinline__ AbsmaxRaw load_absmax_raw(const AbsmaxSrc &s, int64_t blk) {
+  AbsmaxRaw r;
+  if (s.dq) {
+    r.q = s.q[blk];
+    r.v = s.scale[blk >> 8];
+  } else {
+    r.q = 0;
+    r.v = s.absmax[blk];
+  }
+  return r;
+}
+
+__device__ __forceinline__ float ahat_of(const AbsmaxRaw &r, int dq, float mu) {
+  return dq ? __fadd_rn(__fmul_rn((float)r.q, r.v), mu) : r.v;
+}
+
 // ------------------------------------------------------------------ register LUT dequant
 //
 // For one block, the 16 possible dequantized values bf16(level_i * a^) are

@@ -10,16 +10,20 @@
 
 namespace nf4 {
 
-// Workspace layout for quantization with double quantization.
-constexpr size_t kBucketBytes = 256 * sizeof(unsigned long long);
-inline size_t absmax_ws_offset() { return kBucketBytes; }
+// Workspace layout for quantization with double quantization: one row of 256
+// exact-mean accumulators per quantize workgroup (at most kQuantGridMax) plus
+// one for the partial tail block, the 256 column sums, an arrival counter
+// (padded to 256 bytes), then the fp32 absmax of every block.
+constexpr int kQuantGridMax = 1024;
+constexpr size_t kPartialBytes = (size_t)(kQuantGridMax + 2) * 256 * sizeof(unsigned long long) + 256;
+inline size_t absmax_ws_offset() { return kPartialBytes; }
 inline size_t quant_workspace_bytes(int64_t nblocks) {
-  size_t b = kBucketBytes + (size_t)nblocks * sizeof(float);
+  size_t b = kPartialBytes + (size_t)nblocks * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
 
 hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t *packed,
-                           float *absmax_out, unsigned long long *buckets, uint32_t *status,
+                           float *absmax_out, unsigned long long *partials, uint32_t *status,
                            int dq, int8_t *q_out, float *scale_out, float *mean_out,
                            hipStream_t stream);
 

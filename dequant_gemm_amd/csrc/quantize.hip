@@ -7,10 +7,13 @@
 // quantized to 8 bits with their own meta-scales).
 //
 // Kernels, in launch order:
-//   zero_u64_kernel          clears the 256 exact-mean accumulators
-//   quantize_blocks_kernel   full 64-blocks: absmax, codes, packing, accumulators
-//   quantize_tail_kernel     the one partial block at the end, if any
-//   mean_finalize_kernel     exact mean of all absmax values, one rounding
+//   quantize_blocks_kernel   full 64-blocks: absmax, codes, packing; with double
+//                            quantization also one row of 256 exact-mean
+//                            accumulators per workgroup (plain stores)
+//   quantize_tail_kernel     the one partial block at the end, if any (its own
+//                            accumulator row)
+//   mean_reduce_kernel       sums the rows column by column; the last
+//                            workgroup forms the exact mean, one rounding
 //   double_quant_kernel      int8 absmax and one fp32 scale per 256 blocks
 #include "nf4_launch.h"
 
@@ -95,42 +98,55 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
   return word;
 }
 
-__global__ void zero_u64_kernel(unsigned long long *p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0ull;
-}
-
 // Eight lanes per block, eight elements per lane.  Each lane's eight codes
 // form one 32-bit word of the packed output (element 2j in the low nibble of
-// byte j).  With double quantization the block absmax is also accumulated,
-// exactly, as integer significand sums per binary exponent.
+// byte j).  With double quantization each workgroup also sums the significands
+// of its block absmax values per binary exponent (exact integer sums) and
+// stores the 256 sums as its row of `partials`.  The next block's load is in
+// flight while the current block is encoded.
 template <bool BF16, bool DQ>
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     const void *__restrict__ w, int64_t nfull, uint8_t *__restrict__ packed,
-    float *__restrict__ absmax, unsigned long long *__restrict__ buckets, uint32_t *status) {
+    float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status,
+    unsigned int *arrivals) {
   __shared__ Cell cells[129];
   __shared__ unsigned long long lbuck[256];
+  if (DQ && blockIdx.x == 0 && threadIdx.x == 0) *arrivals = 0u;  // for mean_reduce_kernel
   build_cells(cells);
   if (DQ) lbuck[threadIdx.x] = 0ull;
   __syncthreads();
 
   const int part = threadIdx.x & 7;
   const int slot = threadIdx.x >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 32;
+  auto load = [&](int64_t blk, uint4 &u, uint4 &v) {
+    if (BF16) {
+      u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(w) + blk * kBlock + part * 8);
+    } else {
+      const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(w) + blk * kBlock + part * 8);
+      u = p[0];
+      v = p[1];
+    }
+  };
   bool bad = false;
-  for (int64_t blk = (int64_t)blockIdx.x * 32 + slot; blk < nfull; blk += (int64_t)gridDim.x * 32) {
+  int64_t blk = (int64_t)blockIdx.x * 32 + slot;
+  uint4 cu = make_uint4(0, 0, 0, 0), cv = cu;
+  if (blk < nfull) load(blk, cu, cv);
+  for (; blk < nfull; blk += stride) {
+    uint4 nu = make_uint4(0, 0, 0, 0), nv = nu;
+    const int64_t nb = blk + stride < nfull ? blk + stride : nfull - 1;
+    load(nb, nu, nv);
     float x[8];
     if (BF16) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(
-          reinterpret_cast<const uint16_t *>(w) + blk * kBlock + part * 8);
-      x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x);
-      x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
-      x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z);
-      x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
+      x[0] = bf16_lo(cu.x); x[1] = bf16_hi(cu.x);
+      x[2] = bf16_lo(cu.y); x[3] = bf16_hi(cu.y);
+      x[4] = bf16_lo(cu.z); x[5] = bf16_hi(cu.z);
+      x[6] = bf16_lo(cu.w); x[7] = bf16_hi(cu.w);
     } else {
-      const float4 *p = reinterpret_cast<const float4 *>(
-          reinterpret_cast<const float *>(w) + blk * kBlock + part * 8);
-      const float4 u = p[0], v = p[1];
-      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-      x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+      x[0] = __uint_as_float(cu.x); x[1] = __uint_as_float(cu.y);
+      x[2] = __uint_as_float(cu.z); x[3] = __uint_as_float(cu.w);
+      x[4] = __uint_as_float(cv.x); x[5] = __uint_as_float(cv.y);
+      x[6] = __uint_as_float(cv.z); x[7] = __uint_as_float(cv.w);
     }
     // absmax on the magnitude bits: integer order equals float order for
     // non-negative floats, and NaN/inf compare above every finite value
@@ -159,11 +175,12 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
         atomicAdd(&lbuck[e], sig);
       }
     }
+    cu = nu;
+    cv = nv;
   }
   if (DQ) {
     __syncthreads();
-    const unsigned long long v = lbuck[threadIdx.x];
-    if (v) atomicAdd(&buckets[threadIdx.x], v);
+    partials[(int64_t)blockIdx.x * 256 + threadIdx.x] = lbuck[threadIdx.x];
   }
   if (bad && status) atomicOr(status, 1u);
 }
@@ -173,8 +190,11 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 template <bool BF16, bool DQ>
 __global__ __launch_bounds__(64) void quantize_tail_kernel(
     const void *__restrict__ w, int64_t numel, int64_t blk, uint8_t *__restrict__ packed,
-    float *__restrict__ absmax, unsigned long long *__restrict__ buckets, uint32_t *status) {
+    float *__restrict__ absmax, unsigned long long *__restrict__ partial_row, uint32_t *status,
+    unsigned int *clear_arrivals) {
   __shared__ Cell cells[129];
+  // with no full block there is no quantize_blocks_kernel launch to clear it
+  if (DQ && clear_arrivals && threadIdx.x == 0) *clear_arrivals = 0u;
   build_cells(cells);
   __syncthreads();
   const int lane = threadIdx.x;
@@ -198,80 +218,135 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
   if (!valid) code = 0;
   const int upper = __shfl_down(code, 1);
   if (valid && (lane & 1) == 0) packed[blk * (kBlock / 2) + lane / 2] = (uint8_t)(code | (upper << 4));
+  if (DQ) {
+    // this block's accumulator row: zero everywhere but its exponent
+    const uint32_t ex = m >> 23;
+    const unsigned long long sig = (m & 0x7fffffu) | (ex ? 0x800000u : 0u);
+    for (int i = lane; i < 256; i += 64)
+      partial_row[i] = (m < 0x7f800000u && (uint32_t)i == ex) ? sig : 0ull;
+  }
   if (lane == 0) {
     absmax[blk] = __uint_as_float(m);
-    if (m >= 0x7f800000u) {
-      if (status) atomicOr(status, 1u);
-    } else if (DQ) {
-      const uint32_t ex = m >> 23;
-      atomicAdd(&buckets[ex], (unsigned long long)((m & 0x7fffffu) | (ex ? 0x800000u : 0u)));
-    }
+    if (m >= 0x7f800000u && status) atomicOr(status, 1u);
   }
 }
 
 // Exact mean of all block absmax values, rounded once to fp32 (nearest-even).
-// Every finite fp32 is an integer number of 2^-149 units; bucket e holds the
-// sum of the 24-bit significands of the values with biased exponent e, worth
-// 2^(max(e,1)-1) units each.  The sum S (at most ~310 bits) is divided by the
-// block count as a multi-word integer with 32 extra quotient bits, enough to
-// reach below the smallest subnormal, then rounded on the remainder.
-__global__ void mean_finalize_kernel(const unsigned long long *__restrict__ buckets,
-                                     uint32_t nblocks, float *__restrict__ mean_out) {
-  if (threadIdx.x != 0) return;
+// Every finite fp32 is an integer number of 2^-149 units; column e of the
+// accumulator rows holds sums of the 24-bit significands of the values with
+// biased exponent e, worth 2^(max(e,1)-1) units each.  Workgroup e sums
+// column e over all rows; the last workgroup to finish (an arrival counter
+// that the quantize kernel cleared) forms the total S (at most ~310 bits) as
+// a multi-word integer, divides it by the block count with 32 extra quotient
+// bits -- enough to reach below the smallest subnormal -- and rounds on the
+// remainder.
+// `sums` holds the 256 column totals, `nz` a bitmask of the non-zero ones.
+__device__ float mean_from_sums(const unsigned long long *sums, const unsigned long long nz[4],
+                                uint32_t nblocks) {
   constexpr int W = 13;
-  uint32_t num[W];
+  // S * 2^32 as 32-bit digits held in 64-bit slots (carries resolved at the end)
+  unsigned long long slot[W];
 #pragma unroll
-  for (int i = 0; i < W; ++i) num[i] = 0;
-  for (int e = 0; e < 256; ++e) {
-    const unsigned long long v = buckets[e];
-    if (!v) continue;
-    const int sh = (e > 0 ? e : 1) - 1 + 32;  // S * 2^32
-    const int wi = sh >> 5, bi = sh & 31;
-    const unsigned long long lo = v << bi;
-    const uint32_t part[3] = {(uint32_t)lo, (uint32_t)(lo >> 32), bi ? (uint32_t)(v >> (64 - bi)) : 0u};
-    unsigned long long carry = 0;
-    for (int i = wi; i < W; ++i) {
-      const unsigned long long add = (i - wi < 3) ? part[i - wi] : 0ull;
-      const unsigned long long s = (unsigned long long)num[i] + add + carry;
-      num[i] = (uint32_t)s;
-      carry = s >> 32;
-      if (i - wi >= 2 && carry == 0) break;
+  for (int i = 0; i < W; ++i) slot[i] = 0;
+  for (int w = 0; w < 4; ++w) {
+    unsigned long long m = nz[w];
+    while (m) {
+      const int e = 64 * w + __builtin_ctzll(m);
+      m &= m - 1;
+      const unsigned long long v = sums[e];
+      const int sh = (e > 0 ? e : 1) - 1 + 32;
+      const int wi = sh >> 5, bi = sh & 31;
+      const unsigned long long lo = v << bi;
+      slot[wi] += (uint32_t)lo;
+      slot[wi + 1] += (uint32_t)(lo >> 32);
+      if (bi) slot[wi + 2] += (uint32_t)(v >> (64 - bi));
     }
+  }
+  uint32_t num[W];
+  unsigned long long carry = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const unsigned long long t = slot[i] + carry;
+    num[i] = (uint32_t)t;
+    carry = t >> 32;
   }
   uint32_t q[W];
   unsigned long long rem = 0;
+#pragma unroll
   for (int i = W - 1; i >= 0; --i) {
     const unsigned long long cur = (rem << 32) | num[i];
     q[i] = (uint32_t)(cur / nblocks);
     rem = cur % nblocks;
   }
   int L = 0;
-  for (int i = W - 1; i >= 0; --i)
-    if (q[i]) {
-      L = 32 * i + (32 - __clz(q[i]));
-      break;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if (q[i]) L = 32 * i + (32 - __clz(q[i]));
+  if (L == 0) return 0.f;
+  int p = L - 24 > 32 ? L - 24 : 32;  // lsb kept: 24 bits, or the 2^-149 unit
+  auto bits_at = [&](int pos) -> unsigned long long {  // 64 bits of q starting at bit pos
+    const int w = pos >> 5, b = pos & 31;
+    unsigned long long lo = 0, mid = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if (i == w) lo = q[i];
+      if (i == w + 1) mid = q[i];
+      if (i == w + 2) hi = q[i];
     }
-  uint32_t bits = 0;
-  if (L > 0) {
-    int p = L - 24 > 32 ? L - 24 : 32;  // lsb kept: 24 bits, or the 2^-149 unit
-    auto bit = [&](int i) -> uint32_t { return i < 0 ? 0u : (q[i >> 5] >> (i & 31)) & 1u; };
-    uint32_t kept = 0;
-    for (int b = 0; b < 24; ++b) kept |= bit(p + b) << b;
-    const uint32_t round = bit(p - 1);
-    uint32_t sticky = rem != 0 ? 1u : 0u;
-    for (int i = 0; i < p - 1 && !sticky; ++i) sticky |= bit(i);
-    if (round && (sticky || (kept & 1u))) ++kept;
-    if (kept == (1u << 24)) {
-      kept >>= 1;
-      ++p;
-    }
-    // value = kept * 2^(p - 181)
-    if (kept >= (1u << 23))
-      bits = ((uint32_t)(p - 31) << 23) | (kept & 0x7fffffu);
-    else
-      bits = kept;  // subnormal (p == 32)
+    const unsigned long long x = lo | (mid << 32);
+    return b ? (x >> b) | (hi << (64 - b)) : x;
+  };
+  uint32_t kept = (uint32_t)(bits_at(p) & 0xffffffu);
+  const uint32_t round = (uint32_t)(bits_at(p - 1) & 1u);
+  // sticky: any set bit below p-1, or a non-zero remainder
+  bool sticky = rem != 0;
+  const int sb = p - 1;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    if (32 * i + 32 <= sb) sticky |= q[i] != 0;
+    else if (32 * i < sb) sticky |= (q[i] & ((1u << (sb - 32 * i)) - 1u)) != 0;
   }
-  *mean_out = __uint_as_float(bits);
+  if (round && (sticky || (kept & 1u))) ++kept;
+  if (kept == (1u << 24)) {
+    kept >>= 1;
+    ++p;
+  }
+  // value = kept * 2^(p - 181)
+  const uint32_t bits = kept >= (1u << 23) ? (((uint32_t)(p - 31) << 23) | (kept & 0x7fffffu))
+                                           : kept;  // subnormal (p == 32)
+  return __uint_as_float(bits);
+}
+
+__global__ __launch_bounds__(256) void mean_reduce_kernel(
+    const unsigned long long *__restrict__ partials, int nrows, uint32_t nblocks,
+    unsigned long long *__restrict__ colsum, unsigned int *__restrict__ arrivals,
+    float *__restrict__ mean_out) {
+  __shared__ unsigned long long red[256];
+  __shared__ bool last;
+  const int e = blockIdx.x, t = threadIdx.x;
+  unsigned long long acc = 0;  // each partial sum is below 2^55: no overflow
+  for (int r = t; r < nrows; r += 256) acc += partials[(int64_t)r * 256 + e];
+  red[t] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) red[t] += red[t + s];
+    __syncthreads();
+  }
+  if (t == 0) {
+    colsum[e] = red[0];
+    __threadfence();
+    last = atomicAdd(arrivals, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  __shared__ unsigned long long nz[4];
+  const unsigned long long v = __hip_atomic_load(&colsum[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  red[t] = v;
+  const unsigned long long ball = __ballot(v != 0);
+  if ((t & 63) == 0) nz[t >> 6] = ball;
+  __syncthreads();
+  if (t == 0) *mean_out = mean_from_sums(red, nz, nblocks);
 }
 
 // One wave per group of 256 absmax values.
@@ -310,36 +385,43 @@ __global__ __launch_bounds__(64) void double_quant_kernel(const float *__restric
 }  // namespace
 
 hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t *packed,
-                           float *absmax_out, unsigned long long *buckets, uint32_t *status,
+                           float *absmax_out, unsigned long long *partials, uint32_t *status,
                            int dq, int8_t *q_out, float *scale_out, float *mean_out,
                            hipStream_t stream) {
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
   const int64_t nfull = numel / kBlock;
-  if (dq) hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(256), 0, stream, buckets, 256);
+  unsigned long long *colsum = partials ? partials + (int64_t)(kQuantGridMax + 1) * 256 : nullptr;
+  unsigned int *arrivals = partials ? reinterpret_cast<unsigned int *>(colsum + 256) : nullptr;
+  int grid = 0;
   if (nfull > 0) {
-    int64_t grid = (nfull + 31) / 32;
-    if (grid > 8192) grid = 8192;
+    int64_t g64 = (nfull + 31) / 32;
+    grid = (int)(g64 < kQuantGridMax ? g64 : kQuantGridMax);
     const dim3 g((unsigned)grid), b(256);
     if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<true, true>), g, b, 0, stream, w, nfull, packed, absmax_out, buckets, status);
-      else    hipLaunchKernelGGL((quantize_blocks_kernel<true, false>), g, b, 0, stream, w, nfull, packed, absmax_out, buckets, status);
+      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<true, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
+      else    hipLaunchKernelGGL((quantize_blocks_kernel<true, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
     } else {
-      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<false, true>), g, b, 0, stream, w, nfull, packed, absmax_out, buckets, status);
-      else    hipLaunchKernelGGL((quantize_blocks_kernel<false, false>), g, b, 0, stream, w, nfull, packed, absmax_out, buckets, status);
+      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<false, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
+      else    hipLaunchKernelGGL((quantize_blocks_kernel<false, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
     }
   }
+  int rows = grid;
   if (nfull < nblocks) {
     const dim3 g(1), b(64);
+    unsigned long long *row = partials ? partials + (int64_t)grid * 256 : nullptr;
+    unsigned int *clr = nfull == 0 ? arrivals : nullptr;
     if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, buckets, status);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, buckets, status);
+      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
+      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
     } else {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, buckets, status);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, buckets, status);
+      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
+      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
     }
+    ++rows;
   }
   if (dq) {
-    hipLaunchKernelGGL(mean_finalize_kernel, dim3(1), dim3(64), 0, stream, buckets, (uint32_t)nblocks, mean_out);
+    hipLaunchKernelGGL(mean_reduce_kernel, dim3(256), dim3(256), 0, stream, partials, rows, (uint32_t)nblocks,
+                       colsum, arrivals, mean_out);
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
     hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ngroups), dim3(64), 0, stream, absmax_out, nblocks, mean_out, q_out, scale_out);
   }

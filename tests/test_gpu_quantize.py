@@ -122,6 +122,37 @@ def test_deterministic_and_mean_is_order_free():
     assert u32(c.absmax_mean)[0] == u32(a.absmax_mean)[0]
 
 
+def _blocks_with_absmax(values, seed):
+    """A fp32 weight whose 64-blocks have exactly the given absmax values."""
+    rng = np.random.default_rng(seed)
+    a = np.asarray(values, np.float32)
+    w = (rng.uniform(-1, 1, (a.size, 64)) * a[:, None]).astype(np.float32)
+    w[:, 5] = a                       # the block maximum, attained exactly
+    w = np.minimum(np.maximum(w, -a[:, None]), a[:, None])
+    return torch.from_numpy(w)
+
+
+@pytest.mark.parametrize("case", ["subnormal", "huge", "wide", "tie_even", "tie_odd", "single"])
+def test_exact_mean_edge_cases(case):
+    """The device's exact mean against the oracle where rounding is delicate."""
+    rng = np.random.default_rng(7)
+    one = np.float32(1.0)
+    up = np.nextafter(one, np.float32(2))
+    if case == "subnormal":
+        vals = (np.abs(rng.standard_normal(777)) * 1e-41).astype(np.float32) + np.float32(1e-45)
+    elif case == "huge":
+        vals = np.float32(3.0e38) - (np.abs(rng.standard_normal(300)) * 1e36).astype(np.float32)
+    elif case == "wide":
+        vals = np.abs(rng.standard_normal(2000) * 10.0 ** rng.integers(-37, 37, 2000)).astype(np.float32)
+    elif case == "tie_even":
+        vals = np.array([one, up], np.float32)           # mean 1 + 2^-24: a tie, rounds to 1.0
+    elif case == "tie_odd":
+        vals = np.array([up, np.nextafter(up, np.float32(2))], np.float32)  # tie, rounds up to even
+    else:
+        vals = np.array([np.float32(0.123)], np.float32)
+    _check_roundtrip(_blocks_with_absmax(vals, 3), True, f"mean {case}")
+
+
 @pytest.mark.parametrize("dq", [True, False])
 def test_decode_weight_full(dq):
     _check_roundtrip(synth.decode_weight(0), dq, f"decode dq={dq}")
