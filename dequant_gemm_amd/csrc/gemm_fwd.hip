@@ -14,7 +14,8 @@
 //                     rows, its eight waves split K; every weight byte is read
 //                     once, all of a lane's loads are issued together.
 //   fwd_large_kernel  M > 16, matrix-core-bound: 256x256 output tiles; X
-//                     staged through LDS (double-buffered), each wave
+//                     staged through LDS (double-buffered, filled by direct
+//                     global->LDS loads), each wave
 //                     dequantizes its own 64 weight rows straight into MFMA
 //                     operand registers (no LDS round trip, no duplicate
 //                     dequantization inside the workgroup).
@@ -119,11 +120,13 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
 #define NF4_FWD_SCHED 1
 #endif
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_ROW = BK * 2 + 16;  // bytes; 16 bytes of padding keep ds_read_b128 conflict-free
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int XTILE = BM * BK * 2;          // 64 KiB: 256 rows of 256 bytes
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
-// takes a contiguous run of tiles, then walk tiles in groups of 8 M-tiles so
+// takes a contiguous run of tiles, then walk tiles in groups of 4 M-tiles so
 // that workgroups running together share X row panels and weight columns in
 // their XCD's L2.
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -131,7 +134,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
   const int q = total / 8, r = total % 8;
   const int xcd = bid % 8, idx = bid / 8;
   const int t = xcd * q + (xcd < r ? xcd : r) + idx;
-  constexpr int G = 8;
+  constexpr int G = 4;
   const int per_group = G * tiles_n;
   const int group = t / per_group;
   const int first_m = group * G;
@@ -141,50 +144,150 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
   tn = in_group / gsize;
 }
 
-template <bool Y_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_large_kernel(const uint16_t *__restrict__ X, int64_t M,
-                                                        int64_t N, int64_t K,
-                                                        const uint8_t *__restrict__ packed,
-                                                        AbsmaxSrc src, void *__restrict__ Y,
-                                                        int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][BM * LDS_ROW];
+template <bool DQ>
+__device__ __forceinline__ AbsmaxRaw load_raw(const AbsmaxSrc &s, int64_t blk) {
+  AbsmaxRaw r;
+  if (DQ) {
+    r.q = s.q[blk];
+    r.v = s.scale[blk >> 8];
+  } else {
+    r.q = 0;
+    r.v = s.absmax[blk];
+  }
+  return r;
+}
+
+// A lane's weight state for one K-step: the 64 codes (one whole block) of
+// each of its two columns and the blocks' absmax state.
+struct Codes {
+  uint4 c0a, c0b, c1a, c1b;
+  AbsmaxRaw r0, r1;
+};
+
+// The 128 MFMAs of one 128-wide K-step for a wave's 256x64 slice.  Lane group
+// kg owns K range kg*64 .. +63 of the step -- one whole block per column, one
+// LUT per 64 weights; MFMA slice j (0..7) takes elements 8j..8j+7 of it from
+// both operands.  Dequantization of slice j+1 and the A-fragment LDS reads of
+// slice j+1 are issued while the 16 MFMAs of slice j run.  `xt` is the X tile
+// in LDS; row R's 16-byte chunk c sits at chunk c ^ (R & 7).
+template <bool DQ>
+__device__ __forceinline__ void mma_tile(f32x16 (&acc)[8][2], const uint8_t *xt, int bl, int kg,
+                                         const Codes &cd, float mu, bool real) {
+  const Lut t0 = make_lut(real ? ahat_of(cd.r0, DQ, mu) : 0.f);
+  const Lut t1 = make_lut(real ? ahat_of(cd.r1, DQ, mu) : 0.f);
+  const uint32_t w0[8] = {cd.c0a.x, cd.c0a.y, cd.c0a.z, cd.c0a.w, cd.c0b.x, cd.c0b.y, cd.c0b.z, cd.c0b.w};
+  const uint32_t w1[8] = {cd.c1a.x, cd.c1a.y, cd.c1a.z, cd.c1a.w, cd.c1b.x, cd.c1b.y, cd.c1b.z, cd.c1b.w};
+  const uint8_t *row = xt + bl * 256;
+  const int sw = bl & 7;
+  uint4 a[8];
+  uint32_t b0[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    a[i] = *reinterpret_cast<const uint4 *>(row + 32 * i * 256 + (((kg * 8) ^ sw) << 4));
+  dequant8(w0[0], t0, b0);
+  dequant8(w1[0], t1, b1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint4 an[8];
+    uint32_t bn0[4], bn1[4];
+    if (j < 7) {
+      const int off = ((kg * 8 + j + 1) ^ sw) << 4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) an[i] = *reinterpret_cast<const uint4 *>(row + 32 * i * 256 + off);
+      dequant8(w0[j + 1], t0, bn0);
+      dequant8(w1[j + 1], t1, bn1);
+    }
+    const bf16x8 bv0 = as_bf16x8(b0), bv1 = as_bf16x8(b1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 av = as_bf16x8(a[i]);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv1, acc[i][1], 0, 0, 0);
+    }
+    if (j < 7) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = an[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        b0[e] = bn0[e];
+        b1[e] = bn1[e];
+      }
+    }
+  }
+#if NF4_FWD_SCHED == 1
+  __builtin_amdgcn_iglp_opt(1);
+#elif NF4_FWD_SCHED == 2
+  __builtin_amdgcn_iglp_opt(0);
+#endif
+}
+
+// X tiles (256 rows x 128 K) reach LDS by direct global->LDS loads (no
+// register staging), double-buffered: the next tile loads during a whole
+// K-step of MFMA work.  Wave w's load instruction i fills LDS rows
+// 4(16w + i) .. +3; lane l takes row 4(16w + i) + l/16 and physical chunk
+// l%16, which holds logical chunk (l%16) ^ (row & 7) -- the swizzle that keeps
+// the MFMA-fragment reads (eight rows, one logical chunk) free of LDS bank
+// conflicts.  One barrier per K-step, after this wave's loads of the tile
+// about to be read have completed.
+template <bool Y_BF16, bool DQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_large_kernel(
+    const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    AbsmaxSrc src, void *__restrict__ Y, int tiles_m, int tiles_n) {
+  // two separate arrays (not one indexed by stage) so that the compiler can
+  // tell the tile being read from the tile being loaded and does not make the
+  // reads wait for those loads
+  __shared__ __attribute__((aligned(1024))) uint8_t xs0[XTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs1[XTILE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const float mu = src.dq ? *src.mean : 0.f;
+  const float mu = DQ ? *src.mean : 0.f;
 
   // B operand: this lane's two weight rows (one per 32-column subtile).
   // Columns past N and rows past M load in-bounds stand-ins; their outputs
   // are never stored, so every load is unconditional.
   const int bl = lane & 31, kg = lane >> 5;
   int64_t ncol[2];
-  const uint8_t *wp[2];
+  const uint4 *wq[2];
   int64_t blk0[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     ncol[t] = n0 + 64 * wave + 32 * t + bl;
     const int64_t nn = ncol[t] < N ? ncol[t] : N - 1;
-    wp[t] = packed + nn * (K / 2) + kg * 16;
-    blk0[t] = nn * (K / kBlock);
+    wq[t] = reinterpret_cast<const uint4 *>(packed + nn * (K / 2) + kg * 32);
+    blk0[t] = nn * (K / kBlock) + kg;
   }
 
-  // X staging: eight threads per 128-byte row segment, 32 rows per pass
-  const int xr = tid >> 3, xc = tid & 7;
-  const uint16_t *xp[8];
+  // direct-to-LDS sources: row 4(16w + i) + lane/16, logical chunk (lane%16) ^ (row & 7)
+  const int rsub = lane >> 4;
+  const uint16_t *xsrc[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = m0 + xr + 32 * i;
-    xp[i] = X + (row < M ? row : M - 1) * K + xc * 8;
+  for (int i = 0; i < 16; ++i) {
+    const int r = 4 * (16 * wave + i) + rsub;
+    const int chunk = (lane & 15) ^ (r & 7);
+    const int64_t row = m0 + r;
+    xsrc[i] = X + (row < M ? row : M - 1) * K + chunk * 8;
   }
-
-  const int64_t nk = K / BK;
-  const uint4 *xq[8];
+  const int64_t nk = (K + BK - 1) / BK;
+  const bool half = (K % BK) != 0;
+  auto issue_x = [&](int64_t kt, uint8_t *dst) {
+    // in a 64-wide last step, logical chunks 8..15 (lane bit 3) lie past the
+    // row's end: load the chunk 64 columns back instead (it meets a^ = 0)
+    const int64_t koff = kt * BK - ((half && kt == nk - 1 && (lane & 8)) ? 64 : 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xq[i] = reinterpret_cast<const uint4 *>(xp[i]);
-  const uint4 *wq0 = reinterpret_cast<const uint4 *>(wp[0]);
-  const uint4 *wq1 = reinterpret_cast<const uint4 *>(wp[1]);
-  uint8_t *xs = &smem[0][(xr * LDS_ROW) + xc * 16];
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xsrc[i] + koff),
+                                       (lds_void *)(dst + (16 * wave + i) * 1024), 16, 0, 0);
+  };
+  auto issue_codes = [&](int64_t kt, Codes &cd) {
+    cd.c0a = wq[0][kt * 4];
+    cd.c0b = wq[0][kt * 4 + 1];
+    cd.c1a = wq[1][kt * 4];
+    cd.c1b = wq[1][kt * 4 + 1];
+    cd.r0 = load_raw<DQ>(src, blk0[0] + 2 * kt);
+    cd.r1 = load_raw<DQ>(src, blk0[1] + 2 * kt);
+  };
 
   f32x16 acc[8][2];
 #pragma unroll
@@ -194,107 +297,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
 
-  // prologue: tile 0 to LDS, its codes in registers
-  uint4 x0 = xq[0][0], x1 = xq[1][0], x2 = xq[2][0], x3 = xq[3][0];
-  uint4 x4 = xq[4][0], x5 = xq[5][0], x6 = xq[6][0], x7 = xq[7][0];
-  uint4 cn0 = wq0[0], cn1 = wq1[0];
-  AbsmaxRaw rn0 = load_absmax_raw(src, blk0[0]), rn1 = load_absmax_raw(src, blk0[1]);
-  {
-    uint8_t *d = xs;
-    *reinterpret_cast<uint4 *>(d + 0 * 32 * LDS_ROW) = x0;
-    *reinterpret_cast<uint4 *>(d + 1 * 32 * LDS_ROW) = x1;
-    *reinterpret_cast<uint4 *>(d + 2 * 32 * LDS_ROW) = x2;
-    *reinterpret_cast<uint4 *>(d + 3 * 32 * LDS_ROW) = x3;
-    *reinterpret_cast<uint4 *>(d + 4 * 32 * LDS_ROW) = x4;
-    *reinterpret_cast<uint4 *>(d + 5 * 32 * LDS_ROW) = x5;
-    *reinterpret_cast<uint4 *>(d + 6 * 32 * LDS_ROW) = x6;
-    *reinterpret_cast<uint4 *>(d + 7 * 32 * LDS_ROW) = x7;
-  }
-  __syncthreads();
-
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    const uint4 cc0 = cn0, cc1 = cn1;
-    const AbsmaxRaw r0 = rn0, r1 = rn1;
-    // next tile's loads (the last iteration re-reads tile nk-1, harmlessly)
-    const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-    const int64_t xo = kn * (BK / 8);
-    x0 = xq[0][xo]; x1 = xq[1][xo]; x2 = xq[2][xo]; x3 = xq[3][xo];
-    x4 = xq[4][xo]; x5 = xq[5][xo]; x6 = xq[6][xo]; x7 = xq[7][xo];
-    cn0 = wq0[kn * 2];
-    cn1 = wq1[kn * 2];
-    rn0 = load_absmax_raw(src, blk0[0] + kn);
-    rn1 = load_absmax_raw(src, blk0[1] + kn);
-
-    const Lut t0 = make_lut(ahat_of(r0, src.dq, mu)), t1 = make_lut(ahat_of(r1, src.dq, mu));
-    const uint32_t w0[4] = {cc0.x, cc0.y, cc0.z, cc0.w};
-    const uint32_t w1[4] = {cc1.x, cc1.y, cc1.z, cc1.w};
-    const uint8_t *abase = &smem[cur][bl * LDS_ROW + kg * 64];
-    // Software pipeline over the four 16-wide K slices: the A fragments and
-    // the dequantized B fragments of slice j+1 are produced while the 16
-    // MFMAs of slice j run.
-    uint4 a[8];
-    uint32_t b0[4], b1[4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(abase + 32 * i * LDS_ROW);
-    dequant8(w0[0], t0, b0);
-    dequant8(w1[0], t1, b1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 an[8];
-      uint32_t bn0[4], bn1[4];
-      if (j < 3) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          an[i] = *reinterpret_cast<const uint4 *>(abase + 32 * i * LDS_ROW + 16 * (j + 1));
-        dequant8(w0[j + 1], t0, bn0);
-        dequant8(w1[j + 1], t1, bn1);
-      }
-      const bf16x8 bv0 = as_bf16x8(b0), bv1 = as_bf16x8(b1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8 av = as_bf16x8(a[i]);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv1, acc[i][1], 0, 0, 0);
-      }
-#if NF4_FWD_SCHED == 3
-      if (j < 3) {
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          if (g < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-#endif
-      if (j < 3) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = an[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          b0[e] = bn0[e];
-          b1[e] = bn1[e];
-        }
-      }
+  // K-steps run in pairs (one per LDS buffer); a step past the last real one
+  // re-reads tile nk-1 with a^ forced to 0, so it adds exact zeros.  K % 64 ==
+  // 0 but K % 128 may be 64: then the last real step's upper half (lane group
+  // kg = 1) also gets a^ = 0.
+  const int64_t nk2 = (nk + 1) & ~(int64_t)1;
+  Codes cur, nxt;
+  auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
+  // the upper half of a 64-wide last step points one block past the row: load
+  // the lower half's block instead (its values are multiplied by a^ = 0)
+  auto real_of = [&](int64_t kt) { return kt < nk && !(half && kt == nk - 1 && kg == 1); };
+  auto issue_codes_safe = [&](int64_t kt, Codes &cd) {
+    if (half && kt == nk - 1 && kg == 1) {
+      // stay inside the row: reuse the lower half's codes and block
+      cd.c0a = wq[0][kt * 4 - 4 + 2];
+      cd.c0b = wq[0][kt * 4 - 4 + 3];
+      cd.c1a = wq[1][kt * 4 - 4 + 2];
+      cd.c1b = wq[1][kt * 4 - 4 + 3];
+      cd.r0 = load_raw<DQ>(src, blk0[0] + 2 * kt - 1);
+      cd.r1 = load_raw<DQ>(src, blk0[1] + 2 * kt - 1);
+    } else {
+      issue_codes(kt, cd);
     }
-#if NF4_FWD_SCHED == 1
-    __builtin_amdgcn_iglp_opt(1);
-#elif NF4_FWD_SCHED == 2
-    __builtin_amdgcn_iglp_opt(0);
-#endif
-    {
-      uint8_t *d = xs + (cur ^ 1) * (BM * LDS_ROW);
-      *reinterpret_cast<uint4 *>(d + 0 * 32 * LDS_ROW) = x0;
-      *reinterpret_cast<uint4 *>(d + 1 * 32 * LDS_ROW) = x1;
-      *reinterpret_cast<uint4 *>(d + 2 * 32 * LDS_ROW) = x2;
-      *reinterpret_cast<uint4 *>(d + 3 * 32 * LDS_ROW) = x3;
-      *reinterpret_cast<uint4 *>(d + 4 * 32 * LDS_ROW) = x4;
-      *reinterpret_cast<uint4 *>(d + 5 * 32 * LDS_ROW) = x5;
-      *reinterpret_cast<uint4 *>(d + 6 * 32 * LDS_ROW) = x6;
-      *reinterpret_cast<uint4 *>(d + 7 * 32 * LDS_ROW) = x7;
-    }
-    __syncthreads();
+  };
+  issue_x(0, xs0);
+  issue_codes_safe(0, cur);
+  auto step = [&](int64_t kt, const uint8_t *rd, uint8_t *wr) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    const int64_t kn = clampk(kt + 1);
+    issue_x(kn, wr);
+    issue_codes_safe(kn, nxt);
+    mma_tile<DQ>(acc, rd, bl, kg, cur, mu, real_of(kt));
+    cur = nxt;
+  };
+  for (int64_t kt = 0; kt < nk2; kt += 2) {
+    step(kt, xs0, xs1);
+    step(kt + 1, xs1, xs0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
 #pragma unroll
@@ -331,10 +372,17 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
   } else {
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 g((unsigned)(tiles_m * tiles_n)), b(256);
-    if (y_is_bf16)
-      hipLaunchKernelGGL((fwd_large_kernel<true>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
-    else
-      hipLaunchKernelGGL((fwd_large_kernel<false>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
+    if (src.dq) {
+      if (y_is_bf16)
+        hipLaunchKernelGGL((fwd_large_kernel<true, true>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
+      else
+        hipLaunchKernelGGL((fwd_large_kernel<false, true>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
+    } else {
+      if (y_is_bf16)
+        hipLaunchKernelGGL((fwd_large_kernel<true, false>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
+      else
+        hipLaunchKernelGGL((fwd_large_kernel<false, false>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
+    }
   }
   return hipGetLastError();
 }

@@ -1,7 +1,7 @@
 // nf4_api.hip -- the C ABI declared in include/nf4.h: argument validation,
 // buffer-size arithmetic and kernel dispatch.  Validation touches no HIP API,
 // so every error path can be exercised on a machine without a GPU.
-#include "../../include/nf4.h"
+#include "nf4.h"
 #include "nf4_launch.h"
 
 namespace {
