@@ -13,12 +13,12 @@
 //   fwd_small_kernel  M <= 16, streaming-bound: one workgroup per 16 weight
 //                     rows, its eight waves split K; every weight byte is read
 //                     once, all of a lane's loads are issued together.
-//   fwd_large_kernel  M > 16, matrix-core-bound: 256x256 output tiles; X
+//   fwd_large_kernel  M > 16, matrix-core-bound: 512x128 output tiles; X
 //                     staged through LDS (double-buffered, filled by direct
-//                     global->LDS loads), each wave
-//                     dequantizes its own 64 weight rows straight into MFMA
-//                     operand registers (no LDS round trip, no duplicate
-//                     dequantization inside the workgroup).
+//                     global->LDS loads), each wave dequantizes its own 32
+//                     weight rows straight into MFMA operand registers (no LDS
+//                     round trip, no duplicate dequantization inside the
+//                     workgroup).
 #include "nf4_launch.h"
 
 namespace nf4 {
@@ -113,28 +113,40 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
 }
 
 // ----------------------------------------------------------------- large M
-
-// Instruction-scheduling strategy for the K loop (1: the compiler's
-// single-wave MFMA interleave, the fastest measured on gfx950).
-#ifndef NF4_FWD_SCHED
-#define NF4_FWD_SCHED 1
-#endif
-
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int XTILE = BM * BK * 2;          // 64 KiB: 256 rows of 256 bytes
+//
+// Workgroup tile 512 (M) x 128 (N), four waves, one per SIMD; wave w owns the
+// 32 output columns n0 + 32w .. +31 over all 512 rows: 16 MFMA 32x32x16 tiles
+// stacked along M, 256 accumulator registers.  Each dequantized B fragment is
+// therefore multiplied by 16 A fragments, which keeps the dequantization's
+// VALU work a small fraction of the MFMA time.  Each wave dequantizes only its
+// own columns; the weight never passes through LDS.
+//
+// K advances in steps of 64 (one quantization block): per step a lane holds
+// one 16-byte code chunk (32 codes) and one LUT.  Lane group kg = l/32 owns K
+// range 32kg .. 32kg+31 of the step and MFMA slice j (0..3) takes elements
+// 8j .. 8j+7 of it from both operands (A and B only have to agree on the K
+// index of each slot).
+//
+// X tiles (512 rows x 64 K, 64 KiB) reach LDS by direct global->LDS loads,
+// double-buffered.  The barrier that hands a tile over sits in the middle of
+// the last slice of a step: the second half of that slice's MFMAs covers the
+// first A-fragment reads of the next step and the next tile's load issue.
+constexpr int BM = 512, BN = 128, BK = 64;
+constexpr int XROW = BK * 2;                 // 128-byte LDS rows
+constexpr int XTILE = BM * XROW;             // 64 KiB
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
-// takes a contiguous run of tiles, then walk tiles in groups of 4 M-tiles so
-// that workgroups running together share X row panels and weight columns in
-// their XCD's L2.
+// takes a contiguous run of tiles, then walk tiles in groups of 2 M-tiles so
+// that the workgroups an XCD runs together share X tiles and weight codes in
+// its L2.
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
   const int total = tiles_m * tiles_n;
   const int q = total / 8, r = total % 8;
   const int xcd = bid % 8, idx = bid / 8;
   const int t = xcd * q + (xcd < r ? xcd : r) + idx;
-  constexpr int G = 4;
+  constexpr int G = 2;
   const int per_group = G * tiles_n;
   const int group = t / per_group;
   const int first_m = group * G;
@@ -157,179 +169,215 @@ __device__ __forceinline__ AbsmaxRaw load_raw(const AbsmaxSrc &s, int64_t blk) {
   return r;
 }
 
-// A lane's weight state for one K-step: the 64 codes (one whole block) of
-// each of its two columns and the blocks' absmax state.
-struct Codes {
-  uint4 c0a, c0b, c1a, c1b;
-  AbsmaxRaw r0, r1;
+// A lane's weight state for one K-step: 32 codes and the block's absmax state.
+struct StepCodes {
+  uint4 w;
+  AbsmaxRaw r;
 };
 
-// The 128 MFMAs of one 128-wide K-step for a wave's 256x64 slice.  Lane group
-// kg owns K range kg*64 .. +63 of the step -- one whole block per column, one
-// LUT per 64 weights; MFMA slice j (0..7) takes elements 8j..8j+7 of it from
-// both operands.  Dequantization of slice j+1 and the A-fragment LDS reads of
-// slice j+1 are issued while the 16 MFMAs of slice j run.  `xt` is the X tile
-// in LDS; row R's 16-byte chunk c sits at chunk c ^ (R & 7).
-template <bool DQ>
-__device__ __forceinline__ void mma_tile(f32x16 (&acc)[8][2], const uint8_t *xt, int bl, int kg,
-                                         const Codes &cd, float mu, bool real) {
-  const Lut t0 = make_lut(real ? ahat_of(cd.r0, DQ, mu) : 0.f);
-  const Lut t1 = make_lut(real ? ahat_of(cd.r1, DQ, mu) : 0.f);
-  const uint32_t w0[8] = {cd.c0a.x, cd.c0a.y, cd.c0a.z, cd.c0a.w, cd.c0b.x, cd.c0b.y, cd.c0b.z, cd.c0b.w};
-  const uint32_t w1[8] = {cd.c1a.x, cd.c1a.y, cd.c1a.z, cd.c1a.w, cd.c1b.x, cd.c1b.y, cd.c1b.z, cd.c1b.w};
-  const uint8_t *row = xt + bl * 256;
-  const int sw = bl & 7;
-  uint4 a[8];
-  uint32_t b0[4], b1[4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    a[i] = *reinterpret_cast<const uint4 *>(row + 32 * i * 256 + (((kg * 8) ^ sw) << 4));
-  dequant8(w0[0], t0, b0);
-  dequant8(w1[0], t1, b1);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint4 an[8];
-    uint32_t bn0[4], bn1[4];
-    if (j < 7) {
-      const int off = ((kg * 8 + j + 1) ^ sw) << 4;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) an[i] = *reinterpret_cast<const uint4 *>(row + 32 * i * 256 + off);
-      dequant8(w0[j + 1], t0, bn0);
-      dequant8(w1[j + 1], t1, bn1);
-    }
-    const bf16x8 bv0 = as_bf16x8(b0), bv1 = as_bf16x8(b1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x8 av = as_bf16x8(a[i]);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv1, acc[i][1], 0, 0, 0);
-    }
-    if (j < 7) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = an[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        b0[e] = bn0[e];
-        b1[e] = bn1[e];
-      }
-    }
-  }
-#if NF4_FWD_SCHED == 1
-  __builtin_amdgcn_iglp_opt(1);
-#elif NF4_FWD_SCHED == 2
-  __builtin_amdgcn_iglp_opt(0);
-#endif
+__device__ __forceinline__ void sched_cut() { __builtin_amdgcn_sched_barrier(0); }
+
+template <typename T>
+__device__ __forceinline__ const uint8_t *uniform_ptr(const T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
 }
 
-// X tiles (256 rows x 128 K) reach LDS by direct global->LDS loads (no
-// register staging), double-buffered: the next tile loads during a whole
-// K-step of MFMA work.  Wave w's load instruction i fills LDS rows
-// 4(16w + i) .. +3; lane l takes row 4(16w + i) + l/16 and physical chunk
-// l%16, which holds logical chunk (l%16) ^ (row & 7) -- the swizzle that keeps
-// the MFMA-fragment reads (eight rows, one logical chunk) free of LDS bank
-// conflicts.  One barrier per K-step, after this wave's loads of the tile
-// about to be read have completed.
+__device__ __forceinline__ void mfma2(f32x16 &c0, f32x16 &c1, const uint4 &a0, const uint4 &a1, const uint32_t b[4]) {
+  const bf16x8 bv = as_bf16x8(b);
+  c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bv, c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bv, c1, 0, 0, 0);
+}
+
+// Entries 4q .. 4q+3 of the LUT of bf16(level_i * a^) (one quarter, so that
+// the work can be spread between MFMAs).
+__device__ __forceinline__ void make_lut_quarter(float ahat, int q, Lut &t) {
+  const uint32_t p0 = pack_bf16x2(__fmul_rn(level(4 * q), ahat), __fmul_rn(level(4 * q + 1), ahat));
+  const uint32_t p1 = pack_bf16x2(__fmul_rn(level(4 * q + 2), ahat), __fmul_rn(level(4 * q + 3), ahat));
+  t.lo[q] = perm(p1, p0, 0x06040200u);
+  t.hi[q] = perm(p1, p0, 0x07050301u);
+}
+
 template <bool Y_BF16, bool DQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_large_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, void *__restrict__ Y, int tiles_m, int tiles_n) {
   // two separate arrays (not one indexed by stage) so that the compiler can
-  // tell the tile being read from the tile being loaded and does not make the
-  // reads wait for those loads
+  // tell the tile being read from the tile being loaded
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[XTILE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[XTILE];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const float mu = DQ ? *src.mean : 0.f;
-
-  // B operand: this lane's two weight rows (one per 32-column subtile).
-  // Columns past N and rows past M load in-bounds stand-ins; their outputs
-  // are never stored, so every load is unconditional.
   const int bl = lane & 31, kg = lane >> 5;
-  int64_t ncol[2];
-  const uint4 *wq[2];
-  int64_t blk0[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    ncol[t] = n0 + 64 * wave + 32 * t + bl;
-    const int64_t nn = ncol[t] < N ? ncol[t] : N - 1;
-    wq[t] = reinterpret_cast<const uint4 *>(packed + nn * (K / 2) + kg * 32);
-    blk0[t] = nn * (K / kBlock) + kg;
-  }
 
-  // direct-to-LDS sources: row 4(16w + i) + lane/16, logical chunk (lane%16) ^ (row & 7)
-  const int rsub = lane >> 4;
-  const uint16_t *xsrc[16];
+  // B operand: this lane's weight row; a column past N loads row N-1 (its
+  // outputs are never stored).
+  const int64_t ncol = n0 + 32 * wave + bl;
+  const int64_t nc = ncol < N ? ncol : N - 1;
+  const uint8_t *wq = packed + nc * (K / 2) + kg * 16;
+  const int64_t blk0 = nc * (K / kBlock);
+
+  // X tile loads, buffer-to-LDS: wave w's load i fills LDS bytes
+  // (16w + i) * 1024 .. +1023, i.e. tile rows 8(16w + i) .. +7; lane l takes
+  // row 8(16w + i) + l/8 and physical 16-byte chunk l%8, which holds logical
+  // chunk (l%8) ^ ((row/2) & 7).  One buffer descriptor per wave and step,
+  // based at the wave's first row and sized to its rows that exist: the
+  // lanes of rows past M fall outside it and load zeros.
+  const int64_t wrow0 = m0 + 128 * wave;
+  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 128 ? 128 : M - wrow0);
+  // offsets and sizes are 32-bit: K < 2^24 (checked by the launcher)
+  // (both made explicitly wave-uniform: a buffer descriptor lives in SGPRs)
+  const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * K * 2));
+  const uint8_t *xwave = uniform_ptr(X + (wrows > 0 ? wrow0 : 0) * K);
+  uint32_t xvoff[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int r = 4 * (16 * wave + i) + rsub;
-    const int chunk = (lane & 15) ^ (r & 7);
-    const int64_t row = m0 + r;
-    xsrc[i] = X + (row < M ? row : M - 1) * K + chunk * 8;
+    const int r = 8 * i + (lane >> 3);                             // row within the wave's 128
+    xvoff[i] = (uint32_t)(r * K * 2) + ((uint32_t)((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
-  const int64_t nk = (K + BK - 1) / BK;
-  const bool half = (K % BK) != 0;
-  auto issue_x = [&](int64_t kt, uint8_t *dst) {
-    // in a 64-wide last step, logical chunks 8..15 (lane bit 3) lie past the
-    // row's end: load the chunk 64 columns back instead (it meets a^ = 0)
-    const int64_t koff = kt * BK - ((half && kt == nk - 1 && (lane & 8)) ? 64 : 0);
+  // A fragments: lane l reads row 32i + l%32, logical chunk 4kg + j of slice j,
+  // stored at chunk (4kg + j) ^ ((row/2) & 7) (the row's low five bits are l%32).
+  int aoff[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xsrc[i] + koff),
-                                       (lds_void *)(dst + (16 * wave + i) * 1024), 16, 0, 0);
-  };
-  auto issue_codes = [&](int64_t kt, Codes &cd) {
-    cd.c0a = wq[0][kt * 4];
-    cd.c0b = wq[0][kt * 4 + 1];
-    cd.c1a = wq[1][kt * 4];
-    cd.c1b = wq[1][kt * 4 + 1];
-    cd.r0 = load_raw<DQ>(src, blk0[0] + 2 * kt);
-    cd.r1 = load_raw<DQ>(src, blk0[1] + 2 * kt);
-  };
+  for (int j = 0; j < 4; ++j) aoff[j] = bl * XROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
 
-  f32x16 acc[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
-
-  // K-steps run in pairs (one per LDS buffer); a step past the last real one
-  // re-reads tile nk-1 with a^ forced to 0, so it adds exact zeros.  K % 64 ==
-  // 0 but K % 128 may be 64: then the last real step's upper half (lane group
-  // kg = 1) also gets a^ = 0.
-  const int64_t nk2 = (nk + 1) & ~(int64_t)1;
-  Codes cur, nxt;
+  const int64_t nk = K / BK;
+  const int64_t nk2 = (nk + 1) & ~(int64_t)1;  // steps run in pairs; a padded step has a^ = 0
   auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
-  // the upper half of a 64-wide last step points one block past the row: load
-  // the lower half's block instead (its values are multiplied by a^ = 0)
-  auto real_of = [&](int64_t kt) { return kt < nk && !(half && kt == nk - 1 && kg == 1); };
-  auto issue_codes_safe = [&](int64_t kt, Codes &cd) {
-    if (half && kt == nk - 1 && kg == 1) {
-      // stay inside the row: reuse the lower half's codes and block
-      cd.c0a = wq[0][kt * 4 - 4 + 2];
-      cd.c0b = wq[0][kt * 4 - 4 + 3];
-      cd.c1a = wq[1][kt * 4 - 4 + 2];
-      cd.c1b = wq[1][kt * 4 - 4 + 3];
-      cd.r0 = load_raw<DQ>(src, blk0[0] + 2 * kt - 1);
-      cd.r1 = load_raw<DQ>(src, blk0[1] + 2 * kt - 1);
-    } else {
-      issue_codes(kt, cd);
-    }
+  auto xrsrc = [&](int64_t kt) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + clampk(kt) * (BK * 2)), (short)0,
+                                             wbytes, 0x00020000);
   };
-  issue_x(0, xs0);
-  issue_codes_safe(0, cur);
-  auto step = [&](int64_t kt, const uint8_t *rd, uint8_t *wr) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    const int64_t kn = clampk(kt + 1);
-    issue_x(kn, wr);
-    issue_codes_safe(kn, nxt);
-    mma_tile<DQ>(acc, rd, bl, kg, cur, mu, real_of(kt));
-    cur = nxt;
+  auto issue_x1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t *dst, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (16 * wave + i) * 1024), 16, xvoff[i], 0, 0, 0);
+  };
+  auto issue_codes = [&](int64_t kt, StepCodes &c) {
+    const int64_t k = clampk(kt);
+    c.w = *reinterpret_cast<const uint4 *>(wq + k * (BK / 2));
+    c.r = load_raw<DQ>(src, blk0 + k);
+  };
+  auto ahat_at = [&](int64_t kt, const StepCodes &c) { return kt < nk ? ahat_of(c.r, DQ, mu) : 0.f; };
+
+  f32x16 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  uint4 a0[16], a1[16];
+  uint32_t b0[4], b1[4];
+  uint4 cw;        // codes of the current step
+  Lut lut;         // LUT of the current step
+  StepCodes cn;    // codes of the next step (in flight)
+
+  // prologue: step 0's codes, LUT, first B fragment and first A fragments;
+  // step 1's codes and tile in flight
+  issue_codes(0, cn);
+  {
+    const __amdgpu_buffer_rsrc_t rs = xrsrc(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_x1(rs, xs0, i);
+  }
+  cw = cn.w;
+  {
+    const float ah = ahat_at(0, cn);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) make_lut_quarter(ah, q, lut);
+    Sel4 sa, sb;
+    select8(cw.x, sa, sb);
+    lookup4(sa, lut, b0[0], b0[1]);
+    lookup4(sb, lut, b0[2], b0[3]);
+  }
+  issue_codes(1, cn);
+  {
+    // tile 1: loads 0-3 here, the rest during step 0
+    const __amdgpu_buffer_rsrc_t rs = xrsrc(1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_x1(rs, xs1, i);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + (DQ ? 3 : 2)));
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a0[i] = *reinterpret_cast<const uint4 *>(xs0 + aoff[0] + i * 32 * XROW);
+
+  // One K-step as 32 groups of two MFMAs (slice j = groups 8j .. 8j+7), each
+  // group followed by its share of the other work; sched_cut keeps that order.
+  //   A reads     slices 0-2: two fragments of the next slice per group;
+  //               groups 28-31: four fragments of the next step's slice 0.
+  //   tile loads  the tile two steps ahead goes into `rd` once every wave has
+  //               finished reading it (after the hand-over): loads 0-3 in
+  //               groups 28-31, loads 4-15 in groups 0, 2, .., 22 of the
+  //               next step (where that buffer is `wr`).
+  //   dequant     code word j+1 during slice j; the next step's LUT during
+  //               slice 2 and its first word during the first half of slice 3.
+  //   hand-over   after group 27: wait for this wave's loads, barrier, issue
+  //               the codes two steps ahead.
+  auto step = [&](int64_t kt, uint8_t *rd, uint8_t *wr) {
+    Sel4 sa, sb;
+    Lut lutn;
+    uint4 cwn;
+    float ahn = 0.f;
+    __amdgpu_buffer_rsrc_t rsw = xrsrc(kt + 1), rsr = xrsrc(kt + 2);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int slice = r < 24 ? r / 8 : 3, g = r % 8;
+      uint4 (&acur)[16] = (slice & 1) ? a1 : a0;
+      uint4 (&anext)[16] = (slice & 1) ? a0 : a1;
+      uint32_t *bcur = (slice & 1) ? b1 : b0;
+      uint32_t *bnext = (slice & 1) ? b0 : b1;
+      if (r == 28) {
+        // hand-over: every wave's reads of `rd` are complete and every wave's
+        // part of the next tile has landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        sched_cut();
+        issue_codes(kt + 2, cn);
+        sched_cut();
+      }
+      mfma2(acc[2 * g], acc[2 * g + 1], acur[2 * g], acur[2 * g + 1], bcur);
+      if (slice < 3) {
+        const int off = aoff[slice + 1];
+        anext[2 * g] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g) * 32 * XROW);
+        anext[2 * g + 1] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g + 1) * 32 * XROW);
+      } else if (r >= 28) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * (r - 28) + u;
+          a0[i] = *reinterpret_cast<const uint4 *>(wr + aoff[0] + i * 32 * XROW);
+        }
+      }
+      // tile loads
+      if (r >= 28) issue_x1(rsr, rd, r - 28);
+      if (r <= 22 && (r & 1) == 0) issue_x1(rsw, wr, 4 + r / 2);
+      // dequantization
+      if (slice < 3) {
+        const uint32_t d = slice == 0 ? cw.y : (slice == 1 ? cw.z : cw.w);
+        if (g == 1) select8(d, sa, sb);
+        if (g == 3) lookup4(sa, lut, bnext[0], bnext[1]);
+        if (g == 5) lookup4(sb, lut, bnext[2], bnext[3]);
+      }
+      if (slice == 2 && (g & 1) == 0) {
+        if (g == 0) ahn = ahat_at(kt + 1, cn);
+        make_lut_quarter(ahn, g / 2, lutn);
+      }
+      if (r == 24) {
+        cwn = cn.w;
+        select8(cwn.x, sa, sb);
+      }
+      if (r == 25) lookup4(sa, lutn, b0[0], b0[1]);
+      if (r == 26) lookup4(sb, lutn, b0[2], b0[3]);
+      if (r == 27) {
+        lut = lutn;
+        cw = cwn;
+      }
+      sched_cut();
+    }
   };
   for (int64_t kt = 0; kt < nk2; kt += 2) {
     step(kt, xs0, xs1);
@@ -338,20 +386,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
+  if (ncol < N) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    if (ncol[t] >= N) continue;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
         if (row < M) {
-          const int64_t off = row * N + ncol[t];
+          const int64_t off = row * N + ncol;
           if (Y_BF16)
-            reinterpret_cast<uint16_t *>(Y)[off] = (uint16_t)(pack_bf16x2(acc[i][t][r], 0.f) & 0xffffu);
+            reinterpret_cast<uint16_t *>(Y)[off] = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
           else
-            reinterpret_cast<float *>(Y)[off] = acc[i][t][r];
+            reinterpret_cast<float *>(Y)[off] = acc[i][r];
         }
       }
     }

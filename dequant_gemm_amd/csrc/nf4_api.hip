@@ -145,7 +145,7 @@ static int check_gemm(const void *A, int64_t M, const nf4_qtensor *q, void *C, i
   if (st) return st;
   if (M < 0 || M > kMaxDim) return NF4_ERR_SHAPE;
   if (!valid_dtype(c_dtype)) return NF4_ERR_DTYPE;
-  if (q->cols % NF4_BLOCKSIZE != 0) return NF4_ERR_UNSUPPORTED;
+  if (q->cols % NF4_BLOCKSIZE != 0 || q->cols >= NF4_GEMM_COLS_LIMIT) return NF4_ERR_UNSUPPORTED;
   if (M == 0) return NF4_OK;
   if (!A || !C) return NF4_ERR_NULL;
   if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;

@@ -39,6 +39,13 @@ __host__ __device__ constexpr float threshold(int i) { return __builtin_bit_cast
 
 // ------------------------------------------------------------------ small helpers
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | (7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14);
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   // Byte permute of the 8-byte value {hi, lo}: selector bytes 0-3 pick bytes of
   // `lo`, 4-7 bytes of `hi`, 12 gives 0x00 and 13 or more gives 0xFF.
@@ -147,6 +154,39 @@ __device__ __forceinline__ void dequant8(uint32_t d, const Lut &t, uint32_t out[
   lut_lookup4(sb, t, lo, hi);
   out[2] = perm(hi, lo, 0x05010400u);
   out[3] = perm(hi, lo, 0x07030602u);
+}
+
+// The same lookup with the two table halves combined by AND instead of a
+// bit-3 mask.  For four codes c the lower-half selector is c (codes 0..7) or
+// c + 8 (codes 8..15, selector 16..23, which makes the byte-permute emit 0xFF);
+// the upper-half selector is that value with bit 4 flipped: c + 16 (0xFF) for
+// codes 0..7 and c - 8 for codes 8..15.  Each half's lookup therefore yields
+// the table byte where it owns the code and 0xFF elsewhere, and the AND of the
+// two is the entry.
+struct Sel4 {
+  uint32_t lo;   // selectors into entries 0..7
+  uint32_t hi;   // selectors into entries 8..15
+};
+
+// Eight packed codes (element 2j in the low nibble of byte j) -> selectors for
+// elements 0..3 (a) and 4..7 (b), in element order.
+__device__ __forceinline__ void select8(uint32_t d, Sel4 &a, Sel4 &b) {
+  const uint32_t even = d & 0x0f0f0f0fu;
+  const uint32_t odd = (d >> 4) & 0x0f0f0f0fu;
+  const uint32_t ea = even + (d & 0x08080808u);
+  const uint32_t oa = odd + (odd & 0x08080808u);
+  a.lo = perm(oa, ea, 0x05010400u);
+  b.lo = perm(oa, ea, 0x07030602u);
+  a.hi = a.lo ^ 0x10101010u;
+  b.hi = b.lo ^ 0x10101010u;
+}
+
+// Four selected codes -> their bf16 values as two bf16x2 words (element order).
+__device__ __forceinline__ void lookup4(const Sel4 &s, const Lut &t, uint32_t &w0, uint32_t &w1) {
+  const uint32_t lo = perm(t.lo[1], t.lo[0], s.lo) & perm(t.lo[3], t.lo[2], s.hi);
+  const uint32_t hi = perm(t.hi[1], t.hi[0], s.lo) & perm(t.hi[3], t.hi[2], s.hi);
+  w0 = perm(hi, lo, 0x05010400u);
+  w1 = perm(hi, lo, 0x07030602u);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t w[4]) {

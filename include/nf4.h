@@ -86,6 +86,8 @@ enum nf4_dtype {
 
 /* Largest element count a quantized tensor may hold (2^37). */
 #define NF4_MAX_NUMEL ((int64_t)1 << 37)
+/* The GEMMs take weights with fewer columns than this (32-bit tile offsets). */
+#define NF4_GEMM_COLS_LIMIT ((int64_t)1 << 24)
 /* The only supported block size. */
 #define NF4_BLOCKSIZE 64
 /* Absmax values per double-quantization group. */
@@ -174,8 +176,8 @@ int nf4_dequantize(const nf4_qtensor *q, void *out, int out_dtype, void *stream)
  * Y = X W^T.  X: device bf16 [M, K] with K = q->cols; Y: device [M, N] with
  * N = q->rows, in y_dtype (NF4_F32, or NF4_BF16 = one rounding of the fp32
  * accumulator).  W^ is dequantized on chip to bf16 and never written to
- * memory.  Requires K % 64 == 0 (NF4_ERR_UNSUPPORTED otherwise).  M == 0 is
- * a successful no-op.  "Zenbit" page, zenbit.pallas_nf4 bullet (fused
+ * memory.  Requires K % 64 == 0 and K < NF4_GEMM_COLS_LIMIT
+ * (NF4_ERR_UNSUPPORTED otherwise).  M == 0 is a successful no-op.  "Zenbit" page, zenbit.pallas_nf4 bullet (fused
  * forward); "bitsandbytes" page, quantized-GEMM paragraph (fp32 output).
  */
 int nf4_matmul_fwd(const void *X, int64_t M, const nf4_qtensor *q, void *Y,
@@ -185,7 +187,8 @@ int nf4_matmul_fwd(const void *X, int64_t M, const nf4_qtensor *q, void *Y,
  * dX = dY W^ (the backward pass with respect to the input of Y = X W^T; no
  * gradient for the frozen weight).  dY: device bf16 [M, N] with N = q->rows;
  * dX: device [M, K] with K = q->cols, in dx_dtype (NF4_F32 or NF4_BF16).
- * Requires K % 64 == 0.  M == 0 is a successful no-op.  "Zenbit" page,
+ * Requires K % 64 == 0 and K < NF4_GEMM_COLS_LIMIT (NF4_ERR_UNSUPPORTED
+ * otherwise).  M == 0 is a successful no-op.  "Zenbit" page,
  * zenbit.pallas_nf4 bullet (fused backward, dL/dX only).
  */
 int nf4_matmul_bwd_dx(const void *dY, int64_t M, const nf4_qtensor *q, void *dX,

@@ -147,6 +147,7 @@ def test_gemm_errors(L, fn):
     assert f(P, 4, ctypes.byref(q), P, 9, None) == 4
     assert f(P + 4, 4, ctypes.byref(q), P, 0, None) == 5
     assert f(P, 4, ctypes.byref(_qt(rows=128, cols=96)), P, 0, None) == 7   # K % 64 != 0
+    assert f(P, 4, ctypes.byref(_qt(rows=1, cols=1 << 24)), P, 0, None) == 7   # K at the column limit
     # M == 0 is a successful no-op that launches nothing
     assert f(None, 0, ctypes.byref(q), None, 0, None) == 0
 
