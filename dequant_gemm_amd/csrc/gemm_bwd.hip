@@ -6,22 +6,33 @@
 // dL/dW is not computed for a frozen quantized base weight.
 //
 // dY is bf16 [M, N]; the weight is NF4 [N, K]; dX is fp32 (or bf16) [M, K].
-// Here the reduction runs over N while the weight's 64-blocks run along K, so
-// the dequantized tile has to change orientation before it can feed the MFMA
-// (whose operands hold eight consecutive reduction indices per lane): each
-// thread dequantizes two weight rows over 32 K, pairs the two rows' values
-// per K into one 32-bit word and writes it to an LDS tile stored K-major
-// ([k][n]); the MFMA then reads B fragments from that tile with 16-byte loads.
+// The reduction runs over N while the weight's 64-blocks run along K, so the
+// dequantized weight has to change orientation before it can feed the MFMA
+// (whose operands hold eight consecutive reduction indices per lane).
 //
-// Tiles: 256 (M) x 256 (K) outputs per workgroup, reduction steps of 64 N,
-// four waves in a 2x2 arrangement of 128x128, MFMA 32x32x16 bf16, dY and the
-// weight tile both double-buffered in LDS.  The codes are loaded two steps
-// ahead and the next step's weight tile is dequantized between the current
-// step's MFMAs, so the dequantization overlaps the matrix cores.
+// Two kernels:
+//   bwd_dx_kernel          N % 8 == 0 (16-byte dY rows) and N < 2^24: dY
+//                          through buffer-to-LDS loads, each wave dequantizes
+//                          its own weight columns row by row into a private
+//                          LDS tile and reads MFMA operands back with
+//                          transposing LDS reads.
+//   bwd_dx_generic_kernel  any shape: dY staged through registers, the
+//                          weight tile written to LDS already transposed.
 #include "nf4_launch.h"
 
 namespace nf4 {
-namespace {
+
+// ------------------------------------------------------------ generic kernel
+//
+// Each thread dequantizes two weight rows over 32 K, pairs the two rows'
+// values per K into one 32-bit word and writes it to an LDS tile stored
+// K-major ([k][n]); the MFMA then reads B fragments from that tile with
+// 16-byte loads.  Tiles: 256 (M) x 256 (K) outputs per workgroup, reduction
+// steps of 64 N, four waves in a 2x2 arrangement of 128x128, dY and the
+// weight tile both double-buffered in LDS.  The codes are loaded two steps
+// ahead and the next step's weight tile is dequantized between the current
+// step's MFMAs.
+namespace generic {
 
 #ifndef NF4_BWD_SCHED
 #define NF4_BWD_SCHED 0
@@ -46,7 +57,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_k, int &
 }
 
 template <bool DX_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_kernel(const uint16_t *__restrict__ dY, int64_t M,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_generic_kernel(const uint16_t *__restrict__ dY, int64_t M,
                                                      int64_t N, int64_t K,
                                                      const uint8_t *__restrict__ packed,
                                                      AbsmaxSrc src, void *__restrict__ dX,
@@ -218,17 +229,383 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-}  // namespace
+}  // namespace generic
+
+namespace tr_kernel {
+// ------------------------------------------------------------ main kernel
+//
+// Workgroup tile 256 (M) x 256 (K), eight waves, two per SIMD; wave w owns the
+// 32 output columns k0 + 32w .. +31 over all 256 rows (8 MFMA 32x32x16 tiles
+// stacked along M).  The reduction runs over N in steps of 64.
+//
+// A operand (dY): 256 x 64 tiles reach LDS by buffer-to-LDS loads through
+// three stages, laid out and read exactly like the X tiles of the forward
+// kernel.
+//
+// B operand (W^, 64 rows n x the wave's 32 columns k): lane l dequantizes row
+// n = 64s + l of the wave's columns -- 32 consecutive codes of one block, one
+// LUT -- and writes the 32 bf16 values as one 64-byte row of a per-wave LDS
+// tile (16-byte chunks XOR-swizzled by (row/4) & 3).  The MFMA wants eight
+// consecutive n of one column per lane; the transposing LDS read
+// ds_read_b64_tr_b16 delivers exactly that: within a 16-lane group, output
+// lane i element e is element i%4 of the 8 bytes addressed by source lane
+// 4e + i/4, so source lane j of group G addresses row r0 + 4h + j/4 and
+// columns 16(G%2) + 4(j%4) .. +3 (kg = G/2, h = which half of the 8 n), and
+// output lane i receives rows r0 + 4h .. +3 of column 16(G%2) + i; r0 is the
+// first of the eight n that lane group kg's A fragment holds in that slice.
+constexpr int TM = 256, TK = 256, TN = 64;
+constexpr int NWAVE = 8;
+constexpr int AROW = TN * 2;             // 128-byte dY rows in LDS
+constexpr int ATILE = TM * AROW;         // 32 KiB
+constexpr int BTILE = TN * 64;           // per-wave weight tile: 64 rows x 32 bf16
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void tile_of_main(int bid, int tiles_m, int tiles_k, int &tm, int &tk) {
+  const int total = tiles_m * tiles_k;
+  const int q = total / 8, r = total % 8;
+  const int xcd = bid % 8, idx = bid / 8;
+  const int t = xcd * q + (xcd < r ? xcd : r) + idx;
+  constexpr int G = 4;
+  const int per_group = G * tiles_k;
+  const int group = t / per_group;
+  const int first_m = group * G;
+  const int gsize = tiles_m - first_m < G ? tiles_m - first_m : G;
+  const int in_group = t % per_group;
+  tm = first_m + in_group % gsize;
+  tk = in_group / gsize;
+}
+
+template <bool DQ>
+__device__ __forceinline__ AbsmaxRaw load_raw(const AbsmaxSrc &s, int64_t blk) {
+  AbsmaxRaw r;
+  if (DQ) {
+    r.q = s.q[blk];
+    r.v = s.scale[blk >> 8];
+  } else {
+    r.q = 0;
+    r.v = s.absmax[blk];
+  }
+  return r;
+}
+
+struct RowCodes {
+  uint4 w;        // 32 codes of this lane's weight row
+  AbsmaxRaw r;
+};
+
+__device__ __forceinline__ void sched_cut() { __builtin_amdgcn_sched_barrier(0); }
+
+template <typename T>
+__device__ __forceinline__ const uint8_t *uniform_ptr(const T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void lut_quarter(float ahat, int q, Lut &t) {
+  const uint32_t p0 = pack_bf16x2(__fmul_rn(level(4 * q), ahat), __fmul_rn(level(4 * q + 1), ahat));
+  const uint32_t p1 = pack_bf16x2(__fmul_rn(level(4 * q + 2), ahat), __fmul_rn(level(4 * q + 3), ahat));
+  t.lo[q] = perm(p1, p0, 0x06040200u);
+  t.hi[q] = perm(p1, p0, 0x07050301u);
+}
+
+template <bool DX_BF16, bool DQ>
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dx_kernel(
+    const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    AbsmaxSrc src, void *__restrict__ dX, int tiles_m, int tiles_k) {
+  __shared__ __attribute__((aligned(1024))) uint8_t as0[ATILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t as1[ATILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t as2[ATILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t bs[NWAVE * BTILE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int tm, tk;
+  tile_of_main(blockIdx.x, tiles_m, tiles_k, tm, tk);
+  const int64_t m0 = (int64_t)tm * TM, k0 = (int64_t)tk * TK;
+  const float mu = DQ ? *src.mean : 0.f;
+  const int bl = lane & 31, kg = lane >> 5;
+
+  // this wave's 32 output columns (K % 64 == 0, so they are all valid or all
+  // past K; past K they read columns K-32 .. K-1 and are never stored)
+  const int64_t kcol = k0 + 32 * wave;
+  const int64_t kc = kcol < K ? kcol : K - 32;
+  // weight row of this lane in step s: n = 64s + lane
+  const uint8_t *wq = packed + (int64_t)lane * (K / 2) + kc / 2;
+  const int64_t blk0 = (int64_t)lane * (K / kBlock) + kc / kBlock;
+
+  // dY tile loads, as the forward kernel's X tiles: wave w's load i (0..3)
+  // covers tile rows 8(4w + i) .. +7; one descriptor per wave and step sized
+  // to its existing rows; a 16-byte chunk past N gets an offset beyond the
+  // descriptor and loads zeros.  (Requires N % 8 == 0 and N < 2^24.)
+  const int64_t wrow0 = m0 + 32 * wave;
+  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 32 ? 32 : M - wrow0);
+  const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * N * 2));
+  const uint8_t *ywave = uniform_ptr(dY + (wrows > 0 ? wrow0 : 0) * N);
+  uint32_t yvoff[4];
+  int ychunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    ychunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    yvoff[i] = (uint32_t)(r * N * 2) + ((uint32_t)ychunk[i] << 4);
+  }
+  int aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = bl * AROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
+
+  // per-wave weight tile: row n at n * 64 bytes, 16-byte chunk c at c ^ ((n >> 2) & 3)
+  uint8_t *bw = bs + wave * BTILE;
+  int bwoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) bwoff[c] = lane * 64 + ((c ^ ((lane >> 2) & 3)) << 4);
+  // transposing reads for slice sl: source lane j of group G, half h: row
+  // 32kg + 8sl + 4h + j/4 (the n range the A fragment of lane group kg holds
+  // in slice sl), columns 16(G%2) + 4(j%4): chunk 2(G%2) + (j%4)/2, byte
+  // 8 * ((j%4) & 1)
+  int broff[4][2];
+  {
+    const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 32 * (G >> 1) + 8 * sl + 4 * h + (j >> 2);
+        const int chunk = 2 * (G & 1) + ((j & 3) >> 1);
+        broff[sl][h] = row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4) + 8 * (j & 1);
+      }
+  }
+
+  const int64_t ns = (N + TN - 1) / TN;
+  const int64_t ns3 = (ns + 2) / 3 * 3;   // steps run in threes; a padded step has zero weights
+  auto clamps = [&](int64_t s) { return s < ns ? s : ns - 1; };
+  auto yrsrc = [&](int64_t s) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(ywave + clamps(s) * (TN * 2)), (short)0,
+                                             wbytes, 0x00020000);
+  };
+  auto issue_y1 = [&](__amdgpu_buffer_rsrc_t rs, int64_t s, uint8_t *dst, int i) {
+    const bool in = clamps(s) * TN + 8 * ychunk[i] < N;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * wave + i) * 1024), 16,
+                                             in ? yvoff[i] : 0x80000000u, 0, 0, 0);
+  };
+  // a row past N loads row N-1's codes (in bounds) and gets a^ = 0
+  auto issue_codes = [&](int64_t s, RowCodes &c) {
+    const int64_t sc = clamps(s);
+    const int64_t n = sc * TN + lane;
+    const int64_t dn = n < N ? sc * TN : N - 1 - lane;     // row offset from this lane's base row
+    c.w = *reinterpret_cast<const uint4 *>(wq + dn * (K / 2));
+    c.r = load_raw<DQ>(src, blk0 + dn * (K / kBlock));
+  };
+  auto ahat_at = [&](int64_t s, const RowCodes &c) {
+    const float v = ahat_of(c.r, DQ, mu);
+    return (s < ns && s * TN + lane < N) ? v : 0.f;
+  };
+  // The transposing read is issued as inline assembly: the compiler's wait
+  // insertion cannot tell the intrinsic's LDS address apart from the dY tiles
+  // that buffer-to-LDS loads are filling and would wait for all of those loads
+  // before every such read.  Its results are waited for explicitly
+  // (lgkm_wait) before the MFMA that consumes them.
+  const uint32_t bwaddr = (uint32_t)(uintptr_t)bw;
+  auto tr_read = [&](int sl, int h) {
+    v4s v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(bwaddr + (uint32_t)broff[sl][h]) : "memory");
+    return v;
+  };
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  uint4 a[8];
+  v4s b0[2], b1[2];      // B fragments (two 4 x bf16 halves each) of the current and next slice
+  uint32_t st[16];       // the next step's dequantized weight row, staged for the LDS write
+  RowCodes cs0, cs1, cs2;
+
+  // prologue: dY tiles 0 and 1 and the codes of steps 0 and 1 in flight;
+  // step 0's weight row dequantized and written, its first B fragment read
+  {
+    RowCodes c0;
+    issue_codes(0, c0);
+    const __amdgpu_buffer_rsrc_t r0 = yrsrc(0), r1 = yrsrc(1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_y1(r0, 0, as0, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_y1(r1, 1, as1, i);
+    issue_codes(1, cs1);
+    issue_codes(2, cs2);
+    Lut t;
+    const float ah = ahat_at(0, c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lut_quarter(ah, q, t);
+    const uint32_t wd[4] = {c0.w.x, c0.w.y, c0.w.z, c0.w.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Sel4 sa, sb;
+      select8(wd[c], sa, sb);
+      lookup4(sa, t, st[4 * c], st[4 * c + 1]);
+      lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint4 *>(bw + bwoff[c]) = make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
+    b0[0] = tr_read(0, 0);
+    b0[1] = tr_read(0, 1);
+  }
+  // dY tile 0 landed; the first B fragment read (lgkmcnt(0))
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + 2 * (DQ ? 3 : 2)) & ~(0xF << 8));
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(as0 + aoff[0] + i * 32 * AROW);
+
+  // One N-step as 16 groups of two MFMAs (slice j = groups 4j .. 4j+3):
+  //   A reads     as in the forward kernel (the group's two fragments again
+  //               for the next slice; the next step's slice 0 after the
+  //               hand-over, from `nx`)
+  //   B reads     the next slice's two transposing reads in the slice's
+  //               first two groups; the next step's slice 0 after the
+  //               hand-over (after this wave's write of the next tile)
+  //   dY loads    the tile two steps ahead into `ld`: groups 0, 4, 8, 12
+  //   dequant     the next step's LUT and its four code words in groups
+  //               0-11, staged in registers; written to the weight tile in
+  //               group 12 (its last reads were issued in slice 2)
+  //   hand-over   before group 14: this wave's LDS traffic is complete and
+  //               the next dY tile has landed, barrier, codes three steps
+  //               ahead (into the slot of this step's own codes: step s + i
+  //               sits in slot (s + i) % 3)
+  auto step = [&](int64_t s, uint8_t *rd, uint8_t *nx, uint8_t *ld, const RowCodes &cn, RowCodes &cfill) {
+    Sel4 sa, sb;
+    Lut t;
+    float ahn = 0.f;
+    const __amdgpu_buffer_rsrc_t rsl = yrsrc(s + 2);
+    const uint32_t wd[4] = {cn.w.x, cn.w.y, cn.w.z, cn.w.w};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int slice = r / 4, g = r % 4;
+      const v4s *bc = (slice & 1) ? b1 : b0;
+      v4s *bn = (slice & 1) ? b0 : b1;
+      if (r == 14) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4) & ~(0xF << 8));   // vmcnt(4) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        sched_cut();
+        issue_codes(s + 3, cfill);
+        b0[0] = tr_read(0, 0);
+        b0[1] = tr_read(0, 1);
+        sched_cut();
+      }
+      if (g == 0) {
+        // the slice's B fragment: issued in groups 4j-4 and 4j-3 (slices 1-3,
+        // followed by four A reads) or after the previous hand-over (slice 0,
+        // followed by eight A reads)
+        if (slice == 0)
+          __builtin_amdgcn_s_waitcnt(lgkm_imm(8));
+        else
+          __builtin_amdgcn_s_waitcnt(lgkm_imm(4));
+        sched_cut();
+      }
+      {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, (uint4){(uint32_t)__builtin_bit_cast(uint64_t, bc[0]),
+                                                             (uint32_t)(__builtin_bit_cast(uint64_t, bc[0]) >> 32),
+                                                             (uint32_t)__builtin_bit_cast(uint64_t, bc[1]),
+                                                             (uint32_t)(__builtin_bit_cast(uint64_t, bc[1]) >> 32)});
+        acc[2 * g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[2 * g]), bv, acc[2 * g], 0, 0, 0);
+        acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[2 * g + 1]), bv, acc[2 * g + 1], 0, 0, 0);
+      }
+      if (slice < 3) {
+        const int off = aoff[slice + 1];
+        a[2 * g] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g) * 32 * AROW);
+        a[2 * g + 1] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g + 1) * 32 * AROW);
+        if (g < 2) bn[g] = tr_read(slice + 1, g);
+      } else if (r >= 14) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * (r - 14) + u;
+          a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * AROW);
+        }
+      }
+      if (g == 0) issue_y1(rsl, s + 2, ld, slice);
+      // dequantization of the next step's weight row
+      if (r == 0) {
+        ahn = ahat_at(s + 1, cn);
+        lut_quarter(ahn, 0, t);
+        lut_quarter(ahn, 1, t);
+      }
+      if (r == 1) {
+        lut_quarter(ahn, 2, t);
+        lut_quarter(ahn, 3, t);
+      }
+      if (r >= 2 && r <= 13) {
+        const int c = (r - 2) / 3, ph = (r - 2) % 3;
+        if (ph == 0) select8(wd[c], sa, sb);
+        if (ph == 1) lookup4(sa, t, st[4 * c], st[4 * c + 1]);
+        if (ph == 2) lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
+      }
+      if (r == 13) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<uint4 *>(bw + bwoff[c]) = make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
+      }
+      sched_cut();
+    }
+  };
+  for (int64_t s = 0; s < ns3; s += 3) {
+    step(s, as0, as1, as2, cs1, cs0);
+    step(s + 1, as1, as2, as0, cs2, cs1);
+    step(s + 2, as2, as0, as1, cs0, cs2);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
+  const int64_t col = kcol + bl;
+  if (kcol < K) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
+        if (row < M) {
+          const int64_t off = row * K + col;
+          if (DX_BF16)
+            reinterpret_cast<uint16_t *>(dX)[off] = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
+          else
+            reinterpret_cast<float *>(dX)[off] = acc[i][r];
+        }
+      }
+    }
+  }
+}
+}  // namespace tr_kernel
 
 hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
                          const AbsmaxSrc &src, void *dx, int dx_is_bf16, hipStream_t stream) {
   const uint16_t *dY = reinterpret_cast<const uint16_t *>(dy);
-  const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
-  const dim3 g((unsigned)(tiles_m * tiles_k)), b(256);
-  if (dx_is_bf16)
-    hipLaunchKernelGGL((bwd_dx_kernel<true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-  else
-    hipLaunchKernelGGL((bwd_dx_kernel<false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+  if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
+    using namespace tr_kernel;
+    const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
+    const dim3 g((unsigned)(tiles_m * tiles_k)), b(64 * NWAVE);
+    if (src.dq) {
+      if (dx_is_bf16)
+        hipLaunchKernelGGL((bwd_dx_kernel<true, true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+      else
+        hipLaunchKernelGGL((bwd_dx_kernel<false, true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+    } else {
+      if (dx_is_bf16)
+        hipLaunchKernelGGL((bwd_dx_kernel<true, false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+      else
+        hipLaunchKernelGGL((bwd_dx_kernel<false, false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+    }
+  } else {
+    using namespace generic;
+    const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
+    const dim3 g((unsigned)(tiles_m * tiles_k)), b(256);
+    if (dx_is_bf16)
+      hipLaunchKernelGGL((bwd_dx_generic_kernel<true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+    else
+      hipLaunchKernelGGL((bwd_dx_generic_kernel<false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+  }
   return hipGetLastError();
 }
 

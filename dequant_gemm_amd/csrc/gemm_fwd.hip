@@ -13,9 +13,9 @@
 //   fwd_small_kernel  M <= 16, streaming-bound: one workgroup per 16 weight
 //                     rows, its eight waves split K; every weight byte is read
 //                     once, all of a lane's loads are issued together.
-//   fwd_large_kernel  M > 16, matrix-core-bound: 512x128 output tiles; X
-//                     staged through LDS (double-buffered, filled by direct
-//                     global->LDS loads), each wave dequantizes its own 32
+//   fwd_large_kernel  M > 16, matrix-core-bound: 256x256 output tiles, eight
+//                     waves; X staged through LDS (three stages, filled by
+//                     buffer-to-LDS loads), each wave dequantizes its own 32
 //                     weight rows straight into MFMA operand registers (no LDS
 //                     round trip, no duplicate dequantization inside the
 //                     workgroup).
@@ -114,12 +114,13 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
 
 // ----------------------------------------------------------------- large M
 //
-// Workgroup tile 512 (M) x 128 (N), four waves, one per SIMD; wave w owns the
-// 32 output columns n0 + 32w .. +31 over all 512 rows: 16 MFMA 32x32x16 tiles
-// stacked along M, 256 accumulator registers.  Each dequantized B fragment is
-// therefore multiplied by 16 A fragments, which keeps the dequantization's
-// VALU work a small fraction of the MFMA time.  Each wave dequantizes only its
-// own columns; the weight never passes through LDS.
+// Workgroup tile 256 (M) x 256 (N), eight waves, two per SIMD; wave w owns the
+// 32 output columns n0 + 32w .. +31 over all 256 rows: 8 MFMA 32x32x16 tiles
+// stacked along M, 128 accumulator registers.  Each wave dequantizes only its
+// own columns (the weight never passes through LDS, and no column is
+// dequantized twice in a workgroup); each dequantized B fragment feeds 8
+// MFMAs.  While one wave of a SIMD waits on a load issue or a barrier, the
+// other keeps the matrix core busy.
 //
 // K advances in steps of 64 (one quantization block): per step a lane holds
 // one 16-byte code chunk (32 codes) and one LUT.  Lane group kg = l/32 owns K
@@ -127,18 +128,19 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
 // 8j .. 8j+7 of it from both operands (A and B only have to agree on the K
 // index of each slot).
 //
-// X tiles (512 rows x 64 K, 64 KiB) reach LDS by direct global->LDS loads,
-// double-buffered.  The barrier that hands a tile over sits in the middle of
-// the last slice of a step: the second half of that slice's MFMAs covers the
-// first A-fragment reads of the next step and the next tile's load issue.
-constexpr int BM = 512, BN = 128, BK = 64;
+// X tiles (256 rows x 64 K, 32 KiB) reach LDS by buffer-to-LDS loads through
+// three stages: the tile two steps ahead loads during a whole step.  The
+// barrier that hands a tile over sits in the middle of the last slice, so the
+// slice's second half covers the next step's first A-fragment reads.
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NWAVE = 8;
 constexpr int XROW = BK * 2;                 // 128-byte LDS rows
-constexpr int XTILE = BM * XROW;             // 64 KiB
+constexpr int XTILE = BM * XROW;             // 32 KiB
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
-// takes a contiguous run of tiles, then walk tiles in groups of 2 M-tiles so
+// takes a contiguous run of tiles, then walk tiles in groups of 4 M-tiles so
 // that the workgroups an XCD runs together share X tiles and weight codes in
 // its L2.
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -146,7 +148,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
   const int q = total / 8, r = total % 8;
   const int xcd = bid % 8, idx = bid / 8;
   const int t = xcd * q + (xcd < r ? xcd : r) + idx;
-  constexpr int G = 2;
+  constexpr int G = 4;
   const int per_group = G * tiles_n;
   const int group = t / per_group;
   const int first_m = group * G;
@@ -201,13 +203,14 @@ __device__ __forceinline__ void make_lut_quarter(float ahat, int q, Lut &t) {
 }
 
 template <bool Y_BF16, bool DQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_large_kernel(
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_large_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, void *__restrict__ Y, int tiles_m, int tiles_n) {
-  // two separate arrays (not one indexed by stage) so that the compiler can
-  // tell the tile being read from the tile being loaded
+  // separate arrays (not one indexed by stage) so that the compiler can tell
+  // the tile being read from the tiles being loaded
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[XTILE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[XTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs2[XTILE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int tm, tn;
@@ -223,22 +226,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint8_t *wq = packed + nc * (K / 2) + kg * 16;
   const int64_t blk0 = nc * (K / kBlock);
 
-  // X tile loads, buffer-to-LDS: wave w's load i fills LDS bytes
-  // (16w + i) * 1024 .. +1023, i.e. tile rows 8(16w + i) .. +7; lane l takes
-  // row 8(16w + i) + l/8 and physical 16-byte chunk l%8, which holds logical
-  // chunk (l%8) ^ ((row/2) & 7).  One buffer descriptor per wave and step,
-  // based at the wave's first row and sized to its rows that exist: the
-  // lanes of rows past M fall outside it and load zeros.
-  const int64_t wrow0 = m0 + 128 * wave;
-  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 128 ? 128 : M - wrow0);
-  // offsets and sizes are 32-bit: K < 2^24 (checked by the launcher)
-  // (both made explicitly wave-uniform: a buffer descriptor lives in SGPRs)
+  // X tile loads, buffer-to-LDS: wave w's load i (0..3) fills LDS bytes
+  // (4w + i) * 1024 .. +1023, i.e. tile rows 8(4w + i) .. +7; lane l takes row
+  // 8(4w + i) + l/8 and physical 16-byte chunk l%8, which holds logical chunk
+  // (l%8) ^ ((row/2) & 7).  One buffer descriptor per wave and step, based at
+  // the wave's first row and sized to its rows that exist: lanes of rows past
+  // M fall outside it and load zeros.  Offsets and sizes are 32-bit (K < 2^24,
+  // checked by the API); the descriptor fields are made explicitly
+  // wave-uniform since a descriptor lives in SGPRs.
+  const int64_t wrow0 = m0 + 32 * wave;
+  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 32 ? 32 : M - wrow0);
   const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * K * 2));
   const uint8_t *xwave = uniform_ptr(X + (wrows > 0 ? wrow0 : 0) * K);
-  uint32_t xvoff[16];
+  uint32_t xvoff[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 8 * i + (lane >> 3);                             // row within the wave's 128
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);                             // row within the wave's 32
     xvoff[i] = (uint32_t)(r * K * 2) + ((uint32_t)((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
   // A fragments: lane l reads row 32i + l%32, logical chunk 4kg + j of slice j,
@@ -248,14 +251,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int j = 0; j < 4; ++j) aoff[j] = bl * XROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
 
   const int64_t nk = K / BK;
-  const int64_t nk2 = (nk + 1) & ~(int64_t)1;  // steps run in pairs; a padded step has a^ = 0
+  const int64_t nk3 = (nk + 2) / 3 * 3;  // steps run in threes; a padded step has a^ = 0
   auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
   auto xrsrc = [&](int64_t kt) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + clampk(kt) * (BK * 2)), (short)0,
                                              wbytes, 0x00020000);
   };
   auto issue_x1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t *dst, int i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (16 * wave + i) * 1024), 16, xvoff[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * wave + i) * 1024), 16, xvoff[i], 0, 0, 0);
   };
   auto issue_codes = [&](int64_t kt, StepCodes &c) {
     const int64_t k = clampk(kt);
@@ -264,29 +267,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto ahat_at = [&](int64_t kt, const StepCodes &c) { return kt < nk ? ahat_of(c.r, DQ, mu) : 0.f; };
 
-  f32x16 acc[16];
+  f32x16 acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  uint4 a0[16], a1[16];
+  uint4 a[8];      // A fragments; pair g is refilled for the next slice right after its MFMAs issue
   uint32_t b0[4], b1[4];
   uint4 cw;        // codes of the current step
   Lut lut;         // LUT of the current step
-  StepCodes cn;    // codes of the next step (in flight)
+  // codes of the next two steps, in flight: step kt + 1 + i sits in slot
+  // (kt + 1 + i) % 3, so that with three steps per loop iteration every
+  // slot keeps its registers (a loop-carried copy would wait for the load)
+  StepCodes cs0, cs1, cs2;
 
-  // prologue: step 0's codes, LUT, first B fragment and first A fragments;
-  // step 1's codes and tile in flight
-  issue_codes(0, cn);
+  // prologue: tiles 0 and 1 and the codes of steps 0 and 1 in flight (in the
+  // steady state's order: a tile, then the codes of the step before it)
   {
-    const __amdgpu_buffer_rsrc_t rs = xrsrc(0);
+    StepCodes c0;
+    issue_codes(0, c0);
+    const __amdgpu_buffer_rsrc_t r0 = xrsrc(0), r1 = xrsrc(1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) issue_x1(rs, xs0, i);
-  }
-  cw = cn.w;
-  {
-    const float ah = ahat_at(0, cn);
+    for (int i = 0; i < 4; ++i) issue_x1(r0, xs0, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_x1(r1, xs1, i);
+    issue_codes(1, cs1);
+    cw = c0.w;
+    const float ah = ahat_at(0, c0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) make_lut_quarter(ah, q, lut);
     Sel4 sa, sb;
@@ -294,101 +302,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lookup4(sa, lut, b0[0], b0[1]);
     lookup4(sb, lut, b0[2], b0[3]);
   }
-  issue_codes(1, cn);
-  {
-    // tile 1: loads 0-3 here, the rest during step 0
-    const __amdgpu_buffer_rsrc_t rs = xrsrc(1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_x1(rs, xs1, i);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + (DQ ? 3 : 2)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + (DQ ? 3 : 2)));   // tile 0 landed
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a0[i] = *reinterpret_cast<const uint4 *>(xs0 + aoff[0] + i * 32 * XROW);
+  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(xs0 + aoff[0] + i * 32 * XROW);
 
-  // One K-step as 32 groups of two MFMAs (slice j = groups 8j .. 8j+7), each
+  // One K-step as 16 groups of two MFMAs (slice j = groups 4j .. 4j+3), each
   // group followed by its share of the other work; sched_cut keeps that order.
-  //   A reads     slices 0-2: two fragments of the next slice per group;
-  //               groups 28-31: four fragments of the next step's slice 0.
-  //   tile loads  the tile two steps ahead goes into `rd` once every wave has
-  //               finished reading it (after the hand-over): loads 0-3 in
-  //               groups 28-31, loads 4-15 in groups 0, 2, .., 22 of the
-  //               next step (where that buffer is `wr`).
+  //   A reads     slices 0-2: the group's two fragments again, for the next
+  //               slice; groups 14-15: four fragments each of the next step's
+  //               slice 0 (from `nx`), in registers whose MFMAs have issued.
+  //   tile loads  the tile two steps ahead, into `ld` (free since the previous
+  //               hand-over): one load in each of groups 0, 4, 8, 12.
   //   dequant     code word j+1 during slice j; the next step's LUT during
   //               slice 2 and its first word during the first half of slice 3.
-  //   hand-over   after group 27: wait for this wave's loads, barrier, issue
-  //               the codes two steps ahead.
-  auto step = [&](int64_t kt, uint8_t *rd, uint8_t *wr) {
+  //   hand-over   after group 13: this wave's LDS reads and the next tile's
+  //               loads are complete (only the four loads of the tile two
+  //               steps ahead may be outstanding), then the barrier, then the
+  //               codes two steps ahead.
+  auto step = [&](int64_t kt, uint8_t *rd, uint8_t *nx, uint8_t *ld, const StepCodes &cn, StepCodes &cfill) {
     Sel4 sa, sb;
-    Lut lutn;
-    uint4 cwn;
     float ahn = 0.f;
-    __amdgpu_buffer_rsrc_t rsw = xrsrc(kt + 1), rsr = xrsrc(kt + 2);
+    const __amdgpu_buffer_rsrc_t rsl = xrsrc(kt + 2);
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const int slice = r < 24 ? r / 8 : 3, g = r % 8;
-      uint4 (&acur)[16] = (slice & 1) ? a1 : a0;
-      uint4 (&anext)[16] = (slice & 1) ? a0 : a1;
+    for (int r = 0; r < 16; ++r) {
+      const int slice = r / 4, g = r % 4;
       uint32_t *bcur = (slice & 1) ? b1 : b0;
       uint32_t *bnext = (slice & 1) ? b0 : b1;
-      if (r == 28) {
-        // hand-over: every wave's reads of `rd` are complete and every wave's
-        // part of the next tile has landed
-        __builtin_amdgcn_s_waitcnt(0);
+      if (r == 14) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4) & ~(0xF << 8));   // vmcnt(4) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         sched_cut();
-        issue_codes(kt + 2, cn);
+        issue_codes(kt + 2, cfill);
         sched_cut();
       }
-      mfma2(acc[2 * g], acc[2 * g + 1], acur[2 * g], acur[2 * g + 1], bcur);
+      mfma2(acc[2 * g], acc[2 * g + 1], a[2 * g], a[2 * g + 1], bcur);
       if (slice < 3) {
         const int off = aoff[slice + 1];
-        anext[2 * g] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g) * 32 * XROW);
-        anext[2 * g + 1] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g + 1) * 32 * XROW);
-      } else if (r >= 28) {
+        a[2 * g] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g) * 32 * XROW);
+        a[2 * g + 1] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g + 1) * 32 * XROW);
+      } else if (r >= 14) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int i = 4 * (r - 28) + u;
-          a0[i] = *reinterpret_cast<const uint4 *>(wr + aoff[0] + i * 32 * XROW);
+          const int i = 4 * (r - 14) + u;
+          a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * XROW);
         }
       }
-      // tile loads
-      if (r >= 28) issue_x1(rsr, rd, r - 28);
-      if (r <= 22 && (r & 1) == 0) issue_x1(rsw, wr, 4 + r / 2);
-      // dequantization
+      if (g == 0) issue_x1(rsl, ld, slice);
+      // dequantization: word j+1 during slice j (its last use of the LUT is
+      // in group 11); the next step's LUT replaces it in groups 12-13 and
+      // that step's first word is dequantized in groups 14-15
       if (slice < 3) {
         const uint32_t d = slice == 0 ? cw.y : (slice == 1 ? cw.z : cw.w);
         if (g == 1) select8(d, sa, sb);
-        if (g == 3) lookup4(sa, lut, bnext[0], bnext[1]);
-        if (g == 5) lookup4(sb, lut, bnext[2], bnext[3]);
+        if (g == 2) lookup4(sa, lut, bnext[0], bnext[1]);
+        if (g == 3) lookup4(sb, lut, bnext[2], bnext[3]);
       }
-      if (slice == 2 && (g & 1) == 0) {
-        if (g == 0) ahn = ahat_at(kt + 1, cn);
-        make_lut_quarter(ahn, g / 2, lutn);
+      if (r == 8) ahn = ahat_at(kt + 1, cn);
+      if (r == 12) {
+        make_lut_quarter(ahn, 0, lut);
+        make_lut_quarter(ahn, 1, lut);
       }
-      if (r == 24) {
-        cwn = cn.w;
-        select8(cwn.x, sa, sb);
+      if (r == 13) {
+        make_lut_quarter(ahn, 2, lut);
+        make_lut_quarter(ahn, 3, lut);
       }
-      if (r == 25) lookup4(sa, lutn, b0[0], b0[1]);
-      if (r == 26) lookup4(sb, lutn, b0[2], b0[3]);
-      if (r == 27) {
-        lut = lutn;
-        cw = cwn;
+      if (r == 14) {
+        cw = cn.w;
+        select8(cw.x, sa, sb);
+        lookup4(sa, lut, b0[0], b0[1]);
       }
+      if (r == 15) lookup4(sb, lut, b0[2], b0[3]);
       sched_cut();
     }
   };
-  for (int64_t kt = 0; kt < nk2; kt += 2) {
-    step(kt, xs0, xs1);
-    step(kt + 1, xs1, xs0);
+  for (int64_t kt = 0; kt < nk3; kt += 3) {
+    step(kt, xs0, xs1, xs2, cs1, cs2);
+    step(kt + 1, xs1, xs2, xs0, cs2, cs0);
+    step(kt + 2, xs2, xs0, xs1, cs0, cs1);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   if (ncol < N) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
@@ -417,7 +415,7 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
       hipLaunchKernelGGL((fwd_small_kernel<false>), g, b, 0, stream, X, (int)M, N, K, packed, src, y);
   } else {
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const dim3 g((unsigned)(tiles_m * tiles_n)), b(256);
+    const dim3 g((unsigned)(tiles_m * tiles_n)), b(64 * NWAVE);
     if (src.dq) {
       if (y_is_bf16)
         hipLaunchKernelGGL((fwd_large_kernel<true, true>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);

@@ -46,6 +46,11 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
   return (n & 0xF) | (7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14);
 }
 
+// The same for the LDS/scalar-memory counter: at most n outstanding.
+__host__ __device__ constexpr int lgkm_imm(int n) {
+  return 0xF | (7 << 4) | ((n & 0xF) << 8) | (3 << 14);
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   // Byte permute of the 8-byte value {hi, lo}: selector bytes 0-3 pick bytes of
   // `lo`, 4-7 bytes of `hi`, 12 gives 0x00 and 13 or more gives 0xFF.
