@@ -21,6 +21,7 @@
 #include "nf4_launch.h"
 
 namespace nf4 {
+namespace {
 
 // ------------------------------------------------------------ generic kernel
 //
@@ -578,6 +579,8 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 }  // namespace tr_kernel
+
+}  // namespace
 
 hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
                          const AbsmaxSrc &src, void *dx, int dx_is_bf16, hipStream_t stream) {

@@ -24,6 +24,8 @@
 namespace nf4 {
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // ----------------------------------------------------------------- small M
 //
 // MFMA 16x16x32: lane l feeds A row l%16 (an X row) and B column l%16 (a
@@ -136,8 +138,6 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int NWAVE = 8;
 constexpr int XROW = BK * 2;                 // 128-byte LDS rows
 constexpr int XTILE = BM * XROW;             // 32 KiB
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
 // takes a contiguous run of tiles, then walk tiles in groups of 4 M-tiles so
