@@ -245,8 +245,8 @@ namespace tr_kernel {
 //
 // B operand (W^, 64 rows n x the wave's 32 columns k): lane l dequantizes row
 // n = 64s + l of the wave's columns -- 32 consecutive codes of one block, one
-// LUT -- and writes the 32 bf16 values as one 64-byte row of a per-wave LDS
-// tile (16-byte chunks XOR-swizzled by (row/4) & 3).  The MFMA wants eight
+// LUT -- and writes the 32 bf16 values as one row of a per-wave LDS tile
+// (80-byte rows: 64 bytes of data and 16 of padding).  The MFMA wants eight
 // consecutive n of one column per lane; the transposing LDS read
 // ds_read_b64_tr_b16 delivers exactly that: within a 16-lane group, output
 // lane i element e is element i%4 of the 8 bytes addressed by source lane
@@ -258,7 +258,8 @@ constexpr int TM = 256, TK = 256, TN = 64;
 constexpr int NWAVE = 8;
 constexpr int AROW = TN * 2;             // 128-byte dY rows in LDS
 constexpr int ATILE = TM * AROW;         // 32 KiB
-constexpr int BTILE = TN * 64;           // per-wave weight tile: 64 rows x 32 bf16
+constexpr int BROW = 80;                 // weight-tile row: 64 bytes of bf16 + 16 bytes of padding
+constexpr int BTILE = TN * BROW;         // per-wave weight tile: 64 rows x 32 bf16
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -346,48 +347,44 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * N * 2));
   const uint8_t *ywave = uniform_ptr(dY + (wrows > 0 ? wrow0 : 0) * N);
   uint32_t yvoff[4];
-  int ychunk[4];
+  int ylast = 0;   // bit i: load i's chunk exists in the last step (N need not be a multiple of 64)
+  {
+    const int64_t lastn = N - (((N + TN - 1) / TN) - 1) * TN;   // valid n in the last step
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * i + (lane >> 3);
-    ychunk[i] = (lane & 7) ^ ((r >> 1) & 7);
-    yvoff[i] = (uint32_t)(r * N * 2) + ((uint32_t)ychunk[i] << 4);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int ch = (lane & 7) ^ ((r >> 1) & 7);
+      yvoff[i] = (uint32_t)(r * N * 2) + ((uint32_t)ch << 4);
+      ylast |= (8 * ch < lastn) << i;
+    }
   }
   int aoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) aoff[j] = bl * AROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
 
-  // per-wave weight tile: row n at n * 64 bytes, 16-byte chunk c at c ^ ((n >> 2) & 3)
+  // per-wave weight tile: row n at n * 80 bytes (the padding keeps both the
+  // row writes and the transposing reads clear of most bank conflicts;
+  // measured against a 64-byte, XOR-swizzled layout)
   uint8_t *bw = bs + wave * BTILE;
-  int bwoff[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) bwoff[c] = lane * 64 + ((c ^ ((lane >> 2) & 3)) << 4);
-  // transposing reads for slice sl: source lane j of group G, half h: row
+  // transposing reads for slice sl, half h: source lane j of group G reads row
   // 32kg + 8sl + 4h + j/4 (the n range the A fragment of lane group kg holds
-  // in slice sl), columns 16(G%2) + 4(j%4): chunk 2(G%2) + (j%4)/2, byte
-  // 8 * ((j%4) & 1)
-  int broff[4][2];
+  // in slice sl), columns 16(G%2) + 4(j%4): 16-byte chunk 2(G%2) + (j%4)/2,
+  // byte 8 * ((j%4) & 1); the slice/half part of the row is an immediate.
+  uint32_t btr;
   {
     const int G = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 32 * (G >> 1) + 8 * sl + 4 * h + (j >> 2);
-        const int chunk = 2 * (G & 1) + ((j & 3) >> 1);
-        broff[sl][h] = row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4) + 8 * (j & 1);
-      }
+    const int rbase = 32 * (G >> 1) + (j >> 2);
+    const int chunk = 2 * (G & 1) + ((j & 3) >> 1);
+    btr = (uint32_t)(uintptr_t)bw + (uint32_t)(rbase * BROW + (chunk << 4) + 8 * (j & 1));
   }
-
   const int64_t ns = (N + TN - 1) / TN;
-  const int64_t ns3 = (ns + 2) / 3 * 3;   // steps run in threes; a padded step has zero weights
   auto clamps = [&](int64_t s) { return s < ns ? s : ns - 1; };
   auto yrsrc = [&](int64_t s) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(ywave + clamps(s) * (TN * 2)), (short)0,
                                              wbytes, 0x00020000);
   };
   auto issue_y1 = [&](__amdgpu_buffer_rsrc_t rs, int64_t s, uint8_t *dst, int i) {
-    const bool in = clamps(s) * TN + 8 * ychunk[i] < N;
+    const bool in = clamps(s) < ns - 1 || ((ylast >> i) & 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * wave + i) * 1024), 16,
                                              in ? yvoff[i] : 0x80000000u, 0, 0, 0);
   };
@@ -404,15 +401,24 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     return (s < ns && s * TN + lane < N) ? v : 0.f;
   };
   // The transposing read is issued as inline assembly: the compiler's wait
-  // insertion cannot tell the intrinsic's LDS address apart from the dY tiles
-  // that buffer-to-LDS loads are filling and would wait for all of those loads
-  // before every such read.  Its results are waited for explicitly
-  // (lgkm_wait) before the MFMA that consumes them.
-  const uint32_t bwaddr = (uint32_t)(uintptr_t)bw;
+  // insertion cannot tell the intrinsic's LDS address from the dY tiles that
+  // buffer-to-LDS loads are filling and would wait for all of those loads
+  // before every such read.  Its results are waited for explicitly (an
+  // lgkmcnt wait) before the MFMA that consumes them.
   auto tr_read = [&](int sl, int h) {
     v4s v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(bwaddr + (uint32_t)broff[sl][h]) : "memory");
+    switch ((8 * sl + 4 * h) * BROW) {   // the row part as an immediate byte offset
+#define NF4_TR(B) case B: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:" #B : "=v"(v) : "v"(btr) : "memory"); break;
+      NF4_TR(0) NF4_TR(320) NF4_TR(640) NF4_TR(960) NF4_TR(1280) NF4_TR(1600) NF4_TR(1920) NF4_TR(2240)
+#undef NF4_TR
+    }
     return v;
+  };
+  auto write_row = [&](const uint32_t st[16]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint4 *>(bw + lane * BROW + (c << 4)) =
+          make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
   };
 
   f32x16 acc[8];
@@ -450,9 +456,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
       lookup4(sa, t, st[4 * c], st[4 * c + 1]);
       lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<uint4 *>(bw + bwoff[c]) = make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
+    write_row(st);
     b0[0] = tr_read(0, 0);
     b0[1] = tr_read(0, 1);
   }
@@ -544,19 +548,19 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
         if (ph == 1) lookup4(sa, t, st[4 * c], st[4 * c + 1]);
         if (ph == 2) lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
       }
-      if (r == 13) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<uint4 *>(bw + bwoff[c]) = make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
-      }
+      if (r == 13) write_row(st);
       sched_cut();
     }
   };
-  for (int64_t s = 0; s < ns3; s += 3) {
+  // steps run in threes (one per LDS stage); the last one or two after the loop
+  int64_t s = 0;
+  for (; s + 3 <= ns; s += 3) {
     step(s, as0, as1, as2, cs1, cs0);
     step(s + 1, as1, as2, as0, cs2, cs1);
     step(s + 2, as2, as0, as1, cs0, cs2);
   }
+  if (s < ns) step(s, as0, as1, as2, cs1, cs0);
+  if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32

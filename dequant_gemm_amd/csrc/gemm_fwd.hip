@@ -251,7 +251,6 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int j = 0; j < 4; ++j) aoff[j] = bl * XROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
 
   const int64_t nk = K / BK;
-  const int64_t nk3 = (nk + 2) / 3 * 3;  // steps run in threes; a padded step has a^ = 0
   auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
   auto xrsrc = [&](int64_t kt) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + clampk(kt) * (BK * 2)), (short)0,
@@ -376,11 +375,15 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
       sched_cut();
     }
   };
-  for (int64_t kt = 0; kt < nk3; kt += 3) {
+  // steps run in threes (one per LDS stage); the last one or two after the loop
+  int64_t kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
     step(kt, xs0, xs1, xs2, cs1, cs2);
     step(kt + 1, xs1, xs2, xs0, cs2, cs0);
     step(kt + 2, xs2, xs0, xs1, cs0, cs1);
   }
+  if (kt < nk) step(kt, xs0, xs1, xs2, cs1, cs2);
+  if (kt + 1 < nk) step(kt + 1, xs1, xs2, xs0, cs2, cs0);
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
