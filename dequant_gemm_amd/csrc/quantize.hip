@@ -12,8 +12,9 @@
 //                            accumulators per workgroup (plain stores)
 //   quantize_tail_kernel     the one partial block at the end, if any (its own
 //                            accumulator row)
-//   mean_reduce_kernel       sums the rows column by column; the last
-//                            workgroup forms the exact mean, one rounding
+//   mean_reduce_kernel       sums the rows (each workgroup a share of whole
+//                            rows); the last workgroup adds the shares and
+//                            forms the exact mean, one rounding
 //   double_quant_kernel      int8 absmax and one fp32 scale per 256 blocks
 #include "nf4_launch.h"
 
@@ -234,12 +235,14 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
 // Exact mean of all block absmax values, rounded once to fp32 (nearest-even).
 // Every finite fp32 is an integer number of 2^-149 units; column e of the
 // accumulator rows holds sums of the 24-bit significands of the values with
-// biased exponent e, worth 2^(max(e,1)-1) units each.  Workgroup e sums
-// column e over all rows; the last workgroup to finish (an arrival counter
-// that the quantize kernel cleared) forms the total S (at most ~310 bits) as
-// a multi-word integer, divides it by the block count with 32 extra quotient
-// bits -- enough to reach below the smallest subnormal -- and rounds on the
-// remainder.
+// biased exponent e, worth 2^(max(e,1)-1) units each.  The workgroups of
+// mean_reduce_kernel each sum a share of the rows (coalesced row reads) into
+// one row of totals; the last workgroup to finish (an arrival counter that
+// the quantize kernel cleared) adds those rows in a fixed order -- integer
+// sums, so the result does not depend on any order -- forms the total S
+// (at most ~310 bits) as a multi-word integer, divides it by the block count
+// with 32 extra quotient bits -- enough to reach below the smallest subnormal
+// -- and rounds on the remainder.
 // `sums` holds the 256 column totals, `nz` a bitmask of the non-zero ones.
 __device__ float mean_from_sums(const unsigned long long *sums, const unsigned long long nz[4],
                                 uint32_t nblocks) {
@@ -270,13 +273,27 @@ __device__ float mean_from_sums(const unsigned long long *sums, const unsigned l
     num[i] = (uint32_t)t;
     carry = t >> 32;
   }
+  // long division by nblocks, one 32-bit digit at a time: the digit
+  // cur / nblocks (< 2^32 since rem < nblocks) is estimated in fp64 -- cur is
+  // below nblocks * 2^32, so its rounding moves the estimate by less than one
+  // -- and corrected exactly with an integer multiply-subtract
   uint32_t q[W];
   unsigned long long rem = 0;
+  const double dd = (double)nblocks, inv = 1.0 / dd;
 #pragma unroll
   for (int i = W - 1; i >= 0; --i) {
     const unsigned long long cur = (rem << 32) | num[i];
-    q[i] = (uint32_t)(cur / nblocks);
-    rem = cur % nblocks;
+    long long qe = (long long)((double)cur * inv);
+    long long r = (long long)(cur - (unsigned long long)qe * nblocks);
+    if (r < 0) {
+      --qe;
+      r += nblocks;
+    } else if (r >= (long long)nblocks) {
+      ++qe;
+      r -= nblocks;
+    }
+    q[i] = (uint32_t)qe;
+    rem = (unsigned long long)r;
   }
   int L = 0;
 #pragma unroll
@@ -317,31 +334,50 @@ __device__ float mean_from_sums(const unsigned long long *sums, const unsigned l
   return __uint_as_float(bits);
 }
 
+constexpr int kMeanGrid = 32;
+
 __global__ __launch_bounds__(256) void mean_reduce_kernel(
-    const unsigned long long *__restrict__ partials, int nrows, uint32_t nblocks,
+    unsigned long long *__restrict__ partials, int nrows, uint32_t nblocks,
     unsigned long long *__restrict__ colsum, unsigned int *__restrict__ arrivals,
     float *__restrict__ mean_out) {
   __shared__ unsigned long long red[256];
   __shared__ bool last;
-  const int e = blockIdx.x, t = threadIdx.x;
-  unsigned long long acc = 0;  // each partial sum is below 2^55: no overflow
-  for (int r = t; r < nrows; r += 256) acc += partials[(int64_t)r * 256 + e];
-  red[t] = acc;
+  const int t = threadIdx.x;
+  const int g = gridDim.x;
+  // workgroup b sums rows b, b+g, b+2g, .. (coalesced) and, being the only
+  // reader of row b, writes its column totals back over it
+  unsigned long long acc = 0;  // each row entry is below 2^55 and there are at most 1026 rows
+  int r = blockIdx.x;
+  for (; r + 15 * g < nrows; r += 16 * g) {  // sixteen independent loads in flight, then the adds
+    unsigned long long v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = partials[(int64_t)(r + i * g) * 256 + t];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += v[i];
+  }
+  for (; r < nrows; r += g) acc += partials[(int64_t)r * 256 + t];
+  partials[(int64_t)blockIdx.x * 256 + t] = acc;
+  __threadfence();
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
-  }
-  if (t == 0) {
-    colsum[e] = red[0];
-    __threadfence();
-    last = atomicAdd(arrivals, 1u) == gridDim.x - 1;
-  }
+  if (t == 0) last = atomicAdd(arrivals, 1u) == g - 1;
   __syncthreads();
   if (!last) return;
   __threadfence();
+  // the last workgroup adds the g rows of totals (plain loads: the fence above
+  // makes the other workgroups' rows visible, and this workgroup has not read
+  // them before)
+  unsigned long long v = 0;
+  int b = 0;
+  for (; b + 16 <= g; b += 16) {
+    unsigned long long w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = partials[(int64_t)(b + i) * 256 + t];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v += w[i];
+  }
+  for (; b < g; ++b) v += partials[(int64_t)b * 256 + t];
+  colsum[t] = v;
   __shared__ unsigned long long nz[4];
-  const unsigned long long v = __hip_atomic_load(&colsum[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   red[t] = v;
   const unsigned long long ball = __ballot(v != 0);
   if ((t & 63) == 0) nz[t >> 6] = ball;
@@ -420,7 +456,8 @@ hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t 
     ++rows;
   }
   if (dq) {
-    hipLaunchKernelGGL(mean_reduce_kernel, dim3(256), dim3(256), 0, stream, partials, rows, (uint32_t)nblocks,
+    const int mg = rows < kMeanGrid ? rows : kMeanGrid;
+    hipLaunchKernelGGL(mean_reduce_kernel, dim3((unsigned)mg), dim3(256), 0, stream, partials, rows, (uint32_t)nblocks,
                        colsum, arrivals, mean_out);
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
     hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ngroups), dim3(64), 0, stream, absmax_out, nblocks, mean_out, q_out, scale_out);
