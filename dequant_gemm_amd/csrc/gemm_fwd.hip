@@ -202,6 +202,25 @@ __device__ __forceinline__ void make_lut_quarter(float ahat, int q, Lut &t) {
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
 
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+
+// Interleave a scheduling region as `n` repetitions of: one MFMA, `nds` LDS
+// reads, `nv` VALU instructions and, every `vm_every`-th time, one vector
+// memory load.  A few vector-ALU instructions after each MFMA overlap the
+// matrix core almost completely; a burst after one MFMA does not, even with
+// a second wave on the SIMD.
+template <int n, int nds, int nv, int vm_every>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if (nds) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VALU, nv, 0);
+    if (vm_every && i % (vm_every ? vm_every : 1) == 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+  }
+}
+
 template <bool Y_BF16, bool DQ>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_large_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
@@ -272,8 +291,12 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  uint4 a[8];      // A fragments; pair g is refilled for the next slice right after its MFMAs issue
-  uint32_t b0[4], b1[4];
+  uint4 a[8];      // A fragments; each is refilled for the next slice right after its MFMA issues
+  // B fragments rotate through three buffers: step k's slices 0..3 take
+  // p0, p1, p2, p0 with (p0, p1, p2) = (k, k+1, k+2) mod 3, and step k+1's
+  // first word goes to p1, so every word can be dequantized a slice or more
+  // ahead into a buffer no MFMA is reading.
+  uint32_t bb0[4], bb1[4], bb2[4];
   uint4 cw;        // codes of the current step
   Lut lut;         // LUT of the current step
   // codes of the next two steps, in flight: step kt + 1 + i sits in slot
@@ -281,8 +304,9 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   // slot keeps its registers (a loop-carried copy would wait for the load)
   StepCodes cs0, cs1, cs2;
 
-  // prologue: tiles 0 and 1 and the codes of steps 0 and 1 in flight (in the
-  // steady state's order: a tile, then the codes of the step before it)
+  // prologue: the codes of steps 0 and 1 and tiles 0 and 1; all complete
+  // before the barrier (the compiler may reorder these loads, so the wait
+  // counts none of them as outstanding)
   {
     StepCodes c0;
     issue_codes(0, c0);
@@ -298,92 +322,111 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int q = 0; q < 4; ++q) make_lut_quarter(ah, q, lut);
     Sel4 sa, sb;
     select8(cw.x, sa, sb);
-    lookup4(sa, lut, b0[0], b0[1]);
-    lookup4(sb, lut, b0[2], b0[3]);
+    lookup4(sa, lut, bb0[0], bb0[1]);
+    lookup4(sb, lut, bb0[2], bb0[3]);
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + (DQ ? 3 : 2)));   // tile 0 landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
+  sched_cut();
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(xs0 + aoff[0] + i * 32 * XROW);
 
-  // One K-step as 16 groups of two MFMAs (slice j = groups 4j .. 4j+3), each
-  // group followed by its share of the other work; sched_cut keeps that order.
-  //   A reads     slices 0-2: the group's two fragments again, for the next
-  //               slice; groups 14-15: four fragments each of the next step's
-  //               slice 0 (from `nx`), in registers whose MFMAs have issued.
-  //   tile loads  the tile two steps ahead, into `ld` (free since the previous
-  //               hand-over): one load in each of groups 0, 4, 8, 12.
-  //   dequant     code word j+1 during slice j; the next step's LUT during
-  //               slice 2 and its first word during the first half of slice 3.
-  //   hand-over   after group 13: this wave's LDS reads and the next tile's
-  //               loads are complete (only the four loads of the tile two
-  //               steps ahead may be outstanding), then the barrier, then the
-  //               codes two steps ahead.
-  auto step = [&](int64_t kt, uint8_t *rd, uint8_t *nx, uint8_t *ld, const StepCodes &cn, StepCodes &cfill) {
-    Sel4 sa, sb;
-    float ahn = 0.f;
+  // One K-step: four slices of 8 MFMAs (one per 32-row tile), each a
+  // scheduling region whose other work is interleaved evenly between its
+  // MFMAs (about four vector-ALU instructions each):
+  //   slice j < 3   A fragments of slice j+1 (each refilled right after its
+  //                 MFMA); one load of the tile two steps ahead into `ld`
+  //                 (free since the previous hand-over)
+  //   dequant       slice 0: word 1 and word 2's selectors; slice 1: word
+  //                 2's lookups and half of word 3; slice 2: the rest of word
+  //                 3, the next step's a^ and three quarters of its LUT (in
+  //                 place, after word 3's last lookup); slice 3: the last
+  //                 quarter and the next step's first word
+  //   hand-over     after four MFMAs of slice 3: this wave's LDS reads and
+  //                 the next tile's loads complete (only the four loads of the
+  //                 tile two steps ahead may be outstanding), the barrier, the
+  //                 codes two steps ahead; the slice's last four MFMAs cover
+  //                 the reads of the next step's slice-0 fragments from `nx`
+  auto step = [&](int64_t kt, uint8_t *rd, uint8_t *nx, uint8_t *ld, const StepCodes &cn, StepCodes &cfill,
+                  uint32_t *p0, uint32_t *p1, uint32_t *p2) {
+    Sel4 sa, sb, sc, sd;
     const __amdgpu_buffer_rsrc_t rsl = xrsrc(kt + 2);
+    // slice 0
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int slice = r / 4, g = r % 4;
-      uint32_t *bcur = (slice & 1) ? b1 : b0;
-      uint32_t *bnext = (slice & 1) ? b0 : b1;
-      if (r == 14) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4) & ~(0xF << 8));   // vmcnt(4) lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        sched_cut();
-        issue_codes(kt + 2, cfill);
-        sched_cut();
-      }
-      mfma2(acc[2 * g], acc[2 * g + 1], a[2 * g], a[2 * g + 1], bcur);
-      if (slice < 3) {
-        const int off = aoff[slice + 1];
-        a[2 * g] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g) * 32 * XROW);
-        a[2 * g + 1] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g + 1) * 32 * XROW);
-      } else if (r >= 14) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * (r - 14) + u;
-          a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * XROW);
-        }
-      }
-      if (g == 0) issue_x1(rsl, ld, slice);
-      // dequantization: word j+1 during slice j (its last use of the LUT is
-      // in group 11); the next step's LUT replaces it in groups 12-13 and
-      // that step's first word is dequantized in groups 14-15
-      if (slice < 3) {
-        const uint32_t d = slice == 0 ? cw.y : (slice == 1 ? cw.z : cw.w);
-        if (g == 1) select8(d, sa, sb);
-        if (g == 2) lookup4(sa, lut, bnext[0], bnext[1]);
-        if (g == 3) lookup4(sb, lut, bnext[2], bnext[3]);
-      }
-      if (r == 8) ahn = ahat_at(kt + 1, cn);
-      if (r == 12) {
-        make_lut_quarter(ahn, 0, lut);
-        make_lut_quarter(ahn, 1, lut);
-      }
-      if (r == 13) {
-        make_lut_quarter(ahn, 2, lut);
-        make_lut_quarter(ahn, 3, lut);
-      }
-      if (r == 14) {
-        cw = cn.w;
-        select8(cw.x, sa, sb);
-        lookup4(sa, lut, b0[0], b0[1]);
-      }
-      if (r == 15) lookup4(sb, lut, b0[2], b0[3]);
-      sched_cut();
+    for (int i = 0; i < 8; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
+      a[i] = *reinterpret_cast<const uint4 *>(rd + aoff[1] + i * 32 * XROW);
     }
+    issue_x1(rsl, ld, 0);
+    select8(cw.y, sa, sb);
+    lookup4(sa, lut, p1[0], p1[1]);
+    lookup4(sb, lut, p1[2], p1[3]);
+    select8(cw.z, sc, sd);
+    interleave<8, 1, 5, 8>();
+    sched_cut();
+    // slice 1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p1), acc[i], 0, 0, 0);
+      a[i] = *reinterpret_cast<const uint4 *>(rd + aoff[2] + i * 32 * XROW);
+    }
+    issue_x1(rsl, ld, 1);
+    lookup4(sc, lut, p2[0], p2[1]);
+    lookup4(sd, lut, p2[2], p2[3]);
+    select8(cw.w, sa, sb);
+    lookup4(sa, lut, p0[0], p0[1]);
+    interleave<8, 1, 5, 8>();
+    sched_cut();
+    // slice 2
+    const float ahn = ahat_at(kt + 1, cn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p2), acc[i], 0, 0, 0);
+      a[i] = *reinterpret_cast<const uint4 *>(rd + aoff[3] + i * 32 * XROW);
+    }
+    issue_x1(rsl, ld, 2);
+    lookup4(sb, lut, p0[2], p0[3]);
+    make_lut_quarter(ahn, 0, lut);
+    make_lut_quarter(ahn, 1, lut);
+    make_lut_quarter(ahn, 2, lut);
+    interleave<8, 1, 5, 8>();
+    sched_cut();
+    // slice 3, first half
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
+    issue_x1(rsl, ld, 3);
+    make_lut_quarter(ahn, 3, lut);
+    cw = cn.w;
+    select8(cw.x, sa, sb);
+    interleave<4, 0, 5, 4>();
+    sched_cut();
+    // hand-over
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4) & ~(0xF << 8));   // vmcnt(4) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    sched_cut();
+    issue_codes(kt + 2, cfill);
+    sched_cut();
+    // slice 3, second half
+#pragma unroll
+    for (int i = 4; i < 8; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * XROW);
+    lookup4(sa, lut, p1[0], p1[1]);
+    lookup4(sb, lut, p1[2], p1[3]);
+    interleave<4, 2, 4, 0>();
+    sched_cut();
   };
-  // steps run in threes (one per LDS stage); the last one or two after the loop
+  // steps run in threes (one per LDS stage, code slot and B-buffer rotation); the last one or two after the loop
   int64_t kt = 0;
   for (; kt + 3 <= nk; kt += 3) {
-    step(kt, xs0, xs1, xs2, cs1, cs2);
-    step(kt + 1, xs1, xs2, xs0, cs2, cs0);
-    step(kt + 2, xs2, xs0, xs1, cs0, cs1);
+    step(kt, xs0, xs1, xs2, cs1, cs2, bb0, bb1, bb2);
+    step(kt + 1, xs1, xs2, xs0, cs2, cs0, bb1, bb2, bb0);
+    step(kt + 2, xs2, xs0, xs1, cs0, cs1, bb2, bb0, bb1);
   }
-  if (kt < nk) step(kt, xs0, xs1, xs2, cs1, cs2);
-  if (kt + 1 < nk) step(kt + 1, xs1, xs2, xs0, cs2, cs0);
+  if (kt < nk) step(kt, xs0, xs1, xs2, cs1, cs2, bb0, bb1, bb2);
+  if (kt + 1 < nk) step(kt + 1, xs1, xs2, xs0, cs2, cs0, bb1, bb2, bb0);
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32

@@ -44,7 +44,7 @@ def _run(M, N, K, seed, dq=True, out_dtype=torch.float32, wdtype=torch.bfloat16)
     (1, 300, 320), (5, 17, 64), (16, 1000, 192), (3, 4096, 4096),
     (16, 200, 4096), (2, 64, 8192), (1, 48, 40960),                  # small-M: X from global, many K chunks
     (17, 300, 256), (100, 513, 128), (256, 256, 256), (300, 700, 512),  # large-M kernel, ragged tiles
-    (513, 129, 64), (1000, 64, 1024),
+    (513, 129, 64), (1000, 64, 1024), (400, 260, 192), (769, 384, 320),
 ])
 def test_fwd_bwd_ragged(M, N, K):
     Y, dX, x, dy, wh = _run(M, N, K, 7 * M + N + K)
