@@ -67,6 +67,25 @@ def wq_bytes(rows, cols):
     return -(-numel // 2) + nb + 4 * (-(-nb // 256)) + 4
 
 
+def time_graph(fn, reps, per_graph=20):
+    """Average milliseconds per call of ``fn`` replayed from a HIP graph of ``per_graph`` calls.
+
+    For kernels shorter than the host's per-call launch cost (tens of microseconds
+    through ctypes), back-to-back eager calls would time the host, not the kernel.
+    """
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = time_events(g.replay, reps) / per_graph
+    del g
+    return ms
+
+
 def time_events(fn, reps, stream=None):
     """Average milliseconds of ``fn`` over ``reps`` calls between two HIP events."""
     s = torch.cuda.Event(enable_timing=True)
@@ -145,13 +164,16 @@ def bench_prefill(dg, steps, warmup):
 
     # dequantize (context: the unfused path's first half)
     Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
-    ms_dq = time_events(lambda: dg.nf4_dequantize(q, out=Wh), 20)
+    ms_dq = time_graph(lambda: dg.nf4_dequantize(q, out=Wh), 10)
     bdq = wq_bytes(N, K) + N * K * 2
     res["ops"]["dequantize"] = {"ms": ms_dq, "GB/s": bdq / (ms_dq * 1e-3) / 1e9,
                                 "frac_hbm": bdq / (ms_dq * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     # the naive dequantize-then-multiply the pages compare against, for context
-    Xf = X
-    ms_naive = time_events(lambda: (dg.nf4_dequantize(q, out=Wh), torch.matmul(Xf, Wh.t())), 10)
+    naive = lambda: (dg.nf4_dequantize(q, out=Wh), torch.matmul(X, Wh.t()))
+    for _ in range(3):          # library load and kernel selection happen on the first calls
+        naive()
+    torch.cuda.synchronize()
+    ms_naive = time_events(naive, 10)
     res["ops"]["naive_dequant_then_matmul_fwd"] = {"ms": ms_naive, "TFLOP/s": flop / (ms_naive * 1e-3) / 1e12}
     del W, X, dY, Y, dX, Wh, ws
     return res
@@ -187,6 +209,17 @@ def bench_decode(dg, pool=64, reps=20):
                                "frac_hbm": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                                "TFLOP/s": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
         del g
+    # Context: the per-call floor of this measurement -- a one-element kernel replayed
+    # the same way (64 launches per graph).  No kernel can take less per call here.
+    t = torch.zeros(1, device=d)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(pool):
+            t.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    out["decode_launch_floor"] = {"us": time_events(g.replay, reps) / pool * 1e3,
+                                  "what": "one-element kernel, 64 per HIP graph, per call"}
     return out
 
 

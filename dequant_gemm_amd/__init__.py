@@ -3,9 +3,15 @@
 The work runs in ``libnf4.so`` (hand-written HIP for gfx950, C ABI in
 ``include/nf4.h``); this package is its thin Python binding.  Build the library
 with ``python -m dequant_gemm_amd.build``.
+
+Above the C ABI: ``dequant_gemm_amd.nn`` (NF4Linear, a frozen quantized linear
+layer with autograd over the fused GEMMs) and ``dequant_gemm_amd.io`` (saving
+and loading quantized weights).
 """
 from ._lib import (  # noqa: F401
     BLOCKSIZE, DQ_GROUP, EXPORTS, LIB_PATH, NF4Error, QTensor, QTensorStruct,
     empty_qtensor, lib, nf4_codebook, nf4_dequantize, nf4_matmul_bwd_dx, nf4_matmul_fwd,
     nf4_quantize, nf4_sizes, nf4_thresholds,
 )
+from .io import load_qtensor, load_qtensors, save_qtensor, save_qtensors  # noqa: F401,E402
+from .nn import NF4Linear, nf4_linear, quantize_linears  # noqa: F401,E402

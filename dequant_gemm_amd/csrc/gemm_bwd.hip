@@ -279,19 +279,6 @@ __device__ __forceinline__ void tile_of_main(int bid, int tiles_m, int tiles_k, 
   tk = in_group / gsize;
 }
 
-template <bool DQ>
-__device__ __forceinline__ AbsmaxRaw load_raw(const AbsmaxSrc &s, int64_t blk) {
-  AbsmaxRaw r;
-  if (DQ) {
-    r.q = s.q[blk];
-    r.v = s.scale[blk >> 8];
-  } else {
-    r.q = 0;
-    r.v = s.absmax[blk];
-  }
-  return r;
-}
-
 struct RowCodes {
   uint4 w;        // 32 codes of this lane's weight row
   AbsmaxRaw r;

@@ -106,6 +106,22 @@ __device__ __forceinline__ AbsmaxRaw load_absmax_raw(const AbsmaxSrc &s, int64_t
   return r;
 }
 
+// The same with the storage form fixed at compile time, so that no branch sits
+// between a lane's loads (a load inside a runtime branch is waited for before
+// the branch ends, which would serialise it with the loads issued after it).
+template <bool DQ>
+__device__ __forceinline__ AbsmaxRaw load_raw(const AbsmaxSrc &s, int64_t blk) {
+  AbsmaxRaw r;
+  if (DQ) {
+    r.q = s.q[blk];
+    r.v = s.scale[blk >> 8];
+  } else {
+    r.q = 0;
+    r.v = s.absmax[blk];
+  }
+  return r;
+}
+
 __device__ __forceinline__ float ahat_of(const AbsmaxRaw &r, int dq, float mu) {
   return dq ? __fadd_rn(__fmul_rn((float)r.q, r.v), mu) : r.v;
 }
