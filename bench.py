@@ -175,6 +175,22 @@ def bench_prefill(dg, steps, warmup):
     torch.cuda.synchronize()
     ms_naive = time_events(naive, 10)
     res["ops"]["naive_dequant_then_matmul_fwd"] = {"ms": ms_naive, "TFLOP/s": flop / (ms_naive * 1e-3) / 1e12}
+    # the same GEMMs with a rank-64 low-rank adapter term fused in (U, B / V, A^T bf16)
+    r = 64
+    U = synth.normal((M, r), 1.0, 2100).to(d)
+    Bl = synth.normal((N, r), 0.1, 2101).to(d)
+    V = synth.normal((M, r), 1.0, 2102).to(d)
+    At = synth.normal((K, r), 0.1, 2103).to(d)
+    for name, fn, base in (
+            ("fwd_lora_r64", lambda: dg.nf4_matmul_fwd_lora(X, q, U, Bl, out=Y), "fwd"),
+            ("bwd_dx_lora_r64", lambda: dg.nf4_matmul_bwd_dx_lora(dY, q, V, At, out=dX), "bwd_dx")):
+        fn()
+        torch.cuda.synchronize()
+        ms_l = time_events(fn, 10)
+        fl = flop + 2.0 * M * (N if base == "fwd" else K) * r
+        res["ops"][name] = {"ms": ms_l, "TFLOP/s": fl / (ms_l * 1e-3) / 1e12,
+                            "time_vs_plain": ms_l / per[base]}
+    del U, Bl, V, At
     del W, X, dY, Y, dX, Wh, ws
     return res
 

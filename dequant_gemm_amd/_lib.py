@@ -30,7 +30,10 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_thresholds", "nf4_sizes", "nf4_quantize",
-           "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx")
+           "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx", "nf4_matmul_fwd_lora",
+           "nf4_matmul_bwd_dx_lora")
+LORA_RANK_STEP = 16
+LORA_MAX_RANK = 1024
 
 
 class QTensorStruct(ctypes.Structure):
@@ -64,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.nf4_dequantize.argtypes = [ctypes.POINTER(QTensorStruct), vp, i32, vp]
         L.nf4_matmul_fwd.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
         L.nf4_matmul_bwd_dx.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
+        L.nf4_matmul_fwd_lora.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, vp, i64, vp, i32, vp]
+        L.nf4_matmul_bwd_dx_lora.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, vp, i64, vp, i32, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -235,4 +240,53 @@ def nf4_matmul_bwd_dx(dY: torch.Tensor, q: QTensor, out_dtype: torch.dtype = tor
     st = q.struct()
     _check(lib().nf4_matmul_bwd_dx(dY.data_ptr(), M, ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype),
                                    _stream(dY.device)), "nf4_matmul_bwd_dx")
+    return out
+
+
+def _lowrank_operands(U: torch.Tensor, V: torch.Tensor, M: int, cols: int, names: tuple) -> int:
+    for t, nm in zip((U, V), names):
+        _require_device(t, nm)
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise ValueError(f"{nm} must be a 2-D bf16 tensor")
+    r = U.shape[1]
+    if U.shape[0] != M or V.shape != (cols, r):
+        raise ValueError(f"{names[0]} must be [{M}, r] and {names[1]} [{cols}, r] (got {tuple(U.shape)}, "
+                         f"{tuple(V.shape)})")
+    return r
+
+
+def nf4_matmul_fwd_lora(X: torch.Tensor, q: QTensor, U: torch.Tensor, B: torch.Tensor,
+                        out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X W^T + U B^T in one fused pass.  U: bf16 [M, r] (the adapter's X A^T); B: bf16 [N, r]."""
+    _require_device(X, "X")
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or X.shape[1] != q.cols:
+        raise ValueError("X must be bf16 [M, q.cols]")
+    M = X.shape[0]
+    r = _lowrank_operands(U, B, M, q.rows, ("U", "B"))
+    if out is None:
+        out = torch.empty((M, q.rows), dtype=out_dtype, device=X.device)
+    _require_device(out, "out")
+    st = q.struct()
+    _check(lib().nf4_matmul_fwd_lora(X.data_ptr(), M, ctypes.byref(st), U.data_ptr(), B.data_ptr(), r,
+                                     out.data_ptr(), _dtype_enum(out.dtype), _stream(X.device)),
+           "nf4_matmul_fwd_lora")
+    return out
+
+
+def nf4_matmul_bwd_dx_lora(dY: torch.Tensor, q: QTensor, V: torch.Tensor, At: torch.Tensor,
+                           out_dtype: torch.dtype = torch.float32,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX = dY W^ + V A in one fused pass.  V: bf16 [M, r] (dY B); At: bf16 [K, r] (A transposed)."""
+    _require_device(dY, "dY")
+    if dY.dtype != torch.bfloat16 or dY.dim() != 2 or dY.shape[1] != q.rows:
+        raise ValueError("dY must be bf16 [M, q.rows]")
+    M = dY.shape[0]
+    r = _lowrank_operands(V, At, M, q.cols, ("V", "At"))
+    if out is None:
+        out = torch.empty((M, q.cols), dtype=out_dtype, device=dY.device)
+    _require_device(out, "out")
+    st = q.struct()
+    _check(lib().nf4_matmul_bwd_dx_lora(dY.data_ptr(), M, ctypes.byref(st), V.data_ptr(), At.data_ptr(), r,
+                                        out.data_ptr(), _dtype_enum(out.dtype), _stream(dY.device)),
+           "nf4_matmul_bwd_dx_lora")
     return out

@@ -57,11 +57,11 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_k, int &
   tk = in_group / gsize;
 }
 
-template <bool DX_BF16>
+template <bool DX_BF16, bool LR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_generic_kernel(const uint16_t *__restrict__ dY, int64_t M,
                                                      int64_t N, int64_t K,
                                                      const uint8_t *__restrict__ packed,
-                                                     AbsmaxSrc src, void *__restrict__ dX,
+                                                     AbsmaxSrc src, LowRank lr, void *__restrict__ dX,
                                                      int tiles_m, int tiles_k) {
   __shared__ __attribute__((aligned(16))) uint8_t sa[2][TM * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t sb[2][TK * ROWB];
@@ -209,6 +209,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();
   }
 
+  if (LR) {
+    // adapter term, rank slices of 16: lane group kg takes ranks 16s + 8kg .. +7
+    // (rows past M and columns past K read existing ones; never stored)
+    const uint16_t *vrow[4], *urow[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t col = k0 + 128 * wk + 32 * t + bl;
+      vrow[t] = lr.v + (col < K ? col : K - 1) * lr.r + 8 * kg;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = m0 + 128 * wm + 32 * i + bl;
+      urow[i] = lr.u + (row < M ? row : M - 1) * lr.r + 8 * kg;
+    }
+    for (int s = 0; s < lr.r / 16; ++s) {
+      uint4 bv[4], av[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bv[t] = *reinterpret_cast<const uint4 *>(vrow[t] + 16 * s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const uint4 *>(urow[i] + 16 * s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[i]), as_bf16x8(bv[t]), acc[i][t], 0, 0, 0);
+    }
+  }
+
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t col = k0 + 128 * wk + 32 * t + bl;
@@ -301,10 +329,10 @@ __device__ __forceinline__ void lut_quarter(float ahat, int q, Lut &t) {
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
 
-template <bool DX_BF16, bool DQ>
+template <bool DX_BF16, bool DQ, bool LR>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dx_kernel(
     const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    AbsmaxSrc src, void *__restrict__ dX, int tiles_m, int tiles_k) {
+    AbsmaxSrc src, LowRank lr, void *__restrict__ dX, int tiles_m, int tiles_k) {
   __shared__ __attribute__((aligned(1024))) uint8_t as0[ATILE];
   __shared__ __attribute__((aligned(1024))) uint8_t as1[ATILE];
   __shared__ __attribute__((aligned(1024))) uint8_t as2[ATILE];
@@ -549,6 +577,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   if (s < ns) step(s, as0, as1, as2, cs1, cs0);
   if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
   __builtin_amdgcn_s_waitcnt(0);
+  if (LR) add_lowrank_32x8(acc, lr, m0, M, kc + bl, bl, kg);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   const int64_t col = kcol + bl;
@@ -574,31 +603,33 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
 }  // namespace
 
 hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                         const AbsmaxSrc &src, void *dx, int dx_is_bf16, hipStream_t stream) {
+                         const AbsmaxSrc &src, const LowRank &lr, void *dx, int dx_is_bf16,
+                         hipStream_t stream) {
   const uint16_t *dY = reinterpret_cast<const uint16_t *>(dy);
+  const bool has_lr = lr.r > 0;
   if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
     using namespace tr_kernel;
+    using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
+                         int, int);
+    static const K_t kern[8] = {
+        bwd_dx_kernel<false, false, false>, bwd_dx_kernel<false, false, true>,
+        bwd_dx_kernel<false, true, false>,  bwd_dx_kernel<false, true, true>,
+        bwd_dx_kernel<true, false, false>,  bwd_dx_kernel<true, false, true>,
+        bwd_dx_kernel<true, true, false>,   bwd_dx_kernel<true, true, true>};
+    const int sel = (dx_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (has_lr ? 1 : 0);
     const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
     const dim3 g((unsigned)(tiles_m * tiles_k)), b(64 * NWAVE);
-    if (src.dq) {
-      if (dx_is_bf16)
-        hipLaunchKernelGGL((bwd_dx_kernel<true, true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-      else
-        hipLaunchKernelGGL((bwd_dx_kernel<false, true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-    } else {
-      if (dx_is_bf16)
-        hipLaunchKernelGGL((bwd_dx_kernel<true, false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-      else
-        hipLaunchKernelGGL((bwd_dx_kernel<false, false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-    }
+    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
   } else {
     using namespace generic;
+    using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
+                         int, int);
+    static const K_t kern[4] = {bwd_dx_generic_kernel<false, false>, bwd_dx_generic_kernel<false, true>,
+                                bwd_dx_generic_kernel<true, false>, bwd_dx_generic_kernel<true, true>};
+    const int sel = (dx_is_bf16 ? 2 : 0) | (has_lr ? 1 : 0);
     const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
     const dim3 g((unsigned)(tiles_m * tiles_k)), b(256);
-    if (dx_is_bf16)
-      hipLaunchKernelGGL((bwd_dx_generic_kernel<true>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-    else
-      hipLaunchKernelGGL((bwd_dx_generic_kernel<false>), g, b, 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
   }
   return hipGetLastError();
 }

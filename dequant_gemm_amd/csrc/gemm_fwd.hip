@@ -40,10 +40,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kSmallCols = 16;
 constexpr int kSmallWaves = 8;
 
-template <bool Y_BF16, bool DQ>
+template <bool Y_BF16, bool DQ, bool LR>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     const uint16_t *__restrict__ X, int M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    AbsmaxSrc src, void *__restrict__ Y) {
+    AbsmaxSrc src, LowRank lr, void *__restrict__ Y) {
   __shared__ f32x4 red[kSmallWaves - 1][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
@@ -101,6 +101,19 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
         lookup4(sb, t, b[2], b[3]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u][j]), as_bf16x8(b), acc, 0, 0, 0);
       }
+    }
+  }
+  if (LR) {
+    // adapter term: rank slices of 32 dealt to the waves; lane group kg takes
+    // ranks 32s + 8kg .. +7 of both operands (zeros past r)
+    for (int s = wave; 32 * s < lr.r; s += kSmallWaves) {
+      const int rk = 32 * s + 8 * kg;
+      uint4 av = make_uint4(0u, 0u, 0u, 0u), bv = make_uint4(0u, 0u, 0u, 0u);
+      if (rk < lr.r) {
+        bv = *reinterpret_cast<const uint4 *>(lr.v + nc * lr.r + rk);
+        if (mvalid) av = *reinterpret_cast<const uint4 *>(lr.u + (int64_t)m * lr.r + rk);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
     }
   }
   if (wave > 0) red[wave - 1][lane] = acc;
@@ -218,10 +231,10 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <bool Y_BF16, bool DQ>
+template <bool Y_BF16, bool DQ, bool LR>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_large_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    AbsmaxSrc src, void *__restrict__ Y, int tiles_m, int tiles_n) {
+    AbsmaxSrc src, LowRank lr, void *__restrict__ Y, int tiles_m, int tiles_n) {
   // separate arrays (not one indexed by stage) so that the compiler can tell
   // the tile being read from the tiles being loaded
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[XTILE];
@@ -425,6 +438,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   if (kt < nk) step(kt, xs0, xs1, xs2, cs1, cs2, bb0, bb1, bb2);
   if (kt + 1 < nk) step(kt + 1, xs1, xs2, xs0, cs2, cs0, bb1, bb2, bb0);
   __builtin_amdgcn_s_waitcnt(0);
+  if (LR) add_lowrank_32x8(acc, lr, m0, M, nc, bl, kg);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   if (ncol < N) {
@@ -448,27 +462,29 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
 }  // namespace
 
 hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                      const AbsmaxSrc &src, void *y, int y_is_bf16, hipStream_t stream) {
+                      const AbsmaxSrc &src, const LowRank &lr, void *y, int y_is_bf16, hipStream_t stream) {
   const uint16_t *X = reinterpret_cast<const uint16_t *>(x);
+  const int sel = (y_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (lr.r > 0 ? 1 : 0);
   if (M <= 16) {
+    using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *);
+    static const K_t kern[8] = {
+        fwd_small_kernel<false, false, false>, fwd_small_kernel<false, false, true>,
+        fwd_small_kernel<false, true, false>,  fwd_small_kernel<false, true, true>,
+        fwd_small_kernel<true, false, false>,  fwd_small_kernel<true, false, true>,
+        fwd_small_kernel<true, true, false>,   fwd_small_kernel<true, true, true>};
     const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols)), b(64 * kSmallWaves);
-    auto kern = src.dq ? (y_is_bf16 ? fwd_small_kernel<true, true> : fwd_small_kernel<false, true>)
-                       : (y_is_bf16 ? fwd_small_kernel<true, false> : fwd_small_kernel<false, false>);
-    hipLaunchKernelGGL(kern, g, b, 0, stream, X, (int)M, N, K, packed, src, y);
+    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr, y);
   } else {
+    using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
+                         int, int);
+    static const K_t kern[8] = {
+        fwd_large_kernel<false, false, false>, fwd_large_kernel<false, false, true>,
+        fwd_large_kernel<false, true, false>,  fwd_large_kernel<false, true, true>,
+        fwd_large_kernel<true, false, false>,  fwd_large_kernel<true, false, true>,
+        fwd_large_kernel<true, true, false>,   fwd_large_kernel<true, true, true>};
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 g((unsigned)(tiles_m * tiles_n)), b(64 * NWAVE);
-    if (src.dq) {
-      if (y_is_bf16)
-        hipLaunchKernelGGL((fwd_large_kernel<true, true>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
-      else
-        hipLaunchKernelGGL((fwd_large_kernel<false, true>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
-    } else {
-      if (y_is_bf16)
-        hipLaunchKernelGGL((fwd_large_kernel<true, false>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
-      else
-        hipLaunchKernelGGL((fwd_large_kernel<false, false>), g, b, 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
-    }
+    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, X, M, N, K, packed, src, lr, y, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }

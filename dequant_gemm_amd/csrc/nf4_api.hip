@@ -152,10 +152,20 @@ static int check_gemm(const void *A, int64_t M, const nf4_qtensor *q, void *C, i
   return NF4_OK;
 }
 
+static int check_lowrank(int64_t M, const void *U, const void *V, int64_t r) {
+  if (r < NF4_LORA_RANK_STEP || r > NF4_LORA_MAX_RANK || r % NF4_LORA_RANK_STEP != 0) return NF4_ERR_UNSUPPORTED;
+  if (M == 0) return NF4_OK;
+  if (!U || !V) return NF4_ERR_NULL;
+  if (!aligned16(U) || !aligned16(V)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+static const nf4::LowRank kNoLowRank = {nullptr, nullptr, 0};
+
 int nf4_matmul_fwd(const void *X, int64_t M, const nf4_qtensor *q, void *Y, int y_dtype, void *stream) {
   int st = check_gemm(X, M, q, Y, y_dtype);
   if (st || M == 0) return st;
-  return hip_status(nf4::launch_fwd(X, M, q->rows, q->cols, q->packed, absmax_src(q), Y,
+  return hip_status(nf4::launch_fwd(X, M, q->rows, q->cols, q->packed, absmax_src(q), kNoLowRank, Y,
                                     y_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -163,7 +173,29 @@ int nf4_matmul_bwd_dx(const void *dY, int64_t M, const nf4_qtensor *q, void *dX,
                       void *stream) {
   int st = check_gemm(dY, M, q, dX, dx_dtype);
   if (st || M == 0) return st;
-  return hip_status(nf4::launch_bwd_dx(dY, M, q->rows, q->cols, q->packed, absmax_src(q), dX,
+  return hip_status(nf4::launch_bwd_dx(dY, M, q->rows, q->cols, q->packed, absmax_src(q), kNoLowRank, dX,
+                                       dx_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int nf4_matmul_fwd_lora(const void *X, int64_t M, const nf4_qtensor *q, const void *U, const void *B,
+                        int64_t r, void *Y, int y_dtype, void *stream) {
+  int st = check_gemm(X, M, q, Y, y_dtype);
+  if (st) return st;
+  st = check_lowrank(M, U, B, r);
+  if (st || M == 0) return st;
+  const nf4::LowRank lr = {reinterpret_cast<const uint16_t *>(U), reinterpret_cast<const uint16_t *>(B), (int)r};
+  return hip_status(nf4::launch_fwd(X, M, q->rows, q->cols, q->packed, absmax_src(q), lr, Y,
+                                    y_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int nf4_matmul_bwd_dx_lora(const void *dY, int64_t M, const nf4_qtensor *q, const void *V, const void *At,
+                           int64_t r, void *dX, int dx_dtype, void *stream) {
+  int st = check_gemm(dY, M, q, dX, dx_dtype);
+  if (st) return st;
+  st = check_lowrank(M, V, At, r);
+  if (st || M == 0) return st;
+  const nf4::LowRank lr = {reinterpret_cast<const uint16_t *>(V), reinterpret_cast<const uint16_t *>(At), (int)r};
+  return hip_status(nf4::launch_bwd_dx(dY, M, q->rows, q->cols, q->packed, absmax_src(q), lr, dX,
                                        dx_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -126,6 +126,46 @@ __device__ __forceinline__ float ahat_of(const AbsmaxRaw &r, int dq, float mu) {
   return dq ? __fadd_rn(__fmul_rn((float)r.q, r.v), mu) : r.v;
 }
 
+// ------------------------------------------------------------------ low-rank adapter term
+//
+// "bitsandbytes" page, 4-bit/LoRA paragraph: a frozen 4-bit base weight with
+// small trainable adapters.  The GEMMs can add a rank-r product U V^T to their
+// accumulators before the results are stored: U is bf16 [M, r] (the adapter's
+// activations on the reduction side), V is bf16 [output columns, r], both
+// row-major, r a multiple of 16.  The adapter rank index plays the role of the
+// reduction index in extra MFMA K-slices.
+struct LowRank {
+  const uint16_t *u;
+  const uint16_t *v;
+  int r;
+};
+
+// For the 32x32x16 kernels: adds U V^T to one wave's 8 stacked 32-row tiles of
+// the 32 output columns starting at column col0 (lane l: row l%32 of each
+// tile and column col0 + l%32; lane group kg = l/32 takes ranks 16s + 8kg ..
+// +7 of slice s from both operands).  Rows past M read row M-1 and the column
+// must already be clamped to an existing one: those outputs are never stored.
+__device__ __forceinline__ void add_lowrank_32x8(f32x16 acc[8], const LowRank &lr, int64_t m0, int64_t M,
+                                                 int64_t col, int bl, int kg) {
+  const uint16_t *vrow = lr.v + col * lr.r + 8 * kg;
+  const uint16_t *urow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = m0 + 32 * i + bl;
+    urow[i] = lr.u + (row < M ? row : M - 1) * lr.r + 8 * kg;
+  }
+  for (int s = 0; s < lr.r / 16; ++s) {
+    const uint4 bv = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
+    uint4 av[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) av[i] = *reinterpret_cast<const uint4 *>(urow[i] + 16 * s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                       __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+  }
+}
+
 // ------------------------------------------------------------------ register LUT dequant
 //
 // For one block, the 16 possible dequantized values bf16(level_i * a^) are

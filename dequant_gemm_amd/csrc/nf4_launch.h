@@ -30,10 +30,12 @@ hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t 
 hipError_t launch_dequantize(const uint8_t *packed, const AbsmaxSrc &src, int64_t numel,
                              void *out, int out_is_bf16, hipStream_t stream);
 
+// `lr.r == 0`: no adapter term.
 hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                      const AbsmaxSrc &src, void *y, int y_is_bf16, hipStream_t stream);
+                      const AbsmaxSrc &src, const LowRank &lr, void *y, int y_is_bf16, hipStream_t stream);
 
 hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                         const AbsmaxSrc &src, void *dx, int dx_is_bf16, hipStream_t stream);
+                         const AbsmaxSrc &src, const LowRank &lr, void *dx, int dx_is_bf16,
+                         hipStream_t stream);
 
 }  // namespace nf4

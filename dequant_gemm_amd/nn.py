@@ -24,7 +24,8 @@ from typing import Optional
 
 import torch
 
-from ._lib import QTensor, nf4_matmul_bwd_dx, nf4_matmul_fwd, nf4_quantize
+from ._lib import (LORA_MAX_RANK, LORA_RANK_STEP, QTensor, nf4_matmul_bwd_dx, nf4_matmul_bwd_dx_lora,
+                   nf4_matmul_fwd, nf4_matmul_fwd_lora, nf4_quantize)
 
 
 class _NF4Matmul(torch.autograd.Function):
@@ -111,6 +112,92 @@ class NF4Linear(torch.nn.Module):
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"double_quant={self.qweight.double_quant}, out_dtype={self.out_dtype}")
+
+
+class _NF4LoraMatmul(torch.autograd.Function):
+    """y = x W^T + s (x A^T) B^T with the adapter term added inside the fused GEMM.
+
+    The down projection U = bf16(s * x A^T) and, in the backward, V = bf16(s * dy B)
+    are small dense products computed by torch in fp32 and rounded once; the
+    fused kernels then add U B^T (forward) and V A (backward) in their fp32
+    accumulators.  The adapter's own gradients, dA = V^T x and dB = dy^T U
+    (with s folded into U and V), are small dense products left to torch.
+    """
+
+    @staticmethod
+    def forward(ctx, x, lora_a, lora_b, q: QTensor, scaling: float, out_dtype: torch.dtype):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, q.cols)
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        xa = x2.float() @ lora_a.float().t()                 # [M, r] in fp32
+        u = (xa * scaling).to(torch.bfloat16)
+        y = nf4_matmul_fwd_lora(x2, q, u, lora_b.contiguous(), out_dtype)
+        ctx.save_for_backward(x2, lora_a, lora_b, xa)
+        ctx.q, ctx.lead, ctx.scaling = q, lead, scaling
+        return y.reshape(*lead, q.rows)
+
+    @staticmethod
+    def backward(ctx, gy):
+        x2, lora_a, lora_b, xa = ctx.saved_tensors
+        q, s = ctx.q, ctx.scaling
+        g2 = gy.reshape(-1, q.rows)
+        g32 = g2.float()
+        gb = g2 if g2.dtype == torch.bfloat16 else g2.to(torch.bfloat16)
+        if not gb.is_contiguous():
+            gb = gb.contiguous()
+        v32 = (g32 @ lora_b.float()) * s                    # [M, r]
+        dx = nf4_matmul_bwd_dx_lora(gb, q, v32.to(torch.bfloat16), lora_a.t().contiguous(), torch.bfloat16)
+        d_a = (v32.t() @ x2.float()).to(lora_a.dtype)       # [r, K]
+        d_b = ((g32.t() @ xa) * s).to(lora_b.dtype)         # [N, r]
+        return dx.reshape(*ctx.lead, q.cols), d_a, d_b, None, None, None
+
+
+class NF4LoraLinear(torch.nn.Module):
+    """A frozen NF4 linear layer plus a trainable low-rank adapter (QLoRA's layer).
+
+    y = x W^T + (alpha / r) (x A^T) B^T with A [r, in_features] and B
+    [out_features, r] trainable bf16 parameters; B starts at zero, so the layer
+    starts equal to the frozen one.  The adapter term runs inside the fused
+    NF4 GEMM (forward and input gradient).  The rank must be a multiple of 16
+    (at most 1024).
+    """
+
+    def __init__(self, qweight: QTensor, r: int, alpha: float = None,
+                 out_dtype: torch.dtype = torch.bfloat16, seed: int = 0):
+        super().__init__()
+        if r < LORA_RANK_STEP or r > LORA_MAX_RANK or r % LORA_RANK_STEP:
+            raise ValueError(f"rank must be a multiple of {LORA_RANK_STEP} in [{LORA_RANK_STEP}, {LORA_MAX_RANK}]")
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+        self.qweight = qweight
+        self.r = r
+        self.scaling = float(alpha if alpha is not None else r) / r
+        self.out_dtype = out_dtype
+        dev = qweight.device
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        bound = 1.0 / (qweight.cols ** 0.5)                   # uniform init of A, as nn.Linear's weight
+        a = (torch.rand(r, qweight.cols, generator=g) * 2 - 1) * bound
+        self.lora_a = torch.nn.Parameter(a.to(torch.bfloat16).to(dev))
+        self.lora_b = torch.nn.Parameter(torch.zeros(qweight.rows, r, dtype=torch.bfloat16, device=dev))
+
+    @classmethod
+    def from_weight(cls, weight: torch.Tensor, r: int, alpha: float = None, double_quant: bool = True,
+                    out_dtype: torch.dtype = torch.bfloat16, seed: int = 0) -> "NF4LoraLinear":
+        w = weight.detach()
+        return cls(nf4_quantize(w if w.is_contiguous() else w.contiguous(), double_quant=double_quant),
+                   r, alpha, out_dtype, seed)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dtype != torch.bfloat16:
+            raise TypeError(f"x must be bfloat16 (got {x.dtype})")
+        if x.shape[-1] != self.qweight.cols:
+            raise ValueError(f"x has {x.shape[-1]} features, the weight expects {self.qweight.cols}")
+        return _NF4LoraMatmul.apply(x, self.lora_a, self.lora_b, self.qweight, self.scaling, self.out_dtype)
+
+    def extra_repr(self) -> str:
+        return (f"in_features={self.qweight.cols}, out_features={self.qweight.rows}, r={self.r}, "
+                f"scaling={self.scaling}, out_dtype={self.out_dtype}")
 
 
 def quantize_linears(module: torch.nn.Module, double_quant: bool = True,

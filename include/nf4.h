@@ -92,6 +92,9 @@ enum nf4_dtype {
 #define NF4_BLOCKSIZE 64
 /* Absmax values per double-quantization group. */
 #define NF4_DQ_GROUP 256
+/* Low-rank adapter ranks: a multiple of this step, at most the maximum. */
+#define NF4_LORA_RANK_STEP 16
+#define NF4_LORA_MAX_RANK 1024
 
 /*
  * A quantized weight: host struct, device buffers (the QuantState analogue).
@@ -193,6 +196,35 @@ int nf4_matmul_fwd(const void *X, int64_t M, const nf4_qtensor *q, void *Y,
  */
 int nf4_matmul_bwd_dx(const void *dY, int64_t M, const nf4_qtensor *q, void *dX,
                       int dx_dtype, void *stream);
+
+/*
+ * Y = X W^T + U B^T: the fused forward with a low-rank adapter term added in
+ * the same fp32 accumulators before the single store.  "bitsandbytes" page,
+ * 4-bit/LoRA paragraph (frozen 4-bit base weight plus small trainable
+ * adapters); "Zenbit" page, NF4DenseFused.  For an adapter with down
+ * projection A [r, K] and up projection B [N, r] (nn.Linear layouts), U is the
+ * down-projected activation X A^T.  U: device bf16 [M, r]; B: device bf16
+ * [N, r] with N = q->rows (any adapter scaling folded in); both row-major.
+ * X, Y, y_dtype and the shape rules as nf4_matmul_fwd.  r must be a multiple
+ * of NF4_LORA_RANK_STEP in [NF4_LORA_RANK_STEP, NF4_LORA_MAX_RANK]
+ * (NF4_ERR_UNSUPPORTED otherwise); U and B must be 16-byte aligned.  The
+ * adapter product runs on the same bf16 matrix cores with fp32 accumulation.
+ */
+int nf4_matmul_fwd_lora(const void *X, int64_t M, const nf4_qtensor *q,
+                        const void *U, const void *B, int64_t r, void *Y,
+                        int y_dtype, void *stream);
+
+/*
+ * dX = dY W^ + V A: the fused backward with respect to the input, with the
+ * adapter's contribution added in the same accumulators.  For the adapter of
+ * nf4_matmul_fwd_lora, V = dY B (device bf16 [M, r]) and At = A^T (device
+ * bf16 [K, r] with K = q->cols), both row-major.  dY, dX, dx_dtype and the
+ * shape rules as nf4_matmul_bwd_dx; r as nf4_matmul_fwd_lora.  The gradients
+ * of the adapter itself are small dense products left to the caller.
+ */
+int nf4_matmul_bwd_dx_lora(const void *dY, int64_t M, const nf4_qtensor *q,
+                           const void *V, const void *At, int64_t r, void *dX,
+                           int dx_dtype, void *stream);
 
 #ifdef __cplusplus
 }

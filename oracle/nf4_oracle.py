@@ -20,6 +20,8 @@ and no worked example):
   dequantize the weights.
 * [bnb-gemm] same page, the paragraph on quantized-weight GEMM kernels: weights
   dequantized on the fly, float32 multiply, float32 outputs.
+* [bnb-lora] same page, the paragraph on 4-bit training with low-rank
+  adapters: the 4-bit base weight stays frozen while small adapters train.
 
 Readings taken where the pages are silent (each is listed, with the reason, in
 the design notes of the repository):
@@ -41,6 +43,11 @@ the design notes of the repository):
   quantization, else a^ = a; W^ = bf16_rne(fl(c[code] * a^)).
 * R6 GEMMs: Y = X W^T and dX = dY W^ in float64 over bf16 operands; a result
   passes when |err| <= 1e-4 * (|X| |W^|^T) element by element.
+* R7 adapter term: with an adapter of down projection A [r, K] and up
+  projection B [N, r], the layer output is X W^T + (X A^T) B^T and its input
+  gradient dY W^ + (dY B) A.  The fused calls take the bf16 down-projected
+  activation U = X A^T (or V = dY B) as given and add U B^T (or V A) in the
+  same accumulation; the bound adds the adapter product's magnitude term.
 
 Arrays: a weight is a float32 numpy array (bf16 inputs are passed upcast to
 float32, which is exact); bf16 outputs are returned as uint16 bit patterns.
@@ -62,6 +69,7 @@ __all__ = [
     "double_quant", "dq_absmax", "dequantize_codes",
     "quantize", "dequantize", "nblocks_of", "ngroups_of",
     "matmul_fwd", "matmul_bwd_dx", "fwd_bound", "bwd_dx_bound", "gemm_violations", "ppf_stdlib",
+    "matmul_fwd_lora", "matmul_bwd_dx_lora", "fwd_lora_bound", "bwd_dx_lora_bound",
 ]
 
 DELTA = 0.9677083          # R1: QLoRA's offset, the 7-digit literal
@@ -356,6 +364,25 @@ def fwd_bound(x: np.ndarray, w_hat: np.ndarray) -> np.ndarray:
 
 def bwd_dx_bound(dy: np.ndarray, w_hat: np.ndarray) -> np.ndarray:
     return GEMM_RTOL * (np.abs(np.asarray(dy, np.float64)) @ np.abs(np.asarray(w_hat, np.float64)))
+
+
+def matmul_fwd_lora(x: np.ndarray, w_hat: np.ndarray, u: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Y = X W^T + U B^T in float64; U [M,r], B [N,r] ([bnb-lora], R7)."""
+    return matmul_fwd(x, w_hat) + np.asarray(u, np.float64) @ np.asarray(b, np.float64).T
+
+
+def matmul_bwd_dx_lora(dy: np.ndarray, w_hat: np.ndarray, v: np.ndarray, a_t: np.ndarray) -> np.ndarray:
+    """dX = dY W^ + V A in float64; V [M,r], A^T given as a_t [K,r] ([bnb-lora], R7)."""
+    return matmul_bwd_dx(dy, w_hat) + np.asarray(v, np.float64) @ np.asarray(a_t, np.float64).T
+
+
+def fwd_lora_bound(x, w_hat, u, b) -> np.ndarray:
+    return fwd_bound(x, w_hat) + GEMM_RTOL * (np.abs(np.asarray(u, np.float64)) @ np.abs(np.asarray(b, np.float64)).T)
+
+
+def bwd_dx_lora_bound(dy, w_hat, v, a_t) -> np.ndarray:
+    return bwd_dx_bound(dy, w_hat) + GEMM_RTOL * (np.abs(np.asarray(v, np.float64)) @
+                                                  np.abs(np.asarray(a_t, np.float64)).T)
 
 
 def gemm_violations(out: np.ndarray, ref: np.ndarray, bound: np.ndarray) -> int:

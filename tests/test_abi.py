@@ -156,3 +156,25 @@ def test_status_strings(L):
     for s in range(9):
         assert L.nf4_status_string(s)
     assert L.nf4_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("fn", ["nf4_matmul_fwd_lora", "nf4_matmul_bwd_dx_lora"])
+def test_lowrank_gemm_errors(L, fn):
+    f = getattr(L, fn)
+    q = _qt(rows=128, cols=256)
+    ok = lambda **k: f(k.get("A", P), k.get("M", 4), ctypes.byref(k.get("q", q)), k.get("U", P), k.get("V", P),
+                       k.get("r", 16), k.get("C", P), k.get("dt", 0), None)
+    assert ok(A=None) == 1
+    assert ok(C=None) == 1
+    assert ok(U=None) == 1
+    assert ok(V=None) == 1
+    assert ok(U=P + 8) == 5
+    assert ok(V=P + 2) == 5
+    for r in (0, 8, 24, 1040, -16):
+        assert ok(r=r) == 7                                 # rank: multiple of 16 in [16, 1024]
+    assert ok(q=_qt(rows=128, cols=96)) == 7               # K % 64 != 0, as without the adapter
+    assert ok(dt=3) == 4
+    assert f(P, 4, None, P, P, 16, P, 0, None) == 1
+    # M == 0: a successful no-op once the rank is valid
+    assert f(None, 0, ctypes.byref(q), None, None, 32, None, 0, None) == 0
+    assert f(None, 0, ctypes.byref(q), None, None, 17, None, 0, None) == 7

@@ -115,3 +115,44 @@ def test_device_save_load_round_trip(tmp_path):
     y1 = dg.nf4_matmul_fwd(X, back["a"])
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+def test_nf4loralinear_forward_and_gradients():
+    """The adapter layer against a float64 host evaluation of the same formula.
+
+    y = x W^T + s (x A^T) B^T; dx = dy W^ + s (dy B) A; dA = s (dy B)^T x;
+    dB = s dy^T (x A^T).  The kernels' parts are held to the 1e-4 bound; the
+    layer's one bf16 rounding of y / dx and of the adapter activations U, V
+    (each at most 2^-8 relative) is allowed on top.
+    """
+    lib()
+    from dequant_gemm_amd.nn import NF4LoraLinear
+    d = dev()
+    N, K, M, r, alpha = 192, 256, 48, 16, 32.0
+    W = synth.normal((N, K), 0.02, 90, torch.bfloat16)
+    layer = NF4LoraLinear.from_weight(W.to(d), r, alpha)
+    with torch.no_grad():
+        layer.lora_b.copy_(synth.normal((N, r), 0.05, 91).to(d))
+    X = synth.normal((M, K), 1.0, 92)
+    x = X.to(d).reshape(6, 8, K).requires_grad_(True)
+    y = layer(x)
+    dY = synth.normal((M, N), 1.0, 93)
+    y.backward(dY.to(d).reshape(6, 8, N))
+    torch.cuda.synchronize()
+    s = alpha / r
+    wh = O.bf16_bits_to_f32(O.dequantize(oracle_quantize(W, True))).reshape(N, K).astype(np.float64)
+    a = layer.lora_a.detach().float().cpu().numpy().astype(np.float64)
+    b = layer.lora_b.detach().float().cpu().numpy().astype(np.float64)
+    x64, dy64 = X.float().numpy().astype(np.float64), dY.float().numpy().astype(np.float64)
+    xa, dyb = x64 @ a.T, dy64 @ b
+    y_ref = x64 @ wh.T + s * xa @ b.T
+    y_tol = 1e-4 * (np.abs(x64) @ np.abs(wh).T) + 2.0 ** -8 * (np.abs(y_ref) + s * np.abs(xa) @ np.abs(b).T)
+    assert_gemm_within_bound(y.detach().reshape(M, N), y_ref, y_tol, "lora layer y")
+    dx_ref = dy64 @ wh + s * dyb @ a
+    dx_tol = 1e-4 * (np.abs(dy64) @ np.abs(wh)) + 2.0 ** -8 * (np.abs(dx_ref) + s * np.abs(dyb) @ np.abs(a))
+    assert_gemm_within_bound(x.grad.reshape(M, K), dx_ref, dx_tol, "lora layer dx")
+    da_ref, db_ref = s * dyb.T @ x64, s * dy64.T @ xa
+    da_tol = 2.0 ** -7 * s * (np.abs(dyb).T @ np.abs(x64))
+    db_tol = 2.0 ** -7 * s * (np.abs(dy64).T @ np.abs(xa))
+    assert_gemm_within_bound(layer.lora_a.grad, da_ref, da_tol, "lora dA")
+    assert_gemm_within_bound(layer.lora_b.grad, db_ref, db_tol, "lora dB")

@@ -102,3 +102,57 @@ def test_tiny_workload_end_to_end(dq):
     assert y.shape == (8, 256) and dx.shape == (8, 256)
     assert O.gemm_violations(y.astype(np.float32), y, O.fwd_bound(x, wh)) == 0
     assert O.gemm_violations(dx.astype(np.float32), dx, O.bwd_dx_bound(dy, wh)) == 0
+
+
+# ------------------------------------------------------------------ adapter term (R7)
+# "bitsandbytes" page, 4-bit/LoRA paragraph: frozen 4-bit base weight plus a
+# trainable low-rank adapter; the layer adds (X A^T) B^T to X W^T and its input
+# gradient adds (dY B) A to dY W^.
+
+def test_lora_terms_against_exact_rationals():
+    rng = np.random.default_rng(10)
+    M, N, K, r = 3, 4, 64, 16
+    x, w, u, b = _bf16(rng, (M, K)), _bf16(rng, (N, K), 0.02), _bf16(rng, (M, r)), _bf16(rng, (N, r), 0.1)
+    dy, v, at = _bf16(rng, (M, N)), _bf16(rng, (M, r)), _bf16(rng, (K, r), 0.1)
+    y = O.matmul_fwd_lora(x, w, u, b)
+    dx = O.matmul_bwd_dx_lora(dy, w, v, at)
+    F = lambda t: Fraction(float(t))
+    for i in range(M):
+        for j in range(N):
+            terms = [F(x[i, k]) * F(w[j, k]) for k in range(K)] + [F(u[i, t]) * F(b[j, t]) for t in range(r)]
+            assert abs(F(y[i, j]) - sum(terms)) <= Fraction(K + r) * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+        for k in range(K):
+            terms = [F(dy[i, j]) * F(w[j, k]) for j in range(N)] + [F(v[i, t]) * F(at[k, t]) for t in range(r)]
+            assert abs(F(dx[i, k]) - sum(terms)) <= Fraction(N + r) * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+
+
+def test_lora_special_cases():
+    rng = np.random.default_rng(11)
+    r, N, K = 32, 48, 128
+    w, b, at = _bf16(rng, (N, K), 0.02), _bf16(rng, (N, r), 0.1), _bf16(rng, (K, r), 0.1)
+    x = _bf16(rng, (r, K))
+    # zero adapter activations: the plain products
+    assert np.array_equal(O.matmul_fwd_lora(x, w, np.zeros((r, r)), b), O.matmul_fwd(x, w))
+    # zero input, identity adapter activations: the adapter weights themselves
+    eye = np.eye(r, dtype=np.float32)
+    assert np.array_equal(O.matmul_fwd_lora(np.zeros((r, K)), w, eye, b), b.T.astype(np.float64))
+    assert np.array_equal(O.matmul_bwd_dx_lora(np.zeros((r, N)), w, eye, at), at.T.astype(np.float64))
+
+
+def test_lora_bound_rejects_mistakes():
+    rng = np.random.default_rng(12)
+    M, N, K, r = 8, 64, 512, 64
+    x, w = _bf16(rng, (M, K)), _bf16(rng, (N, K), 0.02)
+    u, b = _bf16(rng, (M, r)), _bf16(rng, (N, r), 0.1)
+    ref = O.matmul_fwd_lora(x, w, u, b)
+    bound = O.fwd_lora_bound(x, w, u, b)
+    # fp32 accumulation in any order passes
+    y32 = (x.astype(np.float32) @ w.T.astype(np.float32)) + (u.astype(np.float32) @ b.T.astype(np.float32))
+    assert O.gemm_violations(y32, ref, bound) == 0
+    # a dropped adapter term, a dropped base term, a sign error and a transposed operand do not
+    assert O.gemm_violations(O.matmul_fwd(x, w), ref, bound) > 0
+    assert O.gemm_violations(u.astype(np.float64) @ b.T, ref, bound) > 0
+    assert O.gemm_violations(O.matmul_fwd(x, w) - u.astype(np.float64) @ b.T, ref, bound) > 0
+    sq = _bf16(rng, (r, r), 0.1)
+    assert O.gemm_violations(O.matmul_fwd(x, w)[:, :r] + u @ sq.astype(np.float64),
+                             O.matmul_fwd_lora(x, w[:r], u, sq), O.fwd_lora_bound(x, w[:r], u, sq)) > 0
