@@ -223,18 +223,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int64_t row = m0 + 128 * wm + 32 * i + bl;
       urow[i] = lr.u + (row < M ? row : M - 1) * lr.r + 8 * kg;
     }
-    for (int s = 0; s < lr.r / 16; ++s) {
-      uint4 bv[4], av[4];
+    // two slices in flight: slice s + 1 loads while slice s multiplies
+    auto load = [&](int s, uint4 (&bv)[4], uint4 (&av)[4]) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) bv[t] = *reinterpret_cast<const uint4 *>(vrow[t] + 16 * s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const uint4 *>(urow[i] + 16 * s);
+    };
+    auto mma = [&](const uint4 (&bv)[4], const uint4 (&av)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[i]), as_bf16x8(bv[t]), acc[i][t], 0, 0, 0);
+    };
+    const int ns = lr.r / 16;
+    uint4 b0[4], b1[4], a0[4], a1[4];
+    load(0, b0, a0);
+    int s = 0;
+    for (; s + 2 <= ns; s += 2) {
+      load(s + 1, b1, a1);
+      mma(b0, a0);
+      if (s + 2 < ns) load(s + 2, b0, a0);
+      mma(b1, a1);
     }
+    if (s < ns) mma(b0, a0);
   }
 
 #pragma unroll

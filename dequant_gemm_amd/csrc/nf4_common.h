@@ -154,16 +154,29 @@ __device__ __forceinline__ void add_lowrank_32x8(f32x16 acc[8], const LowRank &l
     const int64_t row = m0 + 32 * i + bl;
     urow[i] = lr.u + (row < M ? row : M - 1) * lr.r + 8 * kg;
   }
-  for (int s = 0; s < lr.r / 16; ++s) {
-    const uint4 bv = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
-    uint4 av[8];
+  // two slices in flight: slice s + 1 loads while slice s multiplies
+  auto load = [&](int s, uint4 &bv, uint4 (&av)[8]) {
+    bv = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
 #pragma unroll
     for (int i = 0; i < 8; ++i) av[i] = *reinterpret_cast<const uint4 *>(urow[i] + 16 * s);
+  };
+  auto mma = [&](const uint4 &bv, const uint4 (&av)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
                                                        __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+  };
+  const int ns = lr.r / 16;
+  uint4 b0, b1, a0[8], a1[8];
+  load(0, b0, a0);
+  int s = 0;
+  for (; s + 2 <= ns; s += 2) {
+    load(s + 1, b1, a1);
+    mma(b0, a0);
+    if (s + 2 < ns) load(s + 2, b0, a0);
+    mma(b1, a1);
   }
+  if (s < ns) mma(b0, a0);
 }
 
 // ------------------------------------------------------------------ register LUT dequant
