@@ -590,7 +590,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   if (s < ns) step(s, as0, as1, as2, cs1, cs0);
   if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
   __builtin_amdgcn_s_waitcnt(0);
-  if (LR) add_lowrank_32x8(acc, lr, m0, M, kc + bl, bl, kg);
+  if (LR) add_lowrank_32x8(acc, lr, m0, M, kc + bl, bl, kg, as0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   const int64_t col = kcol + bl;

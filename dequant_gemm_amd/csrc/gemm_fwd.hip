@@ -438,7 +438,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   if (kt < nk) step(kt, xs0, xs1, xs2, cs1, cs2, bb0, bb1, bb2);
   if (kt + 1 < nk) step(kt + 1, xs1, xs2, xs0, cs2, cs0, bb1, bb2, bb0);
   __builtin_amdgcn_s_waitcnt(0);
-  if (LR) add_lowrank_32x8(acc, lr, m0, M, nc, bl, kg);
+  if (LR) add_lowrank_32x8(acc, lr, m0, M, nc, bl, kg, xs0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   if (ncol < N) {

@@ -140,43 +140,58 @@ struct LowRank {
   int r;
 };
 
-// For the 32x32x16 kernels: adds U V^T to one wave's 8 stacked 32-row tiles of
-// the 32 output columns starting at column col0 (lane l: row l%32 of each
-// tile and column col0 + l%32; lane group kg = l/32 takes ranks 16s + 8kg ..
-// +7 of slice s from both operands).  Rows past M read row M-1 and the column
-// must already be clamped to an existing one: those outputs are never stored.
+// For the 32x32x16 kernels with eight waves (512 threads), each owning 32 output columns of
+// the workgroup's 256 rows: adds U V^T to a wave's 8 stacked 32-row tiles of
+// the columns starting at col0 (lane l: row l%32 of each tile and column
+// col0 + l%32; lane group kg = l/32 takes ranks 16s + 8kg .. +7 of slice s
+// from both operands).  Every wave needs the same 256 rows of U, so the
+// workgroup stages them in LDS (`buf`, 32 KiB that no wave still reads), a
+// chunk of kLrChunk ranks at a time; each wave reads its 32 rows of V from
+// memory.  Rows past M read row M-1 and the column must already be clamped to
+// an existing one: those outputs are never stored.  All waves of the
+// workgroup must call this together (it synchronises them).
+constexpr int kLrChunk = 48;                      // ranks per LDS chunk
+constexpr int kLrRow = 2 * kLrChunk + 16;         // bytes per staged row (16 of padding against bank conflicts)
+
 __device__ __forceinline__ void add_lowrank_32x8(f32x16 acc[8], const LowRank &lr, int64_t m0, int64_t M,
-                                                 int64_t col, int bl, int kg) {
+                                                 int64_t col, int bl, int kg, uint8_t *buf) {
+  static_assert(256 * kLrRow <= 32768, "staged U chunk exceeds the LDS buffer");
   const uint16_t *vrow = lr.v + col * lr.r + 8 * kg;
-  const uint16_t *urow[8];
+  for (int r0 = 0; r0 < lr.r; r0 += kLrChunk) {
+    const int rc = lr.r - r0 < kLrChunk ? lr.r - r0 : kLrChunk;   // a multiple of 16
+    const int cpr = rc / 8;                                        // 16-byte chunks per row
+    __syncthreads();                                               // the buffer is free
+    {
+      // 256 * cpr <= 1536 chunks over the 512 threads: all loads, then all stores
+      constexpr int kPer = 256 * (kLrChunk / 8) / 512;
+      uint4 v[kPer];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = m0 + 32 * i + bl;
-    urow[i] = lr.u + (row < M ? row : M - 1) * lr.r + 8 * kg;
+      for (int k = 0; k < kPer; ++k) {
+        const int c = threadIdx.x + 512 * k;
+        const int row = c / cpr, ch = c - row * cpr;
+        const int64_t grow = m0 + row < M ? m0 + row : M - 1;
+        if (c < 256 * cpr) v[k] = *reinterpret_cast<const uint4 *>(lr.u + grow * lr.r + r0 + 8 * ch);
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int c = threadIdx.x + 512 * k;
+        const int row = c / cpr, ch = c - row * cpr;
+        if (c < 256 * cpr) *reinterpret_cast<uint4 *>(buf + row * kLrRow + 16 * ch) = v[k];
+      }
+    }
+    __syncthreads();
+    for (int s = 0; s < rc / 16; ++s) {
+      const uint4 bv = *reinterpret_cast<const uint4 *>(vrow + r0 + 16 * s);
+      uint4 av[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        av[i] = *reinterpret_cast<const uint4 *>(buf + (32 * i + bl) * kLrRow + 16 * (2 * s + kg));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                         __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+    }
   }
-  // two slices in flight: slice s + 1 loads while slice s multiplies
-  auto load = [&](int s, uint4 &bv, uint4 (&av)[8]) {
-    bv = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) av[i] = *reinterpret_cast<const uint4 *>(urow[i] + 16 * s);
-  };
-  auto mma = [&](const uint4 &bv, const uint4 (&av)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
-                                                       __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
-  };
-  const int ns = lr.r / 16;
-  uint4 b0, b1, a0[8], a1[8];
-  load(0, b0, a0);
-  int s = 0;
-  for (; s + 2 <= ns; s += 2) {
-    load(s + 1, b1, a1);
-    mma(b0, a0);
-    if (s + 2 < ns) load(s + 2, b0, a0);
-    mma(b1, a1);
-  }
-  if (s < ns) mma(b0, a0);
 }
 
 // ------------------------------------------------------------------ register LUT dequant
