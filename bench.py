@@ -1,6 +1,7 @@
 """Benchmark of the NF4 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-decode] [--no-large] [--no-bulk] [--op OP]
 
 One step is one training-layer pass of the prefill workload (X [4096,4096]
 bf16, weight [11008,4096] bf16 N(0,0.02), dY [4096,11008] bf16 N(0,0.01)):
@@ -11,10 +12,12 @@ libnf4.so on torch's current stream, inputs and outputs resident in HBM.
 ``value`` is the step's GEMM throughput, 2 * 2*M*N*K flops per step over the
 step time (quantization included in the time).  The same JSON line carries
 per-kernel timings (HIP events around every launch of the timed steps), the
-dequantizer and the decode-shape forward (M = 1, 4, 16 on a rotating pool of
-64 quantized 4096x4096 weights, replayed from a HIP graph so launch overhead
-does not count), a roofline entry for the dominant kernel and the CPU oracle's
-throughput on a bounded sample of the same workload.
+dequantizer, the rank-64 adapter variants of both GEMMs, the decode-shape
+forward (M = 1, 4, 16 on a rotating pool of 64 quantized 4096x4096 weights,
+replayed from a HIP graph so host launch overhead does not count), the
+outlier-heavy large shape (M = K = 8192, N = 28672, fp32 Student-t weight), the
+32-layer bulk quantize/dequantize round trip, a roofline entry for the dominant
+kernel and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -248,6 +251,92 @@ def bench_decode(dg, pool=64, reps=20):
     return out
 
 
+def _device_normal(shape, std, seed, d, dtype=torch.bfloat16):
+    g = torch.Generator(device=d)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=d, dtype=torch.float32) * std).to(dtype)
+
+
+def bench_large(dg, reps=5):
+    """The outlier-heavy large shape: M=8192, K=8192, N=28672, W = 0.02 * Student-t(4) fp32.
+
+    Inputs are drawn on the device (seeded torch generators, the workload's shapes and
+    distributions); the parity tests draw the same workload on the host.
+    """
+    import synth
+    d = torch.device("cuda:0")
+    M, K, N = synth.LARGE_M, synth.LARGE_K, synth.LARGE_N
+    torch.manual_seed(4000)
+    W = (torch.distributions.StudentT(torch.tensor(4.0, device=d)).sample((N, K)) * 0.02).float().contiguous()
+    X = _device_normal((M, K), 1.0, 4001, d)
+    dY = _device_normal((M, N), 0.01, 4002, d)
+    q = dg.empty_qtensor(N, K, True, d)
+    ws = torch.empty(dg.nf4_sizes(N, K)["workspace_bytes"], dtype=torch.uint8, device=d)
+    Y = torch.empty((M, N), dtype=torch.float32, device=d)
+    dX = torch.empty((M, K), dtype=torch.float32, device=d)
+    quant = lambda: dg.nf4_quantize(W, out=q, workspace=ws)
+    quant()
+    torch.cuda.synchronize()
+    ms_q = time_events(quant, reps)
+    fwd = lambda: dg.nf4_matmul_fwd(X, q, out=Y)
+    bwd = lambda: dg.nf4_matmul_bwd_dx(dY, q, out=dX)
+    fwd(), bwd()
+    torch.cuda.synchronize()
+    ms_f = time_events(fwd, reps)
+    ms_b = time_events(bwd, reps)
+    flop = 2.0 * M * N * K
+    bq = N * K * 4 + wq_bytes(N, K)
+    out = {"large_quantize_f32": {"ms": ms_q, "GB/s": bq / (ms_q * 1e-3) / 1e9,
+                                  "frac_hbm": bq / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+    for name, ms in (("large_fwd", ms_f), ("large_bwd_dx", ms_b)):
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"ms": ms, "TFLOP/s": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
+    del W, X, dY, q, ws, Y, dX
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_bulk(dg, reps=3):
+    """Bulk quantize + dequantize round trip of a 32-layer decoder's linear weights.
+
+    Per layer q, k, v, o [4096, 4096], gate, up [11008, 4096], down [4096, 11008], bf16
+    N(0, 0.02) drawn on the device (seeded per matrix); all 224 matrices are quantized, then
+    all are dequantized, each pass replayed from a HIP graph.
+    """
+    import synth
+    d = torch.device("cuda:0")
+    Ws, qs = [], []
+    for layer in range(synth.BULK_LAYERS):
+        for j in range(len(synth.BULK_NAMES)):
+            shape = synth.bulk_shape(j)
+            Ws.append(_device_normal(shape, 0.02, 3000 + 7 * layer + j, d))
+            qs.append(dg.empty_qtensor(shape[0], shape[1], True, d))
+    numel = sum(w.numel() for w in Ws)
+    ws = torch.empty(max(dg.nf4_sizes(*w.shape)["workspace_bytes"] for w in Ws), dtype=torch.uint8, device=d)
+    outs = {}
+    for w in Ws:
+        outs.setdefault(tuple(w.shape), torch.empty(w.shape, dtype=torch.bfloat16, device=d))
+    quant_all = lambda: [dg.nf4_quantize(w, out=q, workspace=ws) for w, q in zip(Ws, qs)]
+    deq_all = lambda: [dg.nf4_dequantize(q, out=outs[(q.rows, q.cols)]) for q in qs]
+    res = {}
+    for name, fn in (("bulk_quantize", quant_all), ("bulk_dequantize", deq_all)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_events(g.replay, reps)
+        b = sum(2 * w.numel() + wq_bytes(*w.shape) for w in Ws)
+        res[name] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "frac_hbm": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "matrices": len(Ws), "elements": numel}
+        del g
+    del Ws, qs, ws, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s=12.0):
     """The oracle, as it stands, on a bounded sample of the prefill workload."""
     import oracle as O
@@ -365,6 +454,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-large", action="store_true", help="skip the 8192x8192x28672 outlier-heavy shape")
+    ap.add_argument("--no-bulk", action="store_true", help="skip the 32-layer quantize/dequantize round trip")
     ap.add_argument("--op", default=None, choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     a = ap.parse_args()
@@ -386,6 +477,10 @@ def main():
     ops = pre["ops"]
     if not a.no_decode:
         ops.update(bench_decode(dg))
+    if not a.no_large:
+        ops.update(bench_large(dg))
+    if not a.no_bulk:
+        ops.update(bench_bulk(dg))
     dom = "fwd" if ops["fwd"]["ms"] >= ops["bwd_dx"]["ms"] else "bwd_dx"
     ach = ops[dom]["TFLOP/s"]
     line = {

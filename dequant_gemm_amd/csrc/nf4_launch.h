@@ -10,15 +10,16 @@
 
 namespace nf4 {
 
-// Workspace layout for quantization with double quantization: one row of 256
-// exact-mean accumulators per quantize workgroup (at most kQuantGridMax) plus
-// one for the partial tail block, the 256 column sums, an arrival counter
-// (padded to 256 bytes), then the fp32 absmax of every block.
-constexpr int kQuantGridMax = 1024;
-constexpr size_t kPartialBytes = (size_t)(kQuantGridMax + 2) * 256 * sizeof(unsigned long long) + 256;
-inline size_t absmax_ws_offset() { return kPartialBytes; }
+// Workspace layout for quantization with double quantization: one row of
+// kMeanSlots exact-mean accumulators per quantize workgroup (at most
+// kQuantGridMax) plus one for the partial tail block, then the fp32 absmax of
+// every block.
+constexpr int kQuantGridMax = 2048;
+constexpr int kMeanSlots = 16;
+constexpr size_t kPartialBytes = (size_t)(kQuantGridMax + 1) * kMeanSlots * sizeof(unsigned long long);
+inline size_t absmax_ws_offset() { return (kPartialBytes + 255) & ~(size_t)255; }
 inline size_t quant_workspace_bytes(int64_t nblocks) {
-  size_t b = kPartialBytes + (size_t)nblocks * sizeof(float);
+  size_t b = absmax_ws_offset() + (size_t)nblocks * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
 

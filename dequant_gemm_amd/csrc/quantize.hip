@@ -8,14 +8,22 @@
 //
 // Kernels, in launch order:
 //   quantize_blocks_kernel   full 64-blocks: absmax, codes, packing; with double
-//                            quantization also one row of 256 exact-mean
+//                            quantization also one row of exact-mean
 //                            accumulators per workgroup (plain stores)
 //   quantize_tail_kernel     the one partial block at the end, if any (its own
 //                            accumulator row)
-//   mean_reduce_kernel       sums the rows (each workgroup a share of whole
-//                            rows); the last workgroup adds the shares and
-//                            forms the exact mean, one rounding
+//   mean_reduce_kernel       one workgroup: sums the rows and forms the exact
+//                            mean, one rounding
 //   double_quant_kernel      int8 absmax and one fp32 scale per 256 blocks
+//
+// Exact mean.  Every finite fp32 is an integer number of 2^-149 units: a value
+// with biased exponent e and 24-bit significand m is m * 2^(max(e,1)-1) units.
+// A workgroup first sums significands per exponent (LDS, 64-bit), then folds
+// the 256 exponent sums into the digits of one fixed-point integer: slot i
+// accumulates (64-bit, carries left unresolved) the 32-bit digit of weight
+// 2^(32 i) units of every term.  The ten used slots of all rows are summed in
+// 64 bits (no overflow below 2^37 elements) and the carries resolved once at
+// the end: integer sums, so the result does not depend on any order.
 #include "nf4_launch.h"
 
 namespace nf4 {
@@ -105,18 +113,23 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
 // of its block absmax values per binary exponent (exact integer sums) and
 // stores the 256 sums as its row of `partials`.  The next block's load is in
 // flight while the current block is encoded.
+// Adds the exponent-e sum `v` of significands to the digit slots (see above).
+__device__ __forceinline__ void add_to_slots(unsigned long long *slot, int e, unsigned long long v) {
+  const int sh = (e > 0 ? e : 1) - 1;
+  const int wi = sh >> 5, bi = sh & 31;
+  const unsigned long long lo = v << bi;
+  atomicAdd(&slot[wi], (unsigned long long)(uint32_t)lo);
+  atomicAdd(&slot[wi + 1], (unsigned long long)(uint32_t)(lo >> 32));
+  if (bi) atomicAdd(&slot[wi + 2], (unsigned long long)(uint32_t)(v >> (64 - bi)));
+}
+
 template <bool BF16, bool DQ>
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     const void *__restrict__ w, int64_t nfull, uint8_t *__restrict__ packed,
-    float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status,
-    unsigned int *arrivals) {
+    float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status) {
   __shared__ Cell cells[129];
   __shared__ unsigned long long lbuck[256];
-  if (DQ && blockIdx.x == 0 && threadIdx.x == 0) *arrivals = 0u;  // for mean_reduce_kernel
-  build_cells(cells);
-  if (DQ) lbuck[threadIdx.x] = 0ull;
-  __syncthreads();
-
+  __shared__ unsigned long long lslot[kMeanSlots];
   const int part = threadIdx.x & 7;
   const int slot = threadIdx.x >> 3;
   const int64_t stride = (int64_t)gridDim.x * 32;
@@ -132,7 +145,14 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
   bool bad = false;
   int64_t blk = (int64_t)blockIdx.x * 32 + slot;
   uint4 cu = make_uint4(0, 0, 0, 0), cv = cu;
-  if (blk < nfull) load(blk, cu, cv);
+  if (blk < nfull) load(blk, cu, cv);   // in flight while the level table is built
+  build_cells(cells);
+  if (DQ) {
+    lbuck[threadIdx.x] = 0ull;
+    if (threadIdx.x < kMeanSlots) lslot[threadIdx.x] = 0ull;
+  }
+  __syncthreads();
+
   for (; blk < nfull; blk += stride) {
     uint4 nu = make_uint4(0, 0, 0, 0), nv = nu;
     const int64_t nb = blk + stride < nfull ? blk + stride : nfull - 1;
@@ -181,7 +201,10 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
   }
   if (DQ) {
     __syncthreads();
-    partials[(int64_t)blockIdx.x * 256 + threadIdx.x] = lbuck[threadIdx.x];
+    const unsigned long long v = lbuck[threadIdx.x];
+    if (v) add_to_slots(lslot, threadIdx.x, v);
+    __syncthreads();
+    if (threadIdx.x < kMeanSlots) partials[(int64_t)blockIdx.x * kMeanSlots + threadIdx.x] = lslot[threadIdx.x];
   }
   if (bad && status) atomicOr(status, 1u);
 }
@@ -191,11 +214,8 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 template <bool BF16, bool DQ>
 __global__ __launch_bounds__(64) void quantize_tail_kernel(
     const void *__restrict__ w, int64_t numel, int64_t blk, uint8_t *__restrict__ packed,
-    float *__restrict__ absmax, unsigned long long *__restrict__ partial_row, uint32_t *status,
-    unsigned int *clear_arrivals) {
+    float *__restrict__ absmax, unsigned long long *__restrict__ partial_row, uint32_t *status) {
   __shared__ Cell cells[129];
-  // with no full block there is no quantize_blocks_kernel launch to clear it
-  if (DQ && clear_arrivals && threadIdx.x == 0) *clear_arrivals = 0u;
   build_cells(cells);
   __syncthreads();
   const int lane = threadIdx.x;
@@ -219,12 +239,18 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
   if (!valid) code = 0;
   const int upper = __shfl_down(code, 1);
   if (valid && (lane & 1) == 0) packed[blk * (kBlock / 2) + lane / 2] = (uint8_t)(code | (upper << 4));
-  if (DQ) {
-    // this block's accumulator row: zero everywhere but its exponent
+  if (DQ && lane < kMeanSlots) {
+    // this block's accumulator row: the digits of its absmax alone
     const uint32_t ex = m >> 23;
     const unsigned long long sig = (m & 0x7fffffu) | (ex ? 0x800000u : 0u);
-    for (int i = lane; i < 256; i += 64)
-      partial_row[i] = (m < 0x7f800000u && (uint32_t)i == ex) ? sig : 0ull;
+    const int sh = (ex > 0 ? (int)ex : 1) - 1;
+    const unsigned long long lo = sig << (sh & 31);     // below 2^55
+    unsigned long long d = 0;
+    if (m < 0x7f800000u) {
+      if (lane == (sh >> 5)) d = (uint32_t)lo;
+      if (lane == (sh >> 5) + 1) d = lo >> 32;
+    }
+    partial_row[lane] = d;
   }
   if (lane == 0) {
     absmax[blk] = __uint_as_float(m);
@@ -232,56 +258,25 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
   }
 }
 
-// Exact mean of all block absmax values, rounded once to fp32 (nearest-even).
-// Every finite fp32 is an integer number of 2^-149 units; column e of the
-// accumulator rows holds sums of the 24-bit significands of the values with
-// biased exponent e, worth 2^(max(e,1)-1) units each.  The workgroups of
-// mean_reduce_kernel each sum a share of the rows (coalesced row reads) into
-// one row of totals; the last workgroup to finish (an arrival counter that
-// the quantize kernel cleared) adds those rows in a fixed order -- integer
-// sums, so the result does not depend on any order -- forms the total S
-// (at most ~310 bits) as a multi-word integer, divides it by the block count
-// with 32 extra quotient bits -- enough to reach below the smallest subnormal
-// -- and rounds on the remainder.
-// `sums` holds the 256 column totals, `nz` a bitmask of the non-zero ones.
-__device__ float mean_from_sums(const unsigned long long *sums, const unsigned long long nz[4],
-                                uint32_t nblocks) {
-  constexpr int W = 13;
-  // S * 2^32 as 32-bit digits held in 64-bit slots (carries resolved at the end)
-  unsigned long long slot[W];
-#pragma unroll
-  for (int i = 0; i < W; ++i) slot[i] = 0;
-  for (int w = 0; w < 4; ++w) {
-    unsigned long long m = nz[w];
-    while (m) {
-      const int e = 64 * w + __builtin_ctzll(m);
-      m &= m - 1;
-      const unsigned long long v = sums[e];
-      const int sh = (e > 0 ? e : 1) - 1 + 32;
-      const int wi = sh >> 5, bi = sh & 31;
-      const unsigned long long lo = v << bi;
-      slot[wi] += (uint32_t)lo;
-      slot[wi + 1] += (uint32_t)(lo >> 32);
-      if (bi) slot[wi + 2] += (uint32_t)(v >> (64 - bi));
-    }
-  }
-  uint32_t num[W];
-  unsigned long long carry = 0;
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    const unsigned long long t = slot[i] + carry;
-    num[i] = (uint32_t)t;
-    carry = t >> 32;
-  }
+// Exact mean of all block absmax values, rounded once to fp32 (nearest-even),
+// from the total S (in 2^-149 units) given as 32-bit digits: digit[i] has
+// weight 2^(32 i).  S is divided by the block count with 32 extra quotient
+// bits -- enough to reach below the smallest subnormal -- and rounded on the
+// remainder.
+constexpr int kMeanWords = 13;   // S * 2^32 as 32-bit digits (S < 2^(10*32 + 24))
+
+__device__ float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nblocks) {
+  constexpr int W = kMeanWords;
   // long division by nblocks, one 32-bit digit at a time: the digit
   // cur / nblocks (< 2^32 since rem < nblocks) is estimated in fp64 -- cur is
   // below nblocks * 2^32, so its rounding moves the estimate by less than one
   // -- and corrected exactly with an integer multiply-subtract
   uint32_t q[W];
   unsigned long long rem = 0;
-  const double dd = (double)nblocks, inv = 1.0 / dd;
-#pragma unroll
-  for (int i = W - 1; i >= 0; --i) {
+  const double inv = 1.0 / (double)nblocks;
+  int top = W - 1;            // digits above the highest non-zero one give zero quotient digits
+  while (top > 0 && num[top] == 0) q[top--] = 0;
+  for (int i = top; i >= 0; --i) {
     const unsigned long long cur = (rem << 32) | num[i];
     long long qe = (long long)((double)cur * inv);
     long long r = (long long)(cur - (unsigned long long)qe * nblocks);
@@ -334,55 +329,54 @@ __device__ float mean_from_sums(const unsigned long long *sums, const unsigned l
   return __uint_as_float(bits);
 }
 
-constexpr int kMeanGrid = 32;
+// One workgroup of 1024 threads: thread t sums slot t % 16 of rows t/16,
+// t/16 + 64, ... (at most 2049 rows, sixteen loads in flight per thread), the
+// 64 partial sums of each slot are added through LDS, and one thread resolves
+// the carries and forms the mean.  (Spreading the loads over
+// several workgroups that meet through an arrival counter measured slower: the
+// fence, the atomic and the re-read cost more than the loads.)
+constexpr int kMeanThreads = 1024;
 
-__global__ __launch_bounds__(256) void mean_reduce_kernel(
-    unsigned long long *__restrict__ partials, int nrows, uint32_t nblocks,
-    unsigned long long *__restrict__ colsum, unsigned int *__restrict__ arrivals,
-    float *__restrict__ mean_out) {
-  __shared__ unsigned long long red[256];
-  __shared__ bool last;
-  const int t = threadIdx.x;
-  const int g = gridDim.x;
-  // workgroup b sums rows b, b+g, b+2g, .. (coalesced) and, being the only
-  // reader of row b, writes its column totals back over it
-  unsigned long long acc = 0;  // each row entry is below 2^55 and there are at most 1026 rows
-  int r = blockIdx.x;
-  for (; r + 15 * g < nrows; r += 16 * g) {  // sixteen independent loads in flight, then the adds
-    unsigned long long v[16];
+__global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigned long long *__restrict__ partials,
+                                                                  int nrows, uint32_t nblocks,
+                                                                  float *__restrict__ mean_out) {
+  static_assert(kMeanSlots == 16, "the reduction assigns 64 threads per slot");
+  constexpr int G = kMeanThreads / kMeanSlots;   // 64 row lanes
+  constexpr int B = 16;                          // loads in flight per thread
+  __shared__ unsigned long long red[G][kMeanSlots];
+  const int t = threadIdx.x, sl = t & 15, r0 = t >> 4;
+  unsigned long long acc = 0;   // every row slot is below 2^41 and there are at most 2049 rows
+  int r = r0;
+  for (; r + (B - 1) * G < nrows; r += B * G) {
+    unsigned long long v[B];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = partials[(int64_t)(r + i * g) * 256 + t];
+    for (int i = 0; i < B; ++i) v[i] = partials[(int64_t)(r + G * i) * kMeanSlots + sl];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc += v[i];
+    for (int i = 0; i < B; ++i) acc += v[i];
   }
-  for (; r < nrows; r += g) acc += partials[(int64_t)r * 256 + t];
-  partials[(int64_t)blockIdx.x * 256 + t] = acc;
-  __threadfence();
+  for (; r < nrows; r += G) acc += partials[(int64_t)r * kMeanSlots + sl];
+  red[r0][sl] = acc;
   __syncthreads();
-  if (t == 0) last = atomicAdd(arrivals, 1u) == g - 1;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // the last workgroup adds the g rows of totals (plain loads: the fence above
-  // makes the other workgroups' rows visible, and this workgroup has not read
-  // them before)
-  unsigned long long v = 0;
-  int b = 0;
-  for (; b + 16 <= g; b += 16) {
-    unsigned long long w[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = partials[(int64_t)(b + i) * 256 + t];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v += w[i];
+  if (t < kMeanSlots) {
+    unsigned long long v = 0;
+#pragma unroll 16
+    for (int i = 0; i < G; ++i) v += red[i][t];
+    red[0][t] = v;
   }
-  for (; b < g; ++b) v += partials[(int64_t)b * 256 + t];
-  colsum[t] = v;
-  __shared__ unsigned long long nz[4];
-  red[t] = v;
-  const unsigned long long ball = __ballot(v != 0);
-  if ((t & 63) == 0) nz[t >> 6] = ball;
   __syncthreads();
-  if (t == 0) *mean_out = mean_from_sums(red, nz, nblocks);
+  if (t == 0) {
+    // S * 2^32: digit 0 is zero, digit i + 1 is slot i after the carries
+    uint32_t num[kMeanWords];
+    num[0] = 0;
+    unsigned long long carry = 0;
+#pragma unroll
+    for (int i = 0; i < kMeanWords - 1; ++i) {
+      const unsigned long long cur = (i < kMeanSlots ? red[0][i] : 0ull) + carry;
+      num[i + 1] = (uint32_t)cur;
+      carry = cur >> 32;
+    }
+    *mean_out = mean_from_digits(num, nblocks);
+  }
 }
 
 // One wave per group of 256 absmax values.
@@ -426,39 +420,35 @@ hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t 
                            hipStream_t stream) {
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
   const int64_t nfull = numel / kBlock;
-  unsigned long long *colsum = partials ? partials + (int64_t)(kQuantGridMax + 1) * 256 : nullptr;
-  unsigned int *arrivals = partials ? reinterpret_cast<unsigned int *>(colsum + 256) : nullptr;
   int grid = 0;
   if (nfull > 0) {
     int64_t g64 = (nfull + 31) / 32;
     grid = (int)(g64 < kQuantGridMax ? g64 : kQuantGridMax);
     const dim3 g((unsigned)grid), b(256);
     if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<true, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
-      else    hipLaunchKernelGGL((quantize_blocks_kernel<true, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
+      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<true, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
+      else    hipLaunchKernelGGL((quantize_blocks_kernel<true, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
     } else {
-      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<false, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
-      else    hipLaunchKernelGGL((quantize_blocks_kernel<false, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status, arrivals);
+      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<false, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
+      else    hipLaunchKernelGGL((quantize_blocks_kernel<false, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
     }
   }
   int rows = grid;
   if (nfull < nblocks) {
     const dim3 g(1), b(64);
-    unsigned long long *row = partials ? partials + (int64_t)grid * 256 : nullptr;
-    unsigned int *clr = nfull == 0 ? arrivals : nullptr;
+    unsigned long long *row = partials ? partials + (int64_t)grid * kMeanSlots : nullptr;
     if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
+      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
+      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
     } else {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status, clr);
+      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
+      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
     }
     ++rows;
   }
   if (dq) {
-    const int mg = rows < kMeanGrid ? rows : kMeanGrid;
-    hipLaunchKernelGGL(mean_reduce_kernel, dim3((unsigned)mg), dim3(256), 0, stream, partials, rows, (uint32_t)nblocks,
-                       colsum, arrivals, mean_out);
+    hipLaunchKernelGGL(mean_reduce_kernel, dim3(1), dim3(kMeanThreads), 0, stream, partials, rows, (uint32_t)nblocks,
+                       mean_out);
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
     hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ngroups), dim3(64), 0, stream, absmax_out, nblocks, mean_out, q_out, scale_out);
   }

@@ -70,7 +70,7 @@ def test_sizes_closed_forms(L, rows, cols, dq):
     assert s["nblocks"] == nb
     assert s["ngroups"] == -(-nb // 256)
     if dq:
-        assert s["workspace_bytes"] >= 1025 * 2048 + 4 * nb
+        assert s["workspace_bytes"] >= 1025 * 128 + 4 * nb
     else:
         assert s["workspace_bytes"] == 0
 
