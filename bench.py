@@ -16,7 +16,8 @@ dequantizer, the rank-64 adapter variants of both GEMMs, the decode-shape
 forward (M = 1, 4, 16 on a rotating pool of 64 quantized 4096x4096 weights,
 replayed from a HIP graph so host launch overhead does not count), the
 outlier-heavy large shape (M = K = 8192, N = 28672, fp32 Student-t weight), the
-32-layer bulk quantize/dequantize round trip, a roofline entry for the dominant
+32-layer bulk quantize/dequantize round trip, the prefill workload at block sizes
+32, 128 and 256, a roofline entry for the dominant
 kernel and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -337,6 +338,43 @@ def bench_bulk(dg, reps=3):
     return res
 
 
+def bench_blocksizes(dg, reps=5):
+    """The prefill workload with 32, 128 and 256 weights per absmax block."""
+    import synth
+    d = torch.device("cuda:0")
+    M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
+    W = synth.prefill_weight().to(d)
+    X = synth.prefill_x().to(d)
+    dY = synth.prefill_dy().to(d)
+    Y = torch.empty((M, N), dtype=torch.float32, device=d)
+    dX = torch.empty((M, K), dtype=torch.float32, device=d)
+    Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
+    flop = 2.0 * M * N * K
+    out = {}
+    for bs in (32, 128, 256):
+        q = dg.empty_qtensor(N, K, True, d, bs)
+        ws = torch.empty(dg.nf4_sizes(N, K, bs)["workspace_bytes"], dtype=torch.uint8, device=d)
+        fns = {"quantize": lambda: dg.nf4_quantize(W, blocksize=bs, out=q, workspace=ws),
+               "fwd": lambda: dg.nf4_matmul_fwd(X, q, out=Y),
+               "bwd_dx": lambda: dg.nf4_matmul_bwd_dx(dY, q, out=dX)}
+        for fn in fns.values():
+            fn()
+        torch.cuda.synchronize()
+        nb = -(-N * K // bs)
+        wq = N * K // 2 + nb + 4 * (-(-nb // 256)) + 4
+        ms = {k: time_events(fn, reps) for k, fn in fns.items()}
+        ms["dequantize"] = time_graph(lambda: dg.nf4_dequantize(q, out=Wh), reps)
+        out[f"bs{bs}"] = {
+            "quantize_GB/s": (N * K * 2 + wq) / (ms["quantize"] * 1e-3) / 1e9,
+            "dequantize_GB/s": (wq + N * K * 2) / (ms["dequantize"] * 1e-3) / 1e9,
+            "fwd_TFLOP/s": flop / (ms["fwd"] * 1e-3) / 1e12,
+            "bwd_dx_TFLOP/s": flop / (ms["bwd_dx"] * 1e-3) / 1e12,
+            "bits_per_weight": 8.0 * wq / (N * K)}
+    del W, X, dY, Y, dX, Wh
+    torch.cuda.empty_cache()
+    return {"blocksize_variants": out}
+
+
 def cpu_baseline(target_s=12.0):
     """The oracle, as it stands, on a bounded sample of the prefill workload."""
     import oracle as O
@@ -447,6 +485,12 @@ def run_single_op(dg, op, steps, warmup):
     print(json.dumps({"op": op, "steps": steps, "ms_per_call": s.elapsed_time(e) / steps}), flush=True)
 
 
+def _rounded(v):
+    if isinstance(v, dict):
+        return {k: _rounded(x) for k, x in v.items()}
+    return round(v, 4) if isinstance(v, float) else v
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +500,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-large", action="store_true", help="skip the 8192x8192x28672 outlier-heavy shape")
     ap.add_argument("--no-bulk", action="store_true", help="skip the 32-layer quantize/dequantize round trip")
+    ap.add_argument("--no-blocksizes", action="store_true", help="skip the block-size 32/128/256 variants")
     ap.add_argument("--op", default=None, choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     a = ap.parse_args()
@@ -481,6 +526,8 @@ def main():
         ops.update(bench_large(dg))
     if not a.no_bulk:
         ops.update(bench_bulk(dg))
+    if not a.no_blocksizes:
+        ops.update(bench_blocksizes(dg))
     dom = "fwd" if ops["fwd"]["ms"] >= ops["bwd_dx"]["ms"] else "bwd_dx"
     ach = ops[dom]["TFLOP/s"]
     line = {
@@ -503,8 +550,7 @@ def main():
                      "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd_large_kernel" if dom == "fwd" else "bwd_dx_kernel")},
-        "ops": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                for k, v in ops.items()},
+        "ops": {k: _rounded(v) for k, v in ops.items()},
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

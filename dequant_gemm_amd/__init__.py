@@ -9,7 +9,7 @@ layer with autograd over the fused GEMMs) and ``dequant_gemm_amd.io`` (saving
 and loading quantized weights).
 """
 from ._lib import (  # noqa: F401
-    BLOCKSIZE, DQ_GROUP, EXPORTS, LIB_PATH, NF4Error, QTensor, QTensorStruct,
+    BLOCKSIZE, BLOCKSIZES, DQ_GROUP, EXPORTS, LIB_PATH, NF4Error, QTensor, QTensorStruct,
     LORA_MAX_RANK, LORA_RANK_STEP, empty_qtensor, lib, nf4_codebook, nf4_dequantize, nf4_matmul_bwd_dx,
     nf4_matmul_bwd_dx_lora, nf4_matmul_fwd, nf4_matmul_fwd_lora, nf4_quantize, nf4_sizes, nf4_thresholds,
 )

@@ -22,6 +22,7 @@ NF4_OK = 0
 NF4_F32 = 0
 NF4_BF16 = 1
 BLOCKSIZE = 64
+BLOCKSIZES = (32, 64, 128, 256)
 DQ_GROUP = 256
 
 STATUS_NAMES = {
@@ -168,10 +169,12 @@ def nf4_sizes(rows: int, cols: int, blocksize: int = BLOCKSIZE, double_quant: bo
     return {"packed_bytes": pb.value, "nblocks": nb.value, "ngroups": ng.value, "workspace_bytes": ws.value}
 
 
-def empty_qtensor(rows: int, cols: int, double_quant: bool = True, device="cuda") -> QTensor:
-    s = nf4_sizes(rows, cols, BLOCKSIZE, double_quant)
+def empty_qtensor(rows: int, cols: int, double_quant: bool = True, device="cuda",
+                  blocksize: int = BLOCKSIZE) -> QTensor:
+    s = nf4_sizes(rows, cols, blocksize, double_quant)
     dev = torch.device(device)
-    q = QTensor(rows, cols, double_quant, torch.empty(s["packed_bytes"], dtype=torch.uint8, device=dev))
+    q = QTensor(rows, cols, double_quant, torch.empty(s["packed_bytes"], dtype=torch.uint8, device=dev),
+                blocksize=blocksize)
     if double_quant:
         q.absmax_q = torch.empty(s["nblocks"], dtype=torch.int8, device=dev)
         q.absmax_scale = torch.empty(s["ngroups"], dtype=torch.float32, device=dev)
@@ -189,7 +192,7 @@ def nf4_quantize(W: torch.Tensor, blocksize: int = BLOCKSIZE, double_quant: bool
     if W.dim() != 2:
         raise ValueError("W must be 2-D [rows, cols]")
     rows, cols = W.shape
-    q = out if out is not None else empty_qtensor(rows, cols, double_quant, W.device)
+    q = out if out is not None else empty_qtensor(rows, cols, double_quant, W.device, blocksize)
     s = nf4_sizes(rows, cols, blocksize, double_quant)
     if workspace is None and s["workspace_bytes"]:
         workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=W.device)

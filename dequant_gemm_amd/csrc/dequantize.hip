@@ -4,7 +4,7 @@
 // dequantized first (a^ = fp32(fp32(q * s) + mu)) and then used to
 // dequantize the weights, W^ = bf16_rne(fp32(level[code] * a^)).
 // Streaming kernels.  bf16 output: each lane turns 16 bytes of packed codes
-// (32 elements, half a block) into 64 bytes of bf16 through the per-block
+// (32 elements, within one block of 32 or more) into 64 bytes of bf16 through the per-block
 // register table of the 16 values bf16(level_i * a^), the same table the fused
 // GEMMs use.  fp32 output: each lane turns one 32-bit word of codes (eight
 // elements) into 32 bytes of fp32.
@@ -14,7 +14,7 @@ namespace nf4 {
 namespace {
 
 // bf16 kernel: a wave works on tiles of 1 KiB of codes (2,048 elements).  Lane l
-// loads the 16-byte chunk l of the tile (32 elements, half a block) and
+// loads the 16-byte chunk l of the tile (32 elements, inside one block) and
 // dequantizes it into four 16-byte output chunks; these pass through LDS so
 // that each store instruction of the wave writes 1 KiB contiguously (lane l
 // stores output chunk 64j + l of the tile in store j).
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void dequantize_bf16_kernel(const ui
       const int64_t g = (t0 + u) * 64 + lane;        // this lane's 16-byte code chunk
       const int64_t gc = g < n32 ? g : n32 - 1;
       c[u] = reinterpret_cast<const uint4 *>(packed)[gc];
-      r[u] = load_raw<DQ>(src, gc >> 1);
+      r[u] = load_raw<DQ>(src, gc >> (src.lbs - 5));   // chunk gc starts at element 32 gc
     }
     // every load is issued before the first conversion of an int8 absmax
     __builtin_amdgcn_sched_barrier(0);
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
   const int64_t n8 = numel / 8;
   for (int64_t g = start / 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; g < n8; g += (int64_t)gridDim.x * 256) {
     const uint32_t d = *reinterpret_cast<const uint32_t *>(packed + g * 4);
-    const float ah = block_ahat(src, g >> 3, mu);
+    const float ah = block_ahat(src, (g * 8) >> src.lbs, mu);
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = __fmul_rn(lv[(d >> (4 * j)) & 15u], ah);
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
     for (int64_t e = n8 * 8 + threadIdx.x; e < numel; e += 256) {
       const uint8_t byte = packed[e >> 1];
       const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 15u);
-      const float v = __fmul_rn(lv[code], block_ahat(src, e / kBlock, mu));
+      const float v = __fmul_rn(lv[code], block_ahat(src, e >> src.lbs, mu));
       if (OUT_BF16)
         reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
       else

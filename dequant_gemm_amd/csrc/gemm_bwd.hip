@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       cok[h] = kval && n < N;
       const int64_t nc = n < N ? n : N - 1;
       creg[h] = *reinterpret_cast<const uint4 *>(packed + nc * (K / 2) + kqc / 2);
-      rreg[h] = load_absmax_raw(src, (nc * K + kqc) / kBlock);
+      rreg[h] = load_absmax_raw(src, (nc * K + kqc) >> src.lbs);
     }
   };
   auto store_a = [&](int buf) {
@@ -342,7 +342,7 @@ __device__ __forceinline__ void lut_quarter(float ahat, int q, Lut &t) {
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
 
-template <bool DX_BF16, bool DQ, bool LR>
+template <bool DX_BF16, bool DQ, bool LR, bool GBS>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dx_kernel(
     const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ dX, int tiles_m, int tiles_k) {
@@ -364,6 +364,8 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   const int64_t kc = kcol < K ? kcol : K - 32;
   // weight row of this lane in step s: n = 64s + lane
   const uint8_t *wq = packed + (int64_t)lane * (K / 2) + kc / 2;
+  // the block of row n, columns kc .. kc+31: blk0 + (n - lane) K/64 (block size 64), else
+  // the flat index n K + kc shifted by log2(block size) -- never straddles a block
   const int64_t blk0 = (int64_t)lane * (K / kBlock) + kc / kBlock;
 
   // dY tile loads, as the forward kernel's X tiles: wave w's load i (0..3)
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     const int64_t n = sc * TN + lane;
     const int64_t dn = n < N ? sc * TN : N - 1 - lane;     // row offset from this lane's base row
     c.w = *reinterpret_cast<const uint4 *>(wq + dn * (K / 2));
-    c.r = load_raw<DQ>(src, blk0 + dn * (K / kBlock));
+    c.r = load_raw<DQ>(src, GBS ? (((int64_t)lane + dn) * K + kc) >> src.lbs : blk0 + dn * (K / kBlock));
   };
   auto ahat_at = [&](int64_t s, const RowCodes &c) {
     const float v = ahat_of(c.r, DQ, mu);
@@ -624,15 +626,17 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
     using namespace tr_kernel;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
-    static const K_t kern[8] = {
-        bwd_dx_kernel<false, false, false>, bwd_dx_kernel<false, false, true>,
-        bwd_dx_kernel<false, true, false>,  bwd_dx_kernel<false, true, true>,
-        bwd_dx_kernel<true, false, false>,  bwd_dx_kernel<true, false, true>,
-        bwd_dx_kernel<true, true, false>,   bwd_dx_kernel<true, true, true>};
+#define NF4_BWD(GBS)                                                                                          \
+    {bwd_dx_kernel<false, false, false, GBS>, bwd_dx_kernel<false, false, true, GBS>,                          \
+     bwd_dx_kernel<false, true, false, GBS>,  bwd_dx_kernel<false, true, true, GBS>,                           \
+     bwd_dx_kernel<true, false, false, GBS>,  bwd_dx_kernel<true, false, true, GBS>,                           \
+     bwd_dx_kernel<true, true, false, GBS>,   bwd_dx_kernel<true, true, true, GBS>}
+    static const K_t kern[2][8] = {NF4_BWD(false), NF4_BWD(true)};
+#undef NF4_BWD
     const int sel = (dx_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (has_lr ? 1 : 0);
     const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
     const dim3 g((unsigned)(tiles_m * tiles_k)), b(64 * NWAVE);
-    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
+    hipLaunchKernelGGL(kern[src.lbs != 6][sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
   } else {
     using namespace generic;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,

@@ -40,7 +40,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kSmallCols = 16;
 constexpr int kSmallWaves = 8;
 
-template <bool Y_BF16, bool DQ, bool LR>
+template <bool Y_BF16, bool DQ, bool LR, bool BS32>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     const uint16_t *__restrict__ X, int M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ Y) {
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   const bool mvalid = col < M;
   const int m = mvalid ? col : M - 1;          // rows past M likewise
   const float mu = DQ ? *src.mean : 0.f;
-  const int64_t kblocks = K / kBlock;
+  const int64_t kchunks = K / kBlock;          // 64-element chunks per weight row
   const int64_t nsc = (K + 255) / 256;
   const int64_t per = (nsc + kSmallWaves - 1) / kSmallWaves;
   const int64_t s0 = wave * per;
@@ -64,18 +64,21 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t sc = s0; sc < s1; sc += 2) {
     uint4 c[2][2];
-    AbsmaxRaw r[2];
+    AbsmaxRaw r[2], r2[2];   // r2: the second 32-element block of the chunk (block size 32)
     uint4 xa[2][8];
     bool ok[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t bi = 4 * (sc + u) + kg;
-      ok[u] = (sc + u < s1) && (bi < kblocks);
+      const int64_t bi = 4 * (sc + u) + kg;   // 64-element chunk of the weight row
+      ok[u] = (sc + u < s1) && (bi < kchunks);
       const int64_t bic = ok[u] ? bi : 0;
       const uint4 *p = reinterpret_cast<const uint4 *>(wrow + bic * (kBlock / 2));
       c[u][0] = p[0];
       c[u][1] = p[1];
-      r[u] = load_raw<DQ>(src, nc * kblocks + bic);
+      // the chunk's block: its first element's flat index shifted by log2(block size)
+      const int64_t blk = (nc * K + bic * kBlock) >> src.lbs;
+      r[u] = load_raw<DQ>(src, blk);
+      if (BS32) r2[u] = load_raw<DQ>(src, blk + 1);
       // A rows past M are never stored: those lanes feed zeros and load nothing
       // (at M = 1 this removes 15/16 of the X loads, four times the code bytes).
       const uint4 *xp = reinterpret_cast<const uint4 *>(xrow + bic * kBlock);
@@ -90,15 +93,18 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     for (int u = 0; u < 2; ++u) {
       if (sc + u >= s1) break;
       const Lut t = make_lut(ok[u] ? ahat_of(r[u], DQ, mu) : 0.f);
+      Lut t2;
+      if (BS32) t2 = make_lut(ok[u] ? ahat_of(r2[u], DQ, mu) : 0.f);
       const uint32_t words[8] = {c[u][0].x, c[u][0].y, c[u][0].z, c[u][0].w,
                                  c[u][1].x, c[u][1].y, c[u][1].z, c[u][1].w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t b[4];
         Sel4 sa, sb;
+        const Lut &tj = (BS32 && j >= 4) ? t2 : t;
         select8(words[j], sa, sb);
-        lookup4(sa, t, b[0], b[1]);
-        lookup4(sb, t, b[2], b[3]);
+        lookup4(sa, tj, b[0], b[1]);
+        lookup4(sb, tj, b[2], b[3]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u][j]), as_bf16x8(b), acc, 0, 0, 0);
       }
     }
@@ -231,7 +237,7 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <bool Y_BF16, bool DQ, bool LR>
+template <bool Y_BF16, bool DQ, bool LR, bool GBS>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_large_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ Y, int tiles_m, int tiles_n) {
@@ -253,7 +259,10 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   const int64_t ncol = n0 + 32 * wave + bl;
   const int64_t nc = ncol < N ? ncol : N - 1;
   const uint8_t *wq = packed + nc * (K / 2) + kg * 16;
+  // block of step k: blk0 + k (block size 64), else the flat index of the lane's
+  // 32-element chunk shifted by log2(block size) -- a chunk never straddles a block
   const int64_t blk0 = nc * (K / kBlock);
+  const int64_t flat0 = nc * K + 32 * kg;
 
   // X tile loads, buffer-to-LDS: wave w's load i (0..3) fills LDS bytes
   // (4w + i) * 1024 .. +1023, i.e. tile rows 8(4w + i) .. +7; lane l takes row
@@ -291,7 +300,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   auto issue_codes = [&](int64_t kt, StepCodes &c) {
     const int64_t k = clampk(kt);
     c.w = *reinterpret_cast<const uint4 *>(wq + k * (BK / 2));
-    c.r = load_raw<DQ>(src, blk0 + k);
+    c.r = load_raw<DQ>(src, GBS ? (flat0 + k * BK) >> src.lbs : blk0 + k);
   };
   auto ahat_at = [&](int64_t kt, const StepCodes &c) { return kt < nk ? ahat_of(c.r, DQ, mu) : 0.f; };
 
@@ -467,24 +476,28 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
   const int sel = (y_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (lr.r > 0 ? 1 : 0);
   if (M <= 16) {
     using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *);
-    static const K_t kern[8] = {
-        fwd_small_kernel<false, false, false>, fwd_small_kernel<false, false, true>,
-        fwd_small_kernel<false, true, false>,  fwd_small_kernel<false, true, true>,
-        fwd_small_kernel<true, false, false>,  fwd_small_kernel<true, false, true>,
-        fwd_small_kernel<true, true, false>,   fwd_small_kernel<true, true, true>};
+#define NF4_SMALL(BS32)                                                                                       \
+    {fwd_small_kernel<false, false, false, BS32>, fwd_small_kernel<false, false, true, BS32>,                  \
+     fwd_small_kernel<false, true, false, BS32>,  fwd_small_kernel<false, true, true, BS32>,                   \
+     fwd_small_kernel<true, false, false, BS32>,  fwd_small_kernel<true, false, true, BS32>,                   \
+     fwd_small_kernel<true, true, false, BS32>,   fwd_small_kernel<true, true, true, BS32>}
+    static const K_t kern[2][8] = {NF4_SMALL(false), NF4_SMALL(true)};
+#undef NF4_SMALL
     const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols)), b(64 * kSmallWaves);
-    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr, y);
+    hipLaunchKernelGGL(kern[src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr, y);
   } else {
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
-    static const K_t kern[8] = {
-        fwd_large_kernel<false, false, false>, fwd_large_kernel<false, false, true>,
-        fwd_large_kernel<false, true, false>,  fwd_large_kernel<false, true, true>,
-        fwd_large_kernel<true, false, false>,  fwd_large_kernel<true, false, true>,
-        fwd_large_kernel<true, true, false>,   fwd_large_kernel<true, true, true>};
+#define NF4_LARGE(GBS)                                                                                        \
+    {fwd_large_kernel<false, false, false, GBS>, fwd_large_kernel<false, false, true, GBS>,                    \
+     fwd_large_kernel<false, true, false, GBS>,  fwd_large_kernel<false, true, true, GBS>,                     \
+     fwd_large_kernel<true, false, false, GBS>,  fwd_large_kernel<true, false, true, GBS>,                     \
+     fwd_large_kernel<true, true, false, GBS>,   fwd_large_kernel<true, true, true, GBS>}
+    static const K_t kern[2][8] = {NF4_LARGE(false), NF4_LARGE(true)};
+#undef NF4_LARGE
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 g((unsigned)(tiles_m * tiles_n)), b(64 * NWAVE);
-    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, X, M, N, K, packed, src, lr, y, tiles_m, tiles_n);
+    hipLaunchKernelGGL(kern[src.lbs != 6][sel], g, b, 0, stream, X, M, N, K, packed, src, lr, y, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }

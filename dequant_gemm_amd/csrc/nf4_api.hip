@@ -18,13 +18,17 @@ int check_shape(int64_t rows, int64_t cols) {
   return NF4_OK;
 }
 
-int64_t nblocks_of(int64_t numel) { return (numel + NF4_BLOCKSIZE - 1) / NF4_BLOCKSIZE; }
+bool valid_blocksize(int bs) {
+  return bs >= NF4_BLOCKSIZE_MIN && bs <= NF4_BLOCKSIZE_MAX && (bs & (bs - 1)) == 0;
+}
+int log2_of(int bs) { return 31 - __builtin_clz((unsigned)bs); }
+int64_t nblocks_of(int64_t numel, int bs) { return (numel + bs - 1) / bs; }
 int64_t ngroups_of(int64_t nblocks) { return (nblocks + NF4_DQ_GROUP - 1) / NF4_DQ_GROUP; }
 
 // Checks a quantized tensor descriptor and its buffers.
 int check_qtensor(const nf4_qtensor *q) {
   if (!q) return NF4_ERR_NULL;
-  if (q->blocksize != NF4_BLOCKSIZE) return NF4_ERR_BLOCKSIZE;
+  if (!valid_blocksize(q->blocksize)) return NF4_ERR_BLOCKSIZE;
   int st = check_shape(q->rows, q->cols);
   if (st) return st;
   if (q->double_quant != 0 && q->double_quant != 1) return NF4_ERR_UNSUPPORTED;
@@ -48,6 +52,7 @@ nf4::AbsmaxSrc absmax_src(const nf4_qtensor *q) {
   s.scale = q->absmax_scale;
   s.mean = q->absmax_mean;
   s.dq = q->double_quant;
+  s.lbs = log2_of(q->blocksize);
   return s;
 }
 
@@ -62,7 +67,7 @@ const char *nf4_status_string(int status) {
     case NF4_OK: return "ok";
     case NF4_ERR_NULL: return "a required pointer is NULL";
     case NF4_ERR_SHAPE: return "a size is out of range or does not match";
-    case NF4_ERR_BLOCKSIZE: return "blocksize must be 64";
+    case NF4_ERR_BLOCKSIZE: return "blocksize must be 32, 64, 128 or 256";
     case NF4_ERR_DTYPE: return "unknown dtype";
     case NF4_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case NF4_ERR_WORKSPACE: return "workspace too small";
@@ -86,12 +91,12 @@ int nf4_thresholds(float *thresholds15) {
 
 int nf4_sizes(int64_t rows, int64_t cols, int blocksize, int double_quant, int64_t *packed_bytes,
               int64_t *nblocks, int64_t *ngroups, size_t *workspace_bytes) {
-  if (blocksize != NF4_BLOCKSIZE) return NF4_ERR_BLOCKSIZE;
+  if (!valid_blocksize(blocksize)) return NF4_ERR_BLOCKSIZE;
   int st = check_shape(rows, cols);
   if (st) return st;
   if (double_quant != 0 && double_quant != 1) return NF4_ERR_UNSUPPORTED;
   const int64_t numel = rows * cols;
-  const int64_t nb = nblocks_of(numel);
+  const int64_t nb = nblocks_of(numel, blocksize);
   if (packed_bytes) *packed_bytes = (numel + 1) / 2;
   if (nblocks) *nblocks = nb;
   if (ngroups) *ngroups = ngroups_of(nb);
@@ -102,7 +107,7 @@ int nf4_sizes(int64_t rows, int64_t cols, int blocksize, int double_quant, int64
 int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blocksize,
                  int double_quant, const nf4_qtensor *out, void *workspace, size_t workspace_bytes,
                  uint32_t *d_status, void *stream) {
-  if (blocksize != NF4_BLOCKSIZE) return NF4_ERR_BLOCKSIZE;
+  if (!valid_blocksize(blocksize)) return NF4_ERR_BLOCKSIZE;
   if (!W || !out) return NF4_ERR_NULL;
   if (!valid_dtype(w_dtype)) return NF4_ERR_DTYPE;
   int st = check_shape(rows, cols);
@@ -111,10 +116,12 @@ int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blo
   if (!aligned16(W)) return NF4_ERR_ALIGN;
   st = check_qtensor(out);
   if (st) return st;
-  if (out->rows != rows || out->cols != cols || out->double_quant != double_quant) return NF4_ERR_SHAPE;
+  if (out->rows != rows || out->cols != cols || out->double_quant != double_quant ||
+      out->blocksize != blocksize)
+    return NF4_ERR_SHAPE;
   if (d_status && !aligned16(d_status)) return NF4_ERR_ALIGN;
   const int64_t numel = rows * cols;
-  const int64_t nb = nblocks_of(numel);
+  const int64_t nb = nblocks_of(numel, blocksize);
   unsigned long long *partials = nullptr;
   float *absmax = out->absmax;
   if (double_quant) {
@@ -125,9 +132,10 @@ int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blo
     partials = reinterpret_cast<unsigned long long *>(workspace);
     absmax = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + nf4::absmax_ws_offset());
   }
-  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, out->packed, absmax, partials,
-                                         d_status, double_quant, out->absmax_q, out->absmax_scale,
-                                         out->absmax_mean, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, log2_of(blocksize), out->packed, absmax,
+                                         partials, d_status, double_quant, out->absmax_q,
+                                         out->absmax_scale, out->absmax_mean,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 int nf4_dequantize(const nf4_qtensor *q, void *out, int out_dtype, void *stream) {

@@ -79,6 +79,7 @@ struct AbsmaxSrc {
   const float *scale;         // fp32 per group of 256 blocks
   const float *mean;          // one fp32
   int dq;
+  int lbs;                    // log2 of the block size (5..8: 32..256 weights per block)
 };
 
 __device__ __forceinline__ float block_ahat(const AbsmaxSrc &s, int64_t blk, float mu) {

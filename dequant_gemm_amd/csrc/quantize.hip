@@ -107,9 +107,9 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
   return word;
 }
 
-// Eight lanes per block, eight elements per lane.  Each lane's eight codes
-// form one 32-bit word of the packed output (element 2j in the low nibble of
-// byte j).  With double quantization each workgroup also sums the significands
+// LPB lanes per block (block size 8 * LPB: 32, 64, 128 or 256), eight
+// elements per lane.  Each lane's eight codes form one 32-bit word of the
+// packed output (element 2j in the low nibble of byte j).  With double quantization each workgroup also sums the significands
 // of its block absmax values per binary exponent (exact integer sums) and
 // stores the 256 sums as its row of `partials`.  The next block's load is in
 // flight while the current block is encoded.
@@ -123,27 +123,29 @@ __device__ __forceinline__ void add_to_slots(unsigned long long *slot, int e, un
   if (bi) atomicAdd(&slot[wi + 2], (unsigned long long)(uint32_t)(v >> (64 - bi)));
 }
 
-template <bool BF16, bool DQ>
+template <bool BF16, bool DQ, int LPB>
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     const void *__restrict__ w, int64_t nfull, uint8_t *__restrict__ packed,
     float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status) {
+  constexpr int BS = 8 * LPB;        // weights per block
+  constexpr int BPI = 256 / LPB;     // blocks per workgroup and iteration
   __shared__ Cell cells[129];
   __shared__ unsigned long long lbuck[256];
   __shared__ unsigned long long lslot[kMeanSlots];
-  const int part = threadIdx.x & 7;
-  const int slot = threadIdx.x >> 3;
-  const int64_t stride = (int64_t)gridDim.x * 32;
+  const int part = threadIdx.x % LPB;
+  const int slot = threadIdx.x / LPB;
+  const int64_t stride = (int64_t)gridDim.x * BPI;
   auto load = [&](int64_t blk, uint4 &u, uint4 &v) {
     if (BF16) {
-      u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(w) + blk * kBlock + part * 8);
+      u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(w) + blk * BS + part * 8);
     } else {
-      const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(w) + blk * kBlock + part * 8);
+      const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(w) + blk * BS + part * 8);
       u = p[0];
       v = p[1];
     }
   };
   bool bad = false;
-  int64_t blk = (int64_t)blockIdx.x * 32 + slot;
+  int64_t blk = (int64_t)blockIdx.x * BPI + slot;
   uint4 cu = make_uint4(0, 0, 0, 0), cv = cu;
   if (blk < nfull) load(blk, cu, cv);   // in flight while the level table is built
   build_cells(cells);
@@ -174,9 +176,8 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+#pragma unroll
+    for (int sh = 1; sh < LPB; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
 
     uint32_t word;
     if (m >= 0x7f800000u) {
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     } else {
       word = encode8(x, m, cells);
     }
-    *reinterpret_cast<uint32_t *>(packed + blk * (kBlock / 2) + part * 4) = word;
+    *reinterpret_cast<uint32_t *>(packed + blk * (BS / 2) + part * 4) = word;
     if (part == 0) {
       absmax[blk] = __uint_as_float(m);
       if (DQ && m < 0x7f800000u) {
@@ -209,18 +210,18 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
   if (bad && status) atomicOr(status, 1u);
 }
 
-// The partial block at the end (fewer than 64 elements): one wave, one
-// element per lane, exact division.
+// The partial block at the end (fewer than blocksize <= 256 elements): one
+// workgroup of 256 threads, one element per thread, exact division.
 template <bool BF16, bool DQ>
-__global__ __launch_bounds__(64) void quantize_tail_kernel(
-    const void *__restrict__ w, int64_t numel, int64_t blk, uint8_t *__restrict__ packed,
+__global__ __launch_bounds__(256) void quantize_tail_kernel(
+    const void *__restrict__ w, int64_t numel, int64_t blk, int bs, uint8_t *__restrict__ packed,
     float *__restrict__ absmax, unsigned long long *__restrict__ partial_row, uint32_t *status) {
   __shared__ Cell cells[129];
+  __shared__ uint32_t wmax[4];
   build_cells(cells);
-  __syncthreads();
-  const int lane = threadIdx.x;
-  const int64_t e = blk * kBlock + lane;
-  const bool valid = e < numel;
+  const int t = threadIdx.x;
+  const int64_t e = blk * bs + t;
+  const bool valid = t < bs && e < numel;
   float x = 0.f;
   if (valid) {
     if (BF16)
@@ -230,7 +231,10 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
   }
   uint32_t m = __float_as_uint(x) & 0x7fffffffu;
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
+  for (int sh = 1; sh < 64; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   int code = 7;
   if (m != 0 && m < 0x7f800000u) {
     bool unused = false;
@@ -238,8 +242,8 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
   }
   if (!valid) code = 0;
   const int upper = __shfl_down(code, 1);
-  if (valid && (lane & 1) == 0) packed[blk * (kBlock / 2) + lane / 2] = (uint8_t)(code | (upper << 4));
-  if (DQ && lane < kMeanSlots) {
+  if (valid && (t & 1) == 0) packed[(blk * bs + t) / 2] = (uint8_t)(code | (upper << 4));
+  if (DQ && t < kMeanSlots) {
     // this block's accumulator row: the digits of its absmax alone
     const uint32_t ex = m >> 23;
     const unsigned long long sig = (m & 0x7fffffu) | (ex ? 0x800000u : 0u);
@@ -247,12 +251,12 @@ __global__ __launch_bounds__(64) void quantize_tail_kernel(
     const unsigned long long lo = sig << (sh & 31);     // below 2^55
     unsigned long long d = 0;
     if (m < 0x7f800000u) {
-      if (lane == (sh >> 5)) d = (uint32_t)lo;
-      if (lane == (sh >> 5) + 1) d = lo >> 32;
+      if (t == (sh >> 5)) d = (uint32_t)lo;
+      if (t == (sh >> 5) + 1) d = lo >> 32;
     }
-    partial_row[lane] = d;
+    partial_row[t] = d;
   }
-  if (lane == 0) {
+  if (t == 0) {
     absmax[blk] = __uint_as_float(m);
     if (m >= 0x7f800000u && status) atomicOr(status, 1u);
   }
@@ -412,37 +416,51 @@ __global__ __launch_bounds__(64) void double_quant_kernel(const float *__restric
   }
 }
 
+
+template <bool BF16, bool DQ>
+void launch_blocks(int lbs, dim3 g, hipStream_t stream, const void *w, int64_t nfull, uint8_t *packed,
+                   float *absmax_out, unsigned long long *partials, uint32_t *status) {
+  switch (lbs) {
+    case 5: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 4>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+    case 6: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 8>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+    case 7: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 16>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+    default: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 32>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, uint8_t *packed,
+hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs, uint8_t *packed,
                            float *absmax_out, unsigned long long *partials, uint32_t *status,
                            int dq, int8_t *q_out, float *scale_out, float *mean_out,
                            hipStream_t stream) {
-  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
-  const int64_t nfull = numel / kBlock;
+  const int bs = 1 << lbs;
+  const int64_t nblocks = (numel + bs - 1) / bs;
+  const int64_t nfull = numel / bs;
+  const int bpi = 256 / (bs / 8);   // blocks per quantize workgroup and iteration
   int grid = 0;
   if (nfull > 0) {
-    int64_t g64 = (nfull + 31) / 32;
+    int64_t g64 = (nfull + bpi - 1) / bpi;
     grid = (int)(g64 < kQuantGridMax ? g64 : kQuantGridMax);
-    const dim3 g((unsigned)grid), b(256);
+    const dim3 g((unsigned)grid);
     if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<true, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
-      else    hipLaunchKernelGGL((quantize_blocks_kernel<true, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
+      if (dq) launch_blocks<true, true>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
+      else    launch_blocks<true, false>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
     } else {
-      if (dq) hipLaunchKernelGGL((quantize_blocks_kernel<false, true>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
-      else    hipLaunchKernelGGL((quantize_blocks_kernel<false, false>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status);
+      if (dq) launch_blocks<false, true>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
+      else    launch_blocks<false, false>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
     }
   }
   int rows = grid;
   if (nfull < nblocks) {
-    const dim3 g(1), b(64);
+    const dim3 g(1), b(256);
     unsigned long long *row = partials ? partials + (int64_t)grid * kMeanSlots : nullptr;
     if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
+      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
+      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
     } else {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, row, status);
+      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
+      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
     }
     ++rows;
   }

@@ -21,7 +21,7 @@ from typing import Dict
 
 import torch
 
-from ._lib import BLOCKSIZE, QTensor, nf4_codebook, nf4_sizes
+from ._lib import BLOCKSIZES, QTensor, nf4_codebook, nf4_sizes
 
 FORMAT = "nf4-qtensor"
 VERSION = "1"
@@ -88,8 +88,8 @@ def load_qtensors(path: str, device="cpu") -> Dict[str, QTensor]:
         keys = set(f.keys())
         for name, e in entries.items():
             rows, cols, bs, dq = int(e["rows"]), int(e["cols"]), int(e["blocksize"]), bool(e["double_quant"])
-            if bs != BLOCKSIZE:
-                raise ValueError(f"{path}: {name} has block size {bs}; only {BLOCKSIZE} is supported")
+            if bs not in BLOCKSIZES:
+                raise ValueError(f"{path}: {name} has block size {bs}; supported: {BLOCKSIZES}")
             want = _expected_sizes(rows, cols, bs, dq)
             bufs = {}
             for fld, n in want.items():

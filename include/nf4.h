@@ -71,7 +71,7 @@ enum nf4_status {
   NF4_OK = 0,
   NF4_ERR_NULL = 1,         /* a required pointer is NULL */
   NF4_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or too large */
-  NF4_ERR_BLOCKSIZE = 3,    /* blocksize is not 64 */
+  NF4_ERR_BLOCKSIZE = 3,    /* blocksize is not 32, 64, 128 or 256 */
   NF4_ERR_DTYPE = 4,        /* unknown nf4_dtype value */
   NF4_ERR_ALIGN = 5,        /* a device pointer is not 16-byte aligned */
   NF4_ERR_WORKSPACE = 6,    /* workspace smaller than nf4_sizes reports */
@@ -88,8 +88,11 @@ enum nf4_dtype {
 #define NF4_MAX_NUMEL ((int64_t)1 << 37)
 /* The GEMMs take weights with fewer columns than this (32-bit tile offsets). */
 #define NF4_GEMM_COLS_LIMIT ((int64_t)1 << 24)
-/* The only supported block size. */
+/* Weights per absmax block: the default (and the workloads' size) is 64;
+ * 32, 128 and 256 are accepted as well (any power of two in that range). */
 #define NF4_BLOCKSIZE 64
+#define NF4_BLOCKSIZE_MIN 32
+#define NF4_BLOCKSIZE_MAX 256
 /* Absmax values per double-quantization group. */
 #define NF4_DQ_GROUP 256
 /* Low-rank adapter ranks: a multiple of this step, at most the maximum. */
@@ -98,8 +101,11 @@ enum nf4_dtype {
 
 /*
  * A quantized weight: host struct, device buffers (the QuantState analogue).
- * Sizes for rows x cols (numel = rows*cols, nblocks = ceil(numel/64),
- * ngroups = ceil(nblocks/256)):
+ * Blocks run over the row-major flattening: block b holds elements
+ * b*blocksize .. b*blocksize + blocksize - 1 (it may span rows when blocksize
+ * does not divide cols; the last one may be partial).  Sizes for rows x cols
+ * (numel = rows*cols, nblocks = ceil(numel/blocksize), ngroups =
+ * ceil(nblocks/256)):
  *   packed        ceil(numel/2) bytes
  *   absmax        nblocks fp32     (double_quant == 0; NULL otherwise)
  *   absmax_q      nblocks int8     (double_quant == 1)

@@ -60,12 +60,13 @@ def test_thresholds_are_the_exact_decision_boundaries(L):
         assert exact_argmin_code(below, c) == i
 
 
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
 @pytest.mark.parametrize("rows,cols,dq", [(256, 256, True), (4096, 4096, True), (11008, 4096, True),
                                           (28672, 8192, True), (3, 37, False), (1, 1, True)])
-def test_sizes_closed_forms(L, rows, cols, dq):
-    s = dg.nf4_sizes(rows, cols, 64, dq)
+def test_sizes_closed_forms(L, rows, cols, dq, bs):
+    s = dg.nf4_sizes(rows, cols, bs, dq)
     numel = rows * cols
-    nb = -(-numel // 64)
+    nb = -(-numel // bs)
     assert s["packed_bytes"] == -(-numel // 2)
     assert s["nblocks"] == nb
     assert s["ngroups"] == -(-nb // 256)
@@ -99,7 +100,8 @@ def test_sizes_errors(L):
     assert L.nf4_sizes(0, 64, 64, 1, None, None, None, None) == 2
     assert L.nf4_sizes(64, -1, 64, 1, None, None, None, None) == 2
     assert L.nf4_sizes(1 << 20, 1 << 20, 64, 1, None, None, None, None) == 2  # beyond 2^37 elements
-    assert L.nf4_sizes(64, 64, 128, 1, None, None, None, None) == 3
+    for bs in (0, 16, 48, 96, 512, -64):                  # block sizes: 32, 64, 128 or 256
+        assert L.nf4_sizes(64, 64, bs, 1, None, None, None, None) == 3
     assert L.nf4_sizes(64, 64, 64, 2, None, None, None, None) == 7
     assert L.nf4_codebook(None) == 1
 
@@ -112,7 +114,8 @@ def test_quantize_errors(L):
                                       k.get("ws", P), k.get("wsb", ws), k.get("status", None), None)
     assert call(W=None) == 1
     assert call(dt=7) == 4
-    assert call(bs=32) == 3
+    assert call(bs=48) == 3
+    assert call(bs=128) == 2                         # descriptor's block size (64) differs from the call's
     assert call(rows=0) == 2
     assert call(W=P + 2) == 5
     assert call(wsb=ws - 1) == 6
@@ -132,7 +135,7 @@ def test_dequantize_errors(L):
     assert L.nf4_dequantize(ctypes.byref(_qt()), None, 1, None) == 1
     assert L.nf4_dequantize(ctypes.byref(_qt()), P, 5, None) == 4
     assert L.nf4_dequantize(ctypes.byref(_qt()), P + 2, 1, None) == 5
-    assert L.nf4_dequantize(ctypes.byref(_qt(bs=128)), P, 1, None) == 3
+    assert L.nf4_dequantize(ctypes.byref(_qt(bs=16)), P, 1, None) == 3
     assert L.nf4_dequantize(ctypes.byref(_qt(dq=0, absmax=None)), P, 1, None) == 1
 
 

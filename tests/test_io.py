@@ -107,7 +107,7 @@ def test_refuses_malformed(tmp_path):
 
     def other_blocksize(m):
         e = json.loads(m["weights"])
-        e["weight"]["blocksize"] = 128
+        e["weight"]["blocksize"] = 48
         m["weights"] = json.dumps(e)
         return m
     _rewrite(p, bad, meta_fn=other_blocksize)

@@ -186,3 +186,58 @@ def test_dequantized_block_values_lie_in_the_block_lut():
         lut = O.f32_to_bf16_bits((c * q["ahat"][b]).astype(np.float32))
         vals = set(wh[64 * b: 64 * b + 64].tolist())
         assert len(vals) <= 16 and vals <= set(lut.tolist())
+
+
+# ------------------------------------------------------------------ other block sizes
+# The absmax block is 64 weights on the pages ("bitsandbytes" page, double
+# quantization paragraph); the same definition with 32, 128 or 256 weights per
+# block is pinned the same way: exact absmax, exact nearest level of the IEEE
+# quotient, and the relation between the absmax of neighbouring block sizes.
+
+@pytest.mark.parametrize("bs", [32, 128, 256])
+def test_elementwise_bruteforce_other_block_sizes(bs):
+    rng = np.random.default_rng(40 + bs)
+    n = bs * 12 + bs // 2 + 3                                             # partial last block
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w[bs:2 * bs] = rng.standard_t(4, bs).astype(np.float32)
+    w[2 * bs:3 * bs] = np.float32(1e-40) * rng.integers(-5, 6, bs)
+    w[3 * bs:4 * bs] = 0.0
+    q = O.quantize(w, blocksize=bs, double_quant_on=False)
+    c = O.codebook()
+    nb = -(-n // bs)
+    assert q["absmax"].size == nb and q["packed"].size == (n + 1) // 2
+    for b in range(nb):
+        blk = w[bs * b: bs * b + bs]
+        a = max(abs(float(v)) for v in blk)
+        assert q["absmax"][b] == np.float32(a)
+        for i, x in enumerate(blk):
+            want = 7 if a == 0 else exact_argmin_code(np.float32(x) / np.float32(a), c)
+            assert q["codes"][bs * b + i] == want, (bs, b, i)
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_absmax_of_doubled_block_size(bs):
+    rng = np.random.default_rng(7)
+    w = (rng.standard_t(4, bs * 2 * 100 + 37) * 0.02).astype(np.float32)
+    a1 = O.quantize(w, blocksize=bs, double_quant_on=False)["absmax"]
+    a2 = O.quantize(w, blocksize=2 * bs, double_quant_on=False)["absmax"]
+    pairs = np.maximum(a1[0::2][: a2.size], np.append(a1[1::2], np.float32(0))[: a2.size])
+    assert np.array_equal(a2, pairs)
+
+
+@pytest.mark.parametrize("bs", [32, 256])
+def test_double_quant_and_round_trip_other_block_sizes(bs):
+    rng = np.random.default_rng(50 + bs)
+    w = (rng.standard_normal(bs * 256 * 3 + bs * 5) * 0.02).astype(np.float32)
+    q = O.quantize(w, blocksize=bs, double_quant_on=True)
+    nb = -(-w.size // bs)
+    assert q["absmax_q"].size == nb and q["scale"].size == -(-nb // 256)
+    mean = sum(Fraction(float(a)) for a in q["absmax"]) / nb
+    assert abs(Fraction(float(q["mean"])) - mean) <= abs(mean) * Fraction(1, 2 ** 24)
+    err = np.abs(q["ahat"].astype(np.float64) - q["absmax"])
+    s_per_block = np.repeat(q["scale"], 256)[:nb].astype(np.float64)
+    assert np.all(err <= s_per_block / 2 + 4 * np.spacing(np.abs(q["absmax"]).astype(np.float32)))
+    wh = O.bf16_bits_to_f32(O.dequantize(q))
+    q2 = O.quantize(wh, blocksize=bs, double_quant_on=False)
+    ok = np.repeat(q["ahat"] > 0, bs)[: w.size]
+    assert np.array_equal(q2["codes"][ok], q["codes"][ok])
