@@ -596,7 +596,24 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   const int64_t col = kcol + bl;
-  if (kcol < K) {
+  if (m0 + TM <= M && k0 + TK <= K && K < ((int64_t)1 << 27)) {
+    // a full tile: every store is a wave-uniform row address (scalar arithmetic) plus the
+    // lane's 32-bit byte offset (row 4kg, column l%32), with no per-store bounds test
+    constexpr int ES = DX_BF16 ? 2 : 4;
+    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)K + bl) * ES;
+    uint8_t *xcol = reinterpret_cast<uint8_t *>(dX) + (m0 * K + kcol) * ES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        uint8_t *rowp = xcol + (int64_t)(32 * i + 8 * (r / 4) + (r % 4)) * K * ES;
+        if (DX_BF16)
+          *reinterpret_cast<uint16_t *>(rowp + voff) = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
+        else
+          *reinterpret_cast<float *>(rowp + voff) = acc[i][r];
+      }
+    }
+  } else if (kcol < K) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
