@@ -24,7 +24,8 @@
  *
  * Exact semantics (the readings where the pages are silent):
  *  - weight W is logical [rows, cols] row-major, flattened e = r*cols + c;
- *    block b holds elements 64b .. 64b+63 (the last block may be partial);
+ *    with B weights per block (64 by default; 32, 128 or 256), block b holds
+ *    elements Bb .. Bb+B-1 (the last block may be partial);
  *  - a_b = max|x| over the block (fp32); n = fp32(x / a_b) (IEEE division);
  *    code = index of the nearest NF4 level, ties to the lower index; an
  *    all-zero block codes every element 7 (the level 0.0);
