@@ -339,7 +339,8 @@ def bench_bulk(dg, reps=3):
 
 
 def bench_blocksizes(dg, reps=5):
-    """The prefill workload with 32, 128 and 256 weights per absmax block."""
+    """The prefill workload with 32, 128 and 256 weights per absmax block, and at 64
+    without double quantization (fp32 absmax per block)."""
     import synth
     d = torch.device("cuda:0")
     M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
@@ -351,20 +352,21 @@ def bench_blocksizes(dg, reps=5):
     Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
     flop = 2.0 * M * N * K
     out = {}
-    for bs in (32, 128, 256):
-        q = dg.empty_qtensor(N, K, True, d, bs)
-        ws = torch.empty(dg.nf4_sizes(N, K, bs)["workspace_bytes"], dtype=torch.uint8, device=d)
-        fns = {"quantize": lambda: dg.nf4_quantize(W, blocksize=bs, out=q, workspace=ws),
+    for name, bs, dq in (("bs32", 32, True), ("bs128", 128, True), ("bs256", 256, True),
+                         ("bs64_no_double_quant", 64, False)):
+        q = dg.empty_qtensor(N, K, dq, d, bs)
+        ws = torch.empty(dg.nf4_sizes(N, K, bs, dq)["workspace_bytes"], dtype=torch.uint8, device=d) if dq else None
+        fns = {"quantize": lambda: dg.nf4_quantize(W, blocksize=bs, double_quant=dq, out=q, workspace=ws),
                "fwd": lambda: dg.nf4_matmul_fwd(X, q, out=Y),
                "bwd_dx": lambda: dg.nf4_matmul_bwd_dx(dY, q, out=dX)}
         for fn in fns.values():
             fn()
         torch.cuda.synchronize()
         nb = -(-N * K // bs)
-        wq = N * K // 2 + nb + 4 * (-(-nb // 256)) + 4
+        wq = N * K // 2 + (nb + 4 * (-(-nb // 256)) + 4 if dq else 4 * nb)
         ms = {k: time_events(fn, reps) for k, fn in fns.items()}
         ms["dequantize"] = time_graph(lambda: dg.nf4_dequantize(q, out=Wh), reps)
-        out[f"bs{bs}"] = {
+        out[name] = {
             "quantize_GB/s": (N * K * 2 + wq) / (ms["quantize"] * 1e-3) / 1e9,
             "dequantize_GB/s": (wq + N * K * 2) / (ms["dequantize"] * 1e-3) / 1e9,
             "fwd_TFLOP/s": flop / (ms["fwd"] * 1e-3) / 1e12,
