@@ -47,51 +47,99 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   __shared__ f32x4 red[kSmallWaves - 1][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
-  const int64_t n = (int64_t)blockIdx.x * kSmallCols + col;
+  const int64_t n0 = (int64_t)blockIdx.x * kSmallCols;
+  const int64_t n = n0 + col;
   const bool nvalid = n < N;
   const int64_t nc = nvalid ? n : N - 1;       // columns past N compute garbage, never stored
   const bool mvalid = col < M;
-  const int m = mvalid ? col : M - 1;          // rows past M likewise
   const float mu = DQ ? *src.mean : 0.f;
-  const int64_t kchunks = K / kBlock;          // 64-element chunks per weight row
-  const int64_t nsc = (K + 255) / 256;
-  const int64_t per = (nsc + kSmallWaves - 1) / kSmallWaves;
-  const int64_t s0 = wave * per;
-  const int64_t s1 = s0 + per < nsc ? s0 + per : nsc;
-  const uint8_t *wrow = packed + nc * (K / 2);
-  const uint16_t *xrow = X + (int64_t)m * K;
+  const int kchunks = (int)(K / kBlock);       // 64-element chunks per weight row
+  const int nsc = (int)((K + 255) / 256);
+  const int per = (nsc + kSmallWaves - 1) / kSmallWaves;
+  const int s0 = wave * per;
+  const int s1 = s0 + per < nsc ? s0 + per : nsc;
+
+  // All loads go through buffer descriptors based at the workgroup's first
+  // weight row, with 32-bit per-lane offsets (K < 2^24 and 16 rows): no 64-bit
+  // address arithmetic per lane, and a lane whose offset lies past a
+  // descriptor's end reads zeros.  That is how the X loads of rows past M
+  // yield the zeros those lanes feed (their products land in output rows
+  // that are never stored): at M = 1 this removes 15/16 of the X loads, four
+  // times the code bytes, with no masking.  Weight rows past N get zero codes
+  // (their outputs are never stored either).
+  const int rows = (int)(N - n0 < kSmallCols ? N - n0 : kSmallCols);
+  const uint32_t rowb = (uint32_t)(K / 2);
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(packed + n0 * (K / 2)), (short)0,
+                                        (int)(rows * rowb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(X), (short)0, (int)(M * K * 2), 0x00020000);
+  // Blocks: the block of flat element e is e >> lbs.  The workgroup's first
+  // element n0 K is a multiple of 16 * 64, so its block fb = n0 K >> lbs is
+  // exact and a lane's block is fb + ((col K + k) >> lbs).
+  const int64_t nblocks = (N * K + (1 << src.lbs) - 1) >> src.lbs;
+  const int64_t fb = (n0 * K) >> src.lbs;
+  const int64_t fg = fb >> 8;                   // the group of block fb
+  const int fbo = (int)(fb & 255);              // fb's place in its group
+  const int64_t blks = nblocks - fb;            // blocks from fb to the end (descriptor sizes clamp at 2^31 - 1)
+  auto nrec = [](int64_t bytes) { return (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff); };
+  __amdgpu_buffer_rsrc_t ars, srs;              // fp32 absmax, group scales
+  if (DQ) {
+    srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src.scale + fg), (short)0,
+                                            nrec(4 * (((nblocks + 255) >> 8) - fg)), 0x00020000);
+  } else {
+    ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src.absmax + fb), (short)0, nrec(4 * blks), 0x00020000);
+  }
+  // (the int8 absmax is a plain load, clamped to the last block: a sign-extended
+  // buffer byte load gets moved behind every other load)
+  const int8_t *qwg = DQ ? src.q + fb : nullptr;
+  const uint32_t qlast = (uint32_t)(blks - 1 < 0x7fffffff ? blks - 1 : 0x7fffffff);
+  auto load_abs = [&](uint32_t rb) {            // rb: block relative to fb
+    AbsmaxRaw a;
+    if (DQ) {
+      a.q = qwg[rb < qlast ? rb : qlast];
+      a.v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, ((uint32_t)fbo + rb) >> 8 << 2, 0, 0));
+    } else {
+      a.q = 0;
+      a.v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, rb << 2, 0, 0));
+    }
+    return a;
+  };
+  const uint32_t wlane = (uint32_t)col * rowb;             // the lane's row within the descriptor
+  const uint32_t elane = (uint32_t)col * (uint32_t)K;      // its first flat element, relative to n0 K
+  const uint32_t xlane = mvalid ? (uint32_t)col * (uint32_t)K * 2 : 0x80000000u;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t sc = s0; sc < s1; sc += 2) {
+  for (int sc = s0; sc < s1; sc += 2) {
     uint4 c[2][2];
     AbsmaxRaw r[2], r2[2];   // r2: the second 32-element block of the chunk (block size 32)
     uint4 xa[2][8];
     bool ok[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t bi = 4 * (sc + u) + kg;   // 64-element chunk of the weight row
+      const int bi = 4 * (sc + u) + kg;        // 64-element chunk of the weight row
       ok[u] = (sc + u < s1) && (bi < kchunks);
-      const int64_t bic = ok[u] ? bi : 0;
-      const uint4 *p = reinterpret_cast<const uint4 *>(wrow + bic * (kBlock / 2));
-      c[u][0] = p[0];
-      c[u][1] = p[1];
-      // the chunk's block: its first element's flat index shifted by log2(block size)
-      const int64_t blk = (nc * K + bic * kBlock) >> src.lbs;
-      r[u] = load_raw<DQ>(src, blk);
-      if (BS32) r2[u] = load_raw<DQ>(src, blk + 1);
-      // A rows past M are never stored: those lanes feed zeros and load nothing
-      // (at M = 1 this removes 15/16 of the X loads, four times the code bytes).
-      const uint4 *xp = reinterpret_cast<const uint4 *>(xrow + bic * kBlock);
+      const uint32_t bic = ok[u] ? (uint32_t)bi : 0u;
+      const uint32_t wo = wlane + bic * (kBlock / 2);
+      c[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, 0));
+      c[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo + 16, 0, 0));
+      const uint32_t rb = (elane + bic * kBlock) >> src.lbs;
+      r[u] = load_abs(rb);
+      if (BS32) r2[u] = load_abs(rb + 1);
+      const uint32_t xo = xlane + bic * (kBlock * 2);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xa[u][j] = make_uint4(0u, 0u, 0u, 0u);
-      if (mvalid) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xa[u][j] = xp[j];
-      }
+      for (int j = 0; j < 8; ++j)
+        xa[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * j, 0, 0));
+      // every load before any arithmetic, chunk 0's before chunk 1's (left to itself
+      // the compiler sinks the X loads next to their MFMAs to save registers, or
+      // puts both chunks' absmax loads last; either serialises the latencies)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // (a chunk past the wave's range has ok = false: a zero table, so its
+    // MFMAs add exact zeros; no branch, so no load is sunk into one)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      if (sc + u >= s1) break;
       const Lut t = make_lut(ok[u] ? ahat_of(r[u], DQ, mu) : 0.f);
       Lut t2;
       if (BS32) t2 = make_lut(ok[u] ? ahat_of(r2[u], DQ, mu) : 0.f);
@@ -117,7 +165,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
       uint4 av = make_uint4(0u, 0u, 0u, 0u), bv = make_uint4(0u, 0u, 0u, 0u);
       if (rk < lr.r) {
         bv = *reinterpret_cast<const uint4 *>(lr.v + nc * lr.r + rk);
-        if (mvalid) av = *reinterpret_cast<const uint4 *>(lr.u + (int64_t)m * lr.r + rk);
+        if (mvalid) av = *reinterpret_cast<const uint4 *>(lr.u + (int64_t)col * lr.r + rk);
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
     }
