@@ -22,7 +22,7 @@
 // the 256 exponent sums into the digits of one fixed-point integer: slot i
 // accumulates (64-bit, carries left unresolved) the 32-bit digit of weight
 // 2^(32 i) units of every term.  The ten used slots of all rows are summed in
-// 64 bits (no overflow below 2^37 elements) and the carries resolved once at
+// 64 bits (no overflow below 2^37 elements; tensors hold at most 2^36) and the carries resolved once at
 // the end: integer sums, so the result does not depend on any order.
 #include "nf4_launch.h"
 
@@ -333,10 +333,12 @@ __device__ float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nbloc
   return __uint_as_float(bits);
 }
 
-// One workgroup of 1024 threads: thread t sums slot t % 16 of rows t/16,
-// t/16 + 64, ... (at most 2049 rows, sixteen loads in flight per thread), the
-// 64 partial sums of each slot are added through LDS, and one thread resolves
-// the carries and forms the mean.  (Spreading the loads over
+// One workgroup of 1024 threads: thread t sums the 16-byte piece t % 8 (slots
+// 2(t%8) and 2(t%8)+1) of rows t/8, t/8 + 128, ... (at most 2049 rows: all of a
+// thread's seventeen loads in flight at once), the 128 partial sums of each
+// slot are added through LDS in two stages, and one thread resolves the
+// carries and forms the mean.  Integer sums: the order does not matter.
+// (Two dependent rounds of 8-byte loads took ~8.4 us.)  (Spreading the loads over
 // several workgroups that meet through an arrival counter measured slower: the
 // fence, the atomic and the re-read cost more than the loads.)
 constexpr int kMeanThreads = 1024;
@@ -344,29 +346,37 @@ constexpr int kMeanThreads = 1024;
 __global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigned long long *__restrict__ partials,
                                                                   int nrows, uint32_t nblocks,
                                                                   float *__restrict__ mean_out) {
-  static_assert(kMeanSlots == 16, "the reduction assigns 64 threads per slot");
-  constexpr int G = kMeanThreads / kMeanSlots;   // 64 row lanes
-  constexpr int B = 16;                          // loads in flight per thread
-  __shared__ unsigned long long red[G][kMeanSlots];
-  const int t = threadIdx.x, sl = t & 15, r0 = t >> 4;
-  unsigned long long acc = 0;   // every row slot is below 2^41 and there are at most 2049 rows
-  int r = r0;
-  for (; r + (B - 1) * G < nrows; r += B * G) {
-    unsigned long long v[B];
+  static_assert(kMeanSlots == 16, "a row is eight 16-byte pieces of two slots");
+  constexpr int RL = kMeanThreads / 8;                          // 128 rows per pass
+  constexpr int P = (kQuantGridMax + 1 + RL - 1) / RL;          // passes for the most rows (17)
+  __shared__ unsigned long long red[RL][kMeanSlots];
+  const int t = threadIdx.x, pc = t & 7, rl = t >> 3;           // slots 2pc, 2pc+1 of rows rl + 128 i
+  // every load of the thread in flight at once: one memory round trip
+  ulonglong2 v[P];
 #pragma unroll
-    for (int i = 0; i < B; ++i) v[i] = partials[(int64_t)(r + G * i) * kMeanSlots + sl];
-#pragma unroll
-    for (int i = 0; i < B; ++i) acc += v[i];
+  for (int i = 0; i < P; ++i) {
+    const int r = rl + RL * i;
+    v[i] = r < nrows ? reinterpret_cast<const ulonglong2 *>(partials + (int64_t)r * kMeanSlots)[pc]
+                     : make_ulonglong2(0ull, 0ull);
   }
-  for (; r < nrows; r += G) acc += partials[(int64_t)r * kMeanSlots + sl];
-  red[r0][sl] = acc;
+  unsigned long long a0 = 0, a1 = 0;   // every row slot is below 2^41 and there are at most 2049 rows
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    a0 += v[i].x;
+    a1 += v[i].y;
+  }
+  red[rl][2 * pc] = a0;
+  red[rl][2 * pc + 1] = a1;
   __syncthreads();
-  if (t < kMeanSlots) {
-    unsigned long long v = 0;
-#pragma unroll 16
-    for (int i = 0; i < G; ++i) v += red[i][t];
-    red[0][t] = v;
+  // 128 partial rows -> 16 (threads 0..255: slot t%16, rows 8(t/16) .. +7), then -> 1
+  unsigned long long w = 0;
+  if (t < 16 * 16) {
+    const int sl = t & 15, g = t >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w += red[8 * g + i][sl];
   }
+  __syncthreads();
+  if (t < 16 * 16) red[t >> 4][t & 15] = w;
   __syncthreads();
   if (t == 0) {
     // S * 2^32: digit 0 is zero, digit i + 1 is slot i after the carries
@@ -375,7 +385,12 @@ __global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigne
     unsigned long long carry = 0;
 #pragma unroll
     for (int i = 0; i < kMeanWords - 1; ++i) {
-      const unsigned long long cur = (i < kMeanSlots ? red[0][i] : 0ull) + carry;
+      unsigned long long slot = 0;
+      if (i < kMeanSlots) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) slot += red[g][i];
+      }
+      const unsigned long long cur = slot + carry;
       num[i + 1] = (uint32_t)cur;
       carry = cur >> 32;
     }

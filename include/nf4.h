@@ -85,8 +85,9 @@ enum nf4_dtype {
   NF4_BF16 = 1
 };
 
-/* Largest element count a quantized tensor may hold (2^37). */
-#define NF4_MAX_NUMEL ((int64_t)1 << 37)
+/* Largest element count a quantized tensor may hold (2^36; a weight that size
+ * is 128 GiB in bf16, and its block count fits 32 bits at every block size). */
+#define NF4_MAX_NUMEL ((int64_t)1 << 36)
 /* The GEMMs take weights with fewer columns than this (32-bit tile offsets). */
 #define NF4_GEMM_COLS_LIMIT ((int64_t)1 << 24)
 /* Weights per absmax block: the default (and the workloads' size) is 64;

@@ -99,7 +99,14 @@ def test_sizes_errors(L):
     i64 = ctypes.c_int64
     assert L.nf4_sizes(0, 64, 64, 1, None, None, None, None) == 2
     assert L.nf4_sizes(64, -1, 64, 1, None, None, None, None) == 2
-    assert L.nf4_sizes(1 << 20, 1 << 20, 64, 1, None, None, None, None) == 2  # beyond 2^37 elements
+    assert L.nf4_sizes(1 << 20, 1 << 20, 64, 1, None, None, None, None) == 2  # beyond 2^36 elements
+    # exactly 2^36 elements is accepted at every block size (the block count stays below 2^31);
+    # one more row is not
+    nb = i64()
+    for bs in (32, 64, 128, 256):
+        assert L.nf4_sizes(1 << 18, 1 << 18, bs, 1, None, ctypes.byref(nb), None, None) == 0
+        assert nb.value == (1 << 36) // bs
+        assert L.nf4_sizes((1 << 18) + 1, 1 << 18, bs, 1, None, None, None, None) == 2
     for bs in (0, 16, 48, 96, 512, -64):                  # block sizes: 32, 64, 128 or 256
         assert L.nf4_sizes(64, 64, bs, 1, None, None, None, None) == 3
     assert L.nf4_sizes(64, 64, 64, 2, None, None, None, None) == 7
