@@ -21,7 +21,10 @@ and no worked example):
 * [bnb-gemm] same page, the paragraph on quantized-weight GEMM kernels: weights
   dequantized on the fly, float32 multiply, float32 outputs.
 * [bnb-lora] same page, the paragraph on 4-bit training with low-rank
-  adapters: the 4-bit base weight stays frozen while small adapters train.
+  adapters: the 4-bit base weight stays frozen while small adapters train;
+  the 4-bit data type is NF4 or FP4, "standard floating-point 4-bit".  The
+  NF4 paragraph contrasts NF4 with FP4's uniform floating-point spacing, and
+  the QuantState paragraph has the data type travel with the quantized state.
 
 Readings taken where the pages are silent (each is listed, with the reason, in
 the design notes of the repository):
@@ -48,6 +51,13 @@ the design notes of the repository):
   gradient dY W^ + (dY B) A.  The fused calls take the bf16 down-projected
   activation U = X A^T (or V = dY B) as given and add U B^T (or V A) in the
   same accumulation; the bound adds the adapter product's magnitude term.
+* R8 FP4 codebook: the standard 4-bit float E2M1 (one sign bit, two exponent
+  bits with bias 1, one mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+  A code is the format's own bit pattern (bit 3 the sign), its level the
+  value divided by 6 (the largest) and rounded once to float32, so the table
+  spans [-1, 1] like NF4's.  Quantization is the same nearest-level search
+  with ties to the lower code, which in this encoding is toward zero on both
+  sides; zero (and an all-zero block) takes code 0, the +0 level.
 
 Arrays: a weight is a float32 numpy array (bf16 inputs are passed upcast to
 float32, which is exact); bf16 outputs are returned as uint16 bit patterns.
@@ -62,7 +72,8 @@ from scipy.special import ndtri
 
 __all__ = [
     "DELTA", "BLOCKSIZE", "DQ_GROUP", "GEMM_RTOL",
-    "nf4_levels_f64", "codebook",
+    "nf4_levels_f64", "codebook", "fp4_levels_f64", "fp4_codebook", "codebook_of", "zero_code",
+    "QUANT_TYPES",
     "f32_to_bf16_bits", "bf16_bits_to_f32",
     "block_absmax", "normalize", "nearest_code", "encode_blocks", "pack_codes", "unpack_codes",
     "round_rational_to_f32", "exact_mean_f32",
@@ -99,6 +110,43 @@ def nf4_levels_f64(ppf=ndtri):
 def codebook() -> np.ndarray:
     """The NF4 codebook: 16 ascending float32 levels, c[0] = -1, c[7] = 0, c[15] = 1."""
     return np.array(nf4_levels_f64(), dtype=np.float64).astype(np.float32)
+
+
+def fp4_levels_f64():
+    """The 16 FP4 levels in float64, indexed by code (R8).
+
+    Code bits s e1 e0 m: an exponent field of 0 is subnormal, m * 2^-1; a
+    field e >= 1 is 2^(e-1) * (1 + m/2).  The value is divided by the largest
+    magnitude, 6.
+    """
+    out = []
+    for code in range(16):
+        s, e, m = code >> 3, (code >> 1) & 3, code & 1
+        mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+        out.append((-mag if s else mag) / 6.0)
+    return out
+
+
+def fp4_codebook() -> np.ndarray:
+    """The FP4 codebook by code: c[0] = +0, c[7] = 1, c[8] = -0, c[15] = -1 (R8)."""
+    return np.array(fp4_levels_f64(), dtype=np.float64).astype(np.float32)
+
+
+QUANT_TYPES = ("nf4", "fp4")
+
+
+def codebook_of(quant_type: str = "nf4") -> np.ndarray:
+    if quant_type == "nf4":
+        return codebook()
+    if quant_type == "fp4":
+        return fp4_codebook()
+    raise ValueError(f"unknown quant_type {quant_type!r}")
+
+
+def zero_code(c: np.ndarray) -> int:
+    """The code of the +0 level: what an all-zero block codes every element as (R2, R8)."""
+    c = np.asarray(c, np.float32)
+    return int(np.flatnonzero((c == 0) & ~np.signbit(c))[0])
 
 
 # --------------------------------------------------------------------------- bf16 <-> fp32
@@ -189,11 +237,13 @@ def encode_blocks(xb: np.ndarray, a: np.ndarray, c: np.ndarray | None = None) ->
     [bnb-nf4] / [zenbit]: divide by the block absmax, map to the nearest NF4
     level.  A block whose absmax is 0 codes every element as 7 (R2).
     """
+    if c is None:
+        c = codebook()
     xb = np.asarray(xb, np.float32)
     a = np.asarray(a, np.float32)
     n = normalize(xb, a[:, None])
     codes = nearest_code(n, c).reshape(xb.shape)
-    codes[a == 0, :] = 7
+    codes[a == 0, :] = zero_code(c)
     return codes
 
 
@@ -318,20 +368,23 @@ def dequantize_codes(codes: np.ndarray, ahat: np.ndarray, blocksize: int = BLOCK
     return res
 
 
-def quantize(w: np.ndarray, blocksize: int = BLOCKSIZE, double_quant_on: bool = True) -> dict:
-    """Full NF4 blockwise quantization of a float32 weight (row-major flattening).
+def quantize(w: np.ndarray, blocksize: int = BLOCKSIZE, double_quant_on: bool = True,
+             quant_type: str = "nf4") -> dict:
+    """Full 4-bit blockwise quantization of a float32 weight (row-major flattening).
 
-    Returns a dict with ``codes`` (uint8 per element), ``packed`` (uint8),
-    ``absmax`` (float32 per block), and with double quantization ``mean``,
-    ``absmax_q`` (int8 per block), ``scale`` (float32 per group); plus
-    ``ahat`` (the absmax the dequantizer uses).
+    ``quant_type`` picks the codebook: "nf4" (R1) or "fp4" (R8).  Returns a dict
+    with ``codes`` (uint8 per element), ``packed`` (uint8), ``absmax`` (float32
+    per block), and with double quantization ``mean``, ``absmax_q`` (int8 per
+    block), ``scale`` (float32 per group); plus ``ahat`` (the absmax the
+    dequantizer uses).
     """
     w = np.asarray(w, np.float32).ravel()
     if not np.all(np.isfinite(w)):
         raise ValueError("non-finite weight: outside the method's domain")
+    c = codebook_of(quant_type)
     a = block_absmax(w, blocksize)
-    codes = encode_blocks(_blocks(w, blocksize), a).ravel()[: w.size]
-    res = {"numel": w.size, "blocksize": blocksize, "codes": codes,
+    codes = encode_blocks(_blocks(w, blocksize), a, c).ravel()[: w.size]
+    res = {"numel": w.size, "blocksize": blocksize, "codes": codes, "quant_type": quant_type,
            "packed": pack_codes(codes), "absmax": a, "double_quant": bool(double_quant_on)}
     if double_quant_on:
         mu = exact_mean_f32(a)
@@ -343,7 +396,8 @@ def quantize(w: np.ndarray, blocksize: int = BLOCKSIZE, double_quant_on: bool = 
 
 
 def dequantize(qs: dict, out: str = "bf16") -> np.ndarray:
-    return dequantize_codes(qs["codes"], qs["ahat"], qs["blocksize"], out)
+    return dequantize_codes(qs["codes"], qs["ahat"], qs["blocksize"], out,
+                            c=codebook_of(qs.get("quant_type", "nf4")))
 
 
 # --------------------------------------------------------------------------- GEMMs (R6)
