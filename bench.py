@@ -339,8 +339,8 @@ def bench_bulk(dg, reps=3):
 
 
 def bench_blocksizes(dg, reps=5):
-    """The prefill workload with 32, 128 and 256 weights per absmax block, and at 64
-    without double quantization (fp32 absmax per block)."""
+    """The prefill workload with 32, 128 and 256 weights per absmax block, at 64
+    without double quantization (fp32 absmax per block), and with the FP4 level table."""
     import synth
     d = torch.device("cuda:0")
     M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
@@ -352,9 +352,9 @@ def bench_blocksizes(dg, reps=5):
     Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
     flop = 2.0 * M * N * K
     out = {}
-    for name, bs, dq in (("bs32", 32, True), ("bs128", 128, True), ("bs256", 256, True),
-                         ("bs64_no_double_quant", 64, False)):
-        q = dg.empty_qtensor(N, K, dq, d, bs)
+    for name, bs, dq, qt in (("bs32", 32, True, "nf4"), ("bs128", 128, True, "nf4"), ("bs256", 256, True, "nf4"),
+                             ("bs64_no_double_quant", 64, False, "nf4"), ("fp4_bs64", 64, True, "fp4")):
+        q = dg.empty_qtensor(N, K, dq, d, bs, qt)
         ws = torch.empty(dg.nf4_sizes(N, K, bs, dq)["workspace_bytes"], dtype=torch.uint8, device=d) if dq else None
         fns = {"quantize": lambda: dg.nf4_quantize(W, blocksize=bs, double_quant=dq, out=q, workspace=ws),
                "fwd": lambda: dg.nf4_matmul_fwd(X, q, out=Y),

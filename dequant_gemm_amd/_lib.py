@@ -24,13 +24,15 @@ NF4_BF16 = 1
 BLOCKSIZE = 64
 BLOCKSIZES = (32, 64, 128, 256)
 DQ_GROUP = 256
+QUANT_TYPES = {"nf4": 0, "fp4": 1}     # nf4_quant_type: the level table
 
 STATUS_NAMES = {
     0: "NF4_OK", 1: "NF4_ERR_NULL", 2: "NF4_ERR_SHAPE", 3: "NF4_ERR_BLOCKSIZE", 4: "NF4_ERR_DTYPE",
     5: "NF4_ERR_ALIGN", 6: "NF4_ERR_WORKSPACE", 7: "NF4_ERR_UNSUPPORTED", 8: "NF4_ERR_HIP",
+    9: "NF4_ERR_QUANT_TYPE",
 }
 
-EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_thresholds", "nf4_sizes", "nf4_quantize",
+EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_levels", "nf4_thresholds", "nf4_sizes", "nf4_quantize",
            "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx", "nf4_matmul_fwd_lora",
            "nf4_matmul_bwd_dx_lora")
 LORA_RANK_STEP = 16
@@ -44,6 +46,7 @@ class QTensorStruct(ctypes.Structure):
         ("blocksize", ctypes.c_int32), ("double_quant", ctypes.c_int32),
         ("packed", ctypes.c_void_p), ("absmax", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
         ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p),
+        ("quant_type", ctypes.c_int32),
     ]
 
 
@@ -61,6 +64,7 @@ def lib() -> ctypes.CDLL:
         L.nf4_status_string.argtypes = [i32]
         L.nf4_status_string.restype = ctypes.c_char_p
         L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+        L.nf4_levels.argtypes = [i32, ctypes.POINTER(ctypes.c_float)]
         L.nf4_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.nf4_sizes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64), ctypes.POINTER(sz)]
@@ -111,13 +115,20 @@ def _require_device(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _quant_type_enum(quant_type: str) -> int:
+    if quant_type not in QUANT_TYPES:
+        raise ValueError(f"quant_type must be one of {tuple(QUANT_TYPES)} (got {quant_type!r})")
+    return QUANT_TYPES[quant_type]
+
+
 @dataclass
 class QTensor:
-    """An NF4-quantized weight [rows, cols] (the QuantState analogue).
+    """A 4-bit quantized weight [rows, cols] (the QuantState analogue).
 
     Device buffers: ``packed`` (uint8, ceil(numel/2)); without double
-    quantization ``absmax`` (fp32 per 64-block); with it ``absmax_q`` (int8 per
+    quantization ``absmax`` (fp32 per block); with it ``absmax_q`` (int8 per
     block), ``absmax_scale`` (fp32 per 256 blocks) and ``absmax_mean`` (fp32 [1]).
+    ``quant_type`` names the level table: "nf4" (default) or "fp4".
     """
     rows: int
     cols: int
@@ -128,6 +139,7 @@ class QTensor:
     absmax_scale: Optional[torch.Tensor] = None
     absmax_mean: Optional[torch.Tensor] = None
     blocksize: int = BLOCKSIZE
+    quant_type: str = "nf4"
 
     @property
     def shape(self):
@@ -140,7 +152,8 @@ class QTensor:
     def struct(self) -> QTensorStruct:
         return QTensorStruct(self.rows, self.cols, self.blocksize, int(self.double_quant),
                              _ptr(self.packed), _ptr(self.absmax), _ptr(self.absmax_q),
-                             _ptr(self.absmax_scale), _ptr(self.absmax_mean))
+                             _ptr(self.absmax_scale), _ptr(self.absmax_mean),
+                             _quant_type_enum(self.quant_type))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in
@@ -152,6 +165,13 @@ class QTensor:
 def nf4_codebook() -> torch.Tensor:
     out = (ctypes.c_float * 16)()
     _check(lib().nf4_codebook(out), "nf4_codebook")
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def nf4_levels(quant_type: str = "nf4") -> torch.Tensor:
+    """The 16 levels of ``quant_type`` indexed by code (NF4 ascending; FP4 by E2M1 bit pattern)."""
+    out = (ctypes.c_float * 16)()
+    _check(lib().nf4_levels(_quant_type_enum(quant_type), out), "nf4_levels")
     return torch.tensor(list(out), dtype=torch.float32)
 
 
@@ -170,11 +190,12 @@ def nf4_sizes(rows: int, cols: int, blocksize: int = BLOCKSIZE, double_quant: bo
 
 
 def empty_qtensor(rows: int, cols: int, double_quant: bool = True, device="cuda",
-                  blocksize: int = BLOCKSIZE) -> QTensor:
+                  blocksize: int = BLOCKSIZE, quant_type: str = "nf4") -> QTensor:
+    _quant_type_enum(quant_type)
     s = nf4_sizes(rows, cols, blocksize, double_quant)
     dev = torch.device(device)
     q = QTensor(rows, cols, double_quant, torch.empty(s["packed_bytes"], dtype=torch.uint8, device=dev),
-                blocksize=blocksize)
+                blocksize=blocksize, quant_type=quant_type)
     if double_quant:
         q.absmax_q = torch.empty(s["nblocks"], dtype=torch.int8, device=dev)
         q.absmax_scale = torch.empty(s["ngroups"], dtype=torch.float32, device=dev)
@@ -186,13 +207,22 @@ def empty_qtensor(rows: int, cols: int, double_quant: bool = True, device="cuda"
 
 def nf4_quantize(W: torch.Tensor, blocksize: int = BLOCKSIZE, double_quant: bool = True,
                  out: Optional[QTensor] = None, workspace: Optional[torch.Tensor] = None,
-                 status: Optional[torch.Tensor] = None) -> QTensor:
-    """NF4-quantize a 2-D bf16/fp32 device tensor (row-major flattening)."""
+                 status: Optional[torch.Tensor] = None, quant_type: Optional[str] = None) -> QTensor:
+    """4-bit quantize a 2-D bf16/fp32 device tensor (row-major flattening).
+
+    ``quant_type`` is "nf4" (default) or "fp4"; with ``out`` it defaults to
+    ``out.quant_type`` and must agree with it.
+    """
     _require_device(W, "W")
     if W.dim() != 2:
         raise ValueError("W must be 2-D [rows, cols]")
     rows, cols = W.shape
-    q = out if out is not None else empty_qtensor(rows, cols, double_quant, W.device, blocksize)
+    if out is not None:
+        if quant_type is not None and quant_type != out.quant_type:
+            raise ValueError(f"quant_type {quant_type!r} does not match out.quant_type {out.quant_type!r}")
+        q = out
+    else:
+        q = empty_qtensor(rows, cols, double_quant, W.device, blocksize, quant_type or "nf4")
     s = nf4_sizes(rows, cols, blocksize, double_quant)
     if workspace is None and s["workspace_bytes"]:
         workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=W.device)

@@ -29,7 +29,7 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool DQ>
+template <bool DQ, bool FP4>
 __global__ __launch_bounds__(64 * kDqWaves) void dequantize_bf16_kernel(const uint8_t *__restrict__ packed,
                                                                         AbsmaxSrc src, int64_t n32,
                                                                         uint4 *__restrict__ out) {
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void dequantize_bf16_kernel(const ui
     uint4 o[kDqTiles][4];
 #pragma unroll
     for (int u = 0; u < kDqTiles; ++u) {
-      const Lut tab = make_lut(ahat_of(r[u], DQ, mu));
+      const Lut tab = make_lut<FP4>(ahat_of(r[u], DQ, mu));
       const uint32_t w[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -91,12 +91,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void dequantize_bf16_kernel(const ui
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool FP4>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ packed,
                                                          AbsmaxSrc src, int64_t numel,
                                                          void *__restrict__ out, int64_t start) {
   __shared__ float lv[16];
-  if (threadIdx.x < 16) lv[threadIdx.x] = level(threadIdx.x);
+  if (threadIdx.x < 16) lv[threadIdx.x] = lvl<FP4>(threadIdx.x);
   __syncthreads();
   const float mu = src.dq ? *src.mean : 0.f;
   const int64_t n8 = numel / 8;
@@ -145,13 +145,15 @@ hipError_t launch_dequantize(const uint8_t *packed, const AbsmaxSrc &src, int64_
       const int64_t per_wg = 64 * kDqTiles * kDqWaves;   // 16-byte code chunks per workgroup and iteration
       int64_t grid = (n32 + per_wg - 1) / per_wg;
       if (grid > 65536) grid = 65536;
-      auto kern = src.dq ? dequantize_bf16_kernel<true> : dequantize_bf16_kernel<false>;
+      auto kern = src.qt ? (src.dq ? dequantize_bf16_kernel<true, true> : dequantize_bf16_kernel<false, true>)
+                         : (src.dq ? dequantize_bf16_kernel<true, false> : dequantize_bf16_kernel<false, false>);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kDqWaves), 0, stream, packed, src, n32,
                          reinterpret_cast<uint4 *>(out));
     }
     if (numel % 32) {
       const int64_t done = n32 * 32;
-      hipLaunchKernelGGL((dequantize_kernel<true>), dim3(1), dim3(256), 0, stream, packed, src, numel, out, done);
+      auto tail = src.qt ? dequantize_kernel<true, true> : dequantize_kernel<true, false>;
+      hipLaunchKernelGGL(tail, dim3(1), dim3(256), 0, stream, packed, src, numel, out, done);
     }
     return hipGetLastError();
   }
@@ -159,7 +161,8 @@ hipError_t launch_dequantize(const uint8_t *packed, const AbsmaxSrc &src, int64_
   int64_t grid = (n8 + 255) / 256;
   if (grid > 16384) grid = 16384;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((dequantize_kernel<false>), dim3((unsigned)grid), dim3(256), 0, stream, packed, src, numel, out,
+  auto kern = src.qt ? dequantize_kernel<false, true> : dequantize_kernel<false, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, packed, src, numel, out,
                      (int64_t)0);
   return hipGetLastError();
 }

@@ -57,7 +57,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_k, int &
   tk = in_group / gsize;
 }
 
-template <bool DX_BF16, bool LR>
+template <bool DX_BF16, bool LR, bool FP4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_generic_kernel(const uint16_t *__restrict__ dY, int64_t M,
                                                      int64_t N, int64_t K,
                                                      const uint8_t *__restrict__ packed,
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   {
     const uint32_t c0[4] = {creg[0].x, creg[0].y, creg[0].z, creg[0].w};
     const uint32_t c1[4] = {creg[1].x, creg[1].y, creg[1].z, creg[1].w};
-    const Lut t0 = make_lut(cok[0] ? ahat_of(rreg[0], src.dq, mu) : 0.f);
-    const Lut t1 = make_lut(cok[1] ? ahat_of(rreg[1], src.dq, mu) : 0.f);
+    const Lut t0 = make_lut<FP4>(cok[0] ? ahat_of(rreg[0], src.dq, mu) : 0.f);
+    const Lut t1 = make_lut<FP4>(cok[1] ? ahat_of(rreg[1], src.dq, mu) : 0.f);
 #pragma unroll
     for (int j = 0; j < 4; ++j) store_b_part(0, j, c0, c1, t0, t1);
   }
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (s + 2 < nsteps) load_b(s + 2);
     Lut t0, t1;
     if (more) {
-      t0 = make_lut(ok0 ? ahat_of(r0, src.dq, mu) : 0.f);
-      t1 = make_lut(ok1 ? ahat_of(r1, src.dq, mu) : 0.f);
+      t0 = make_lut<FP4>(ok0 ? ahat_of(r0, src.dq, mu) : 0.f);
+      t1 = make_lut<FP4>(ok1 ? ahat_of(r1, src.dq, mu) : 0.f);
     }
     const uint8_t *abase = &sa[cur][(128 * wm + bl) * ROWB + kg * 64];
     const uint8_t *bbase = &sb[cur][(128 * wk + bl) * ROWB + kg * 64];
@@ -335,14 +335,15 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const T *p) {
   return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
 }
 
+template <bool FP4>
 __device__ __forceinline__ void lut_quarter(float ahat, int q, Lut &t) {
-  const uint32_t p0 = pack_bf16x2(__fmul_rn(level(4 * q), ahat), __fmul_rn(level(4 * q + 1), ahat));
-  const uint32_t p1 = pack_bf16x2(__fmul_rn(level(4 * q + 2), ahat), __fmul_rn(level(4 * q + 3), ahat));
+  const uint32_t p0 = pack_bf16x2(__fmul_rn(lvl<FP4>(4 * q), ahat), __fmul_rn(lvl<FP4>(4 * q + 1), ahat));
+  const uint32_t p1 = pack_bf16x2(__fmul_rn(lvl<FP4>(4 * q + 2), ahat), __fmul_rn(lvl<FP4>(4 * q + 3), ahat));
   t.lo[q] = perm(p1, p0, 0x06040200u);
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
 
-template <bool DX_BF16, bool DQ, bool LR, bool GBS>
+template <bool DX_BF16, bool DQ, bool LR, bool GBS, bool FP4>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dx_kernel(
     const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ dX, int tiles_m, int tiles_k) {
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     Lut t;
     const float ah = ahat_at(0, c0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lut_quarter(ah, q, t);
+    for (int q = 0; q < 4; ++q) lut_quarter<FP4>(ah, q, t);
     const uint32_t wd[4] = {c0.w.x, c0.w.y, c0.w.z, c0.w.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -565,12 +566,12 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
       // dequantization of the next step's weight row
       if (r == 0) {
         ahn = ahat_at(s + 1, cn);
-        lut_quarter(ahn, 0, t);
-        lut_quarter(ahn, 1, t);
+        lut_quarter<FP4>(ahn, 0, t);
+        lut_quarter<FP4>(ahn, 1, t);
       }
       if (r == 1) {
-        lut_quarter(ahn, 2, t);
-        lut_quarter(ahn, 3, t);
+        lut_quarter<FP4>(ahn, 2, t);
+        lut_quarter<FP4>(ahn, 3, t);
       }
       if (r >= 2 && r <= 13) {
         const int c = (r - 2) / 3, ph = (r - 2) % 3;
@@ -643,27 +644,32 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
     using namespace tr_kernel;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
-#define NF4_BWD(GBS)                                                                                          \
-    {bwd_dx_kernel<false, false, false, GBS>, bwd_dx_kernel<false, false, true, GBS>,                          \
-     bwd_dx_kernel<false, true, false, GBS>,  bwd_dx_kernel<false, true, true, GBS>,                           \
-     bwd_dx_kernel<true, false, false, GBS>,  bwd_dx_kernel<true, false, true, GBS>,                           \
-     bwd_dx_kernel<true, true, false, GBS>,   bwd_dx_kernel<true, true, true, GBS>}
-    static const K_t kern[2][8] = {NF4_BWD(false), NF4_BWD(true)};
+#define NF4_BWD(GBS, FP4)                                                                                     \
+    {bwd_dx_kernel<false, false, false, GBS, FP4>, bwd_dx_kernel<false, false, true, GBS, FP4>,                \
+     bwd_dx_kernel<false, true, false, GBS, FP4>,  bwd_dx_kernel<false, true, true, GBS, FP4>,                 \
+     bwd_dx_kernel<true, false, false, GBS, FP4>,  bwd_dx_kernel<true, false, true, GBS, FP4>,                 \
+     bwd_dx_kernel<true, true, false, GBS, FP4>,   bwd_dx_kernel<true, true, true, GBS, FP4>}
+    static const K_t kern[2][2][8] = {{NF4_BWD(false, false), NF4_BWD(true, false)},
+                                      {NF4_BWD(false, true), NF4_BWD(true, true)}};
 #undef NF4_BWD
     const int sel = (dx_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (has_lr ? 1 : 0);
     const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
     const dim3 g((unsigned)(tiles_m * tiles_k)), b(64 * NWAVE);
-    hipLaunchKernelGGL(kern[src.lbs != 6][sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
+    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs != 6][sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx,
+                       tiles_m, tiles_k);
   } else {
     using namespace generic;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
-    static const K_t kern[4] = {bwd_dx_generic_kernel<false, false>, bwd_dx_generic_kernel<false, true>,
-                                bwd_dx_generic_kernel<true, false>, bwd_dx_generic_kernel<true, true>};
+    static const K_t kern[2][4] = {
+        {bwd_dx_generic_kernel<false, false, false>, bwd_dx_generic_kernel<false, true, false>,
+         bwd_dx_generic_kernel<true, false, false>, bwd_dx_generic_kernel<true, true, false>},
+        {bwd_dx_generic_kernel<false, false, true>, bwd_dx_generic_kernel<false, true, true>,
+         bwd_dx_generic_kernel<true, false, true>, bwd_dx_generic_kernel<true, true, true>}};
     const int sel = (dx_is_bf16 ? 2 : 0) | (has_lr ? 1 : 0);
     const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
     const dim3 g((unsigned)(tiles_m * tiles_k)), b(256);
-    hipLaunchKernelGGL(kern[sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
+    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx, tiles_m, tiles_k);
   }
   return hipGetLastError();
 }

@@ -40,7 +40,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kSmallCols = 16;
 constexpr int kSmallWaves = 8;
 
-template <bool Y_BF16, bool DQ, bool LR, bool BS32>
+template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     const uint16_t *__restrict__ X, int M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ Y) {
@@ -140,9 +140,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     // MFMAs add exact zeros; no branch, so no load is sunk into one)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const Lut t = make_lut(ok[u] ? ahat_of(r[u], DQ, mu) : 0.f);
+      const Lut t = make_lut<FP4>(ok[u] ? ahat_of(r[u], DQ, mu) : 0.f);
       Lut t2;
-      if (BS32) t2 = make_lut(ok[u] ? ahat_of(r2[u], DQ, mu) : 0.f);
+      if (BS32) t2 = make_lut<FP4>(ok[u] ? ahat_of(r2[u], DQ, mu) : 0.f);
       const uint32_t words[8] = {c[u][0].x, c[u][0].y, c[u][0].z, c[u][0].w,
                                  c[u][1].x, c[u][1].y, c[u][1].z, c[u][1].w};
 #pragma unroll
@@ -259,9 +259,10 @@ __device__ __forceinline__ void mfma2(f32x16 &c0, f32x16 &c1, const uint4 &a0, c
 
 // Entries 4q .. 4q+3 of the LUT of bf16(level_i * a^) (one quarter, so that
 // the work can be spread between MFMAs).
+template <bool FP4>
 __device__ __forceinline__ void make_lut_quarter(float ahat, int q, Lut &t) {
-  const uint32_t p0 = pack_bf16x2(__fmul_rn(level(4 * q), ahat), __fmul_rn(level(4 * q + 1), ahat));
-  const uint32_t p1 = pack_bf16x2(__fmul_rn(level(4 * q + 2), ahat), __fmul_rn(level(4 * q + 3), ahat));
+  const uint32_t p0 = pack_bf16x2(__fmul_rn(lvl<FP4>(4 * q), ahat), __fmul_rn(lvl<FP4>(4 * q + 1), ahat));
+  const uint32_t p1 = pack_bf16x2(__fmul_rn(lvl<FP4>(4 * q + 2), ahat), __fmul_rn(lvl<FP4>(4 * q + 3), ahat));
   t.lo[q] = perm(p1, p0, 0x06040200u);
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
@@ -285,7 +286,7 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <bool Y_BF16, bool DQ, bool LR, bool GBS>
+template <bool Y_BF16, bool DQ, bool LR, bool GBS, bool FP4>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_large_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ Y, int tiles_m, int tiles_n) {
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     cw = c0.w;
     const float ah = ahat_at(0, c0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) make_lut_quarter(ah, q, lut);
+    for (int q = 0; q < 4; ++q) make_lut_quarter<FP4>(ah, q, lut);
     Sel4 sa, sb;
     select8(cw.x, sa, sb);
     lookup4(sa, lut, bb0[0], bb0[1]);
@@ -453,9 +454,9 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     issue_x1(rsl, ld, 2);
     lookup4(sb, lut, p0[2], p0[3]);
-    make_lut_quarter(ahn, 0, lut);
-    make_lut_quarter(ahn, 1, lut);
-    make_lut_quarter(ahn, 2, lut);
+    make_lut_quarter<FP4>(ahn, 0, lut);
+    make_lut_quarter<FP4>(ahn, 1, lut);
+    make_lut_quarter<FP4>(ahn, 2, lut);
     interleave<8, 1, 5, 8>();
     sched_cut();
     // slice 3, first half
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int i = 0; i < 4; ++i)
       acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
     issue_x1(rsl, ld, 3);
-    make_lut_quarter(ahn, 3, lut);
+    make_lut_quarter<FP4>(ahn, 3, lut);
     cw = cn.w;
     select8(cw.x, sa, sb);
     interleave<4, 0, 5, 4>();
@@ -541,28 +542,31 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
   const int sel = (y_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (lr.r > 0 ? 1 : 0);
   if (M <= 16) {
     using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *);
-#define NF4_SMALL(BS32)                                                                                       \
-    {fwd_small_kernel<false, false, false, BS32>, fwd_small_kernel<false, false, true, BS32>,                  \
-     fwd_small_kernel<false, true, false, BS32>,  fwd_small_kernel<false, true, true, BS32>,                   \
-     fwd_small_kernel<true, false, false, BS32>,  fwd_small_kernel<true, false, true, BS32>,                   \
-     fwd_small_kernel<true, true, false, BS32>,   fwd_small_kernel<true, true, true, BS32>}
-    static const K_t kern[2][8] = {NF4_SMALL(false), NF4_SMALL(true)};
+#define NF4_SMALL(BS32, FP4)                                                                                  \
+    {fwd_small_kernel<false, false, false, BS32, FP4>, fwd_small_kernel<false, false, true, BS32, FP4>,        \
+     fwd_small_kernel<false, true, false, BS32, FP4>,  fwd_small_kernel<false, true, true, BS32, FP4>,         \
+     fwd_small_kernel<true, false, false, BS32, FP4>,  fwd_small_kernel<true, false, true, BS32, FP4>,         \
+     fwd_small_kernel<true, true, false, BS32, FP4>,   fwd_small_kernel<true, true, true, BS32, FP4>}
+    static const K_t kern[2][2][8] = {{NF4_SMALL(false, false), NF4_SMALL(true, false)},
+                                      {NF4_SMALL(false, true), NF4_SMALL(true, true)}};
 #undef NF4_SMALL
     const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols)), b(64 * kSmallWaves);
-    hipLaunchKernelGGL(kern[src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr, y);
+    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr, y);
   } else {
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
-#define NF4_LARGE(GBS)                                                                                        \
-    {fwd_large_kernel<false, false, false, GBS>, fwd_large_kernel<false, false, true, GBS>,                    \
-     fwd_large_kernel<false, true, false, GBS>,  fwd_large_kernel<false, true, true, GBS>,                     \
-     fwd_large_kernel<true, false, false, GBS>,  fwd_large_kernel<true, false, true, GBS>,                     \
-     fwd_large_kernel<true, true, false, GBS>,   fwd_large_kernel<true, true, true, GBS>}
-    static const K_t kern[2][8] = {NF4_LARGE(false), NF4_LARGE(true)};
+#define NF4_LARGE(GBS, FP4)                                                                                   \
+    {fwd_large_kernel<false, false, false, GBS, FP4>, fwd_large_kernel<false, false, true, GBS, FP4>,          \
+     fwd_large_kernel<false, true, false, GBS, FP4>,  fwd_large_kernel<false, true, true, GBS, FP4>,           \
+     fwd_large_kernel<true, false, false, GBS, FP4>,  fwd_large_kernel<true, false, true, GBS, FP4>,           \
+     fwd_large_kernel<true, true, false, GBS, FP4>,   fwd_large_kernel<true, true, true, GBS, FP4>}
+    static const K_t kern[2][2][8] = {{NF4_LARGE(false, false), NF4_LARGE(true, false)},
+                                      {NF4_LARGE(false, true), NF4_LARGE(true, true)}};
 #undef NF4_LARGE
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 g((unsigned)(tiles_m * tiles_n)), b(64 * NWAVE);
-    hipLaunchKernelGGL(kern[src.lbs != 6][sel], g, b, 0, stream, X, M, N, K, packed, src, lr, y, tiles_m, tiles_n);
+    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs != 6][sel], g, b, 0, stream, X, M, N, K, packed, src, lr, y,
+                       tiles_m, tiles_n);
   }
   return hipGetLastError();
 }

@@ -32,6 +32,7 @@ int check_qtensor(const nf4_qtensor *q) {
   int st = check_shape(q->rows, q->cols);
   if (st) return st;
   if (q->double_quant != 0 && q->double_quant != 1) return NF4_ERR_UNSUPPORTED;
+  if (q->quant_type != NF4_QT_NF4 && q->quant_type != NF4_QT_FP4) return NF4_ERR_QUANT_TYPE;
   if (!q->packed) return NF4_ERR_NULL;
   if (!aligned16(q->packed)) return NF4_ERR_ALIGN;
   if (q->double_quant) {
@@ -53,6 +54,7 @@ nf4::AbsmaxSrc absmax_src(const nf4_qtensor *q) {
   s.mean = q->absmax_mean;
   s.dq = q->double_quant;
   s.lbs = log2_of(q->blocksize);
+  s.qt = q->quant_type == NF4_QT_FP4 ? 1 : 0;
   return s;
 }
 
@@ -73,6 +75,7 @@ const char *nf4_status_string(int status) {
     case NF4_ERR_WORKSPACE: return "workspace too small";
     case NF4_ERR_UNSUPPORTED: return "unsupported (e.g. GEMM needs cols % 64 == 0)";
     case NF4_ERR_HIP: return "HIP launch failed";
+    case NF4_ERR_QUANT_TYPE: return "quant_type must be NF4_QT_NF4 or NF4_QT_FP4";
     default: return "unknown status";
   }
 }
@@ -80,6 +83,13 @@ const char *nf4_status_string(int status) {
 int nf4_codebook(float *levels16) {
   if (!levels16) return NF4_ERR_NULL;
   for (int i = 0; i < 16; ++i) levels16[i] = nf4::level(i);
+  return NF4_OK;
+}
+
+int nf4_levels(int quant_type, float *levels16) {
+  if (!levels16) return NF4_ERR_NULL;
+  if (quant_type != NF4_QT_NF4 && quant_type != NF4_QT_FP4) return NF4_ERR_QUANT_TYPE;
+  for (int i = 0; i < 16; ++i) levels16[i] = quant_type == NF4_QT_FP4 ? nf4::fp4_level(i) : nf4::level(i);
   return NF4_OK;
 }
 
@@ -132,7 +142,8 @@ int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blo
     partials = reinterpret_cast<unsigned long long *>(workspace);
     absmax = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + nf4::absmax_ws_offset());
   }
-  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, log2_of(blocksize), out->packed, absmax,
+  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, log2_of(blocksize),
+                                         out->quant_type == NF4_QT_FP4, out->packed, absmax,
                                          partials, d_status, double_quant, out->absmax_q,
                                          out->absmax_scale, out->absmax_mean,
                                          reinterpret_cast<hipStream_t>(stream)));

@@ -37,6 +37,27 @@ constexpr uint32_t kThresholdBits[15] = {
 __host__ __device__ constexpr float level(int i) { return __builtin_bit_cast(float, kLevelBits[i]); }
 __host__ __device__ constexpr float threshold(int i) { return __builtin_bit_cast(float, kThresholdBits[i]); }
 
+// FP4 ("bitsandbytes" page, 4-bit training paragraph: FP4, standard
+// floating-point 4-bit): the E2M1 4-bit float.  A code is the format's own bit
+// pattern -- bit 3 the sign, bits 2-1 the exponent with bias 1 (field 0
+// subnormal), bit 0 the mantissa -- and its level is the value divided by 6,
+// the largest magnitude, rounded once to fp32 (the division by 6 of an exact
+// magnitude is one rounding).
+__host__ __device__ constexpr float fp4_level(int code) {
+  const int e = (code >> 1) & 3, m = code & 1;
+  const float mag = e == 0 ? 0.5f * (float)m : (float)(1 << (e - 1)) * (1.0f + 0.5f * (float)m);
+  return (code & 8) ? -(mag / 6.0f) : mag / 6.0f;
+}
+// Decision threshold between FP4 magnitudes i and i+1 (i = 0..6): the largest
+// fp32 value not above their exact midpoint, so that for every fp32 |n|,
+// |n| > t exactly when |n| lies above the midpoint (a tie goes to the smaller
+// magnitude, the lower code).
+__host__ __device__ constexpr float fp4_threshold(int i) {
+  const double mid = ((double)fp4_level(i) + (double)fp4_level(i + 1)) * 0.5;   // exact in fp64
+  const float t = (float)mid;
+  return (double)t > mid ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, t) - 1u) : t;
+}
+
 // ------------------------------------------------------------------ small helpers
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -80,7 +101,13 @@ struct AbsmaxSrc {
   const float *mean;          // one fp32
   int dq;
   int lbs;                    // log2 of the block size (5..8: 32..256 weights per block)
+  int qt;                     // level table: 0 NF4, 1 FP4 (the launchers pick the kernel instantiation)
 };
+
+// Level of code i in the NF4 or FP4 table (a compile-time choice: every kernel
+// that builds tables is instantiated for both, so each keeps its constants).
+template <bool FP4>
+__host__ __device__ constexpr float lvl(int i) { return FP4 ? fp4_level(i) : level(i); }
 
 __device__ __forceinline__ float block_ahat(const AbsmaxSrc &s, int64_t blk, float mu) {
   if (!s.dq) return s.absmax[blk];
@@ -207,11 +234,12 @@ struct Lut {
   uint32_t hi[4];
 };
 
+template <bool FP4>
 __device__ __forceinline__ Lut make_lut(float ahat) {
   uint32_t p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    p[j] = pack_bf16x2(__fmul_rn(level(2 * j), ahat), __fmul_rn(level(2 * j + 1), ahat));
+    p[j] = pack_bf16x2(__fmul_rn(lvl<FP4>(2 * j), ahat), __fmul_rn(lvl<FP4>(2 * j + 1), ahat));
   Lut t;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

@@ -23,8 +23,8 @@ inline size_t quant_workspace_bytes(int64_t nblocks) {
   return (b + 255) & ~(size_t)255;
 }
 
-// `lbs`: log2 of the block size (5..8).
-hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs, uint8_t *packed,
+// `lbs`: log2 of the block size (5..8); `fp4`: the FP4 level table instead of NF4's.
+hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs, bool fp4, uint8_t *packed,
                            float *absmax_out, unsigned long long *partials, uint32_t *status,
                            int dq, int8_t *q_out, float *scale_out, float *mean_out,
                            hipStream_t stream);

@@ -107,6 +107,27 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
   return word;
 }
 
+// FP4 code of a normalised value n: the magnitude index counts the
+// thresholds |n| lies above (a tie goes to the smaller magnitude, the lower
+// code), then the sign; zero of either sign takes code 0 (+0).
+__device__ __forceinline__ int fp4_code(float n) {
+  const float an = fabsf(n);
+  int mi = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) mi += an > fp4_threshold(i) ? 1 : 0;
+  return (n < 0.f && mi > 0) ? 8 + mi : mi;
+}
+
+// FP4 codes of eight values of one block with absmax bits `m` (finite,
+// non-zero): exact IEEE division, then the thresholds.
+__device__ __forceinline__ uint32_t encode8_fp4(const float x[8], uint32_t m) {
+  const float a = __uint_as_float(m);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= (uint32_t)fp4_code(x[i] / a) << (4 * i);
+  return word;
+}
+
 // LPB lanes per block (block size 8 * LPB: 32, 64, 128 or 256), eight
 // elements per lane.  Each lane's eight codes form one 32-bit word of the
 // packed output (element 2j in the low nibble of byte j).  With double quantization each workgroup also sums the significands
@@ -123,7 +144,7 @@ __device__ __forceinline__ void add_to_slots(unsigned long long *slot, int e, un
   if (bi) atomicAdd(&slot[wi + 2], (unsigned long long)(uint32_t)(v >> (64 - bi)));
 }
 
-template <bool BF16, bool DQ, int LPB>
+template <bool BF16, bool DQ, int LPB, bool FP4>
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     const void *__restrict__ w, int64_t nfull, uint8_t *__restrict__ packed,
     float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status) {
@@ -148,7 +169,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
   int64_t blk = (int64_t)blockIdx.x * BPI + slot;
   uint4 cu = make_uint4(0, 0, 0, 0), cv = cu;
   if (blk < nfull) load(blk, cu, cv);   // in flight while the level table is built
-  build_cells(cells);
+  if (!FP4) build_cells(cells);
   if (DQ) {
     lbuck[threadIdx.x] = 0ull;
     if (threadIdx.x < kMeanSlots) lslot[threadIdx.x] = 0ull;
@@ -179,14 +200,15 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 #pragma unroll
     for (int sh = 1; sh < LPB; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
 
+    constexpr uint32_t kZeroWord = FP4 ? 0u : 0x77777777u;   // every code the +0 level
     uint32_t word;
     if (m >= 0x7f800000u) {
       bad = true;
-      word = 0x77777777u;
+      word = kZeroWord;
     } else if (m == 0) {
-      word = 0x77777777u;  // all-zero block: every code is level 0.0
+      word = kZeroWord;  // all-zero block
     } else {
-      word = encode8(x, m, cells);
+      word = FP4 ? encode8_fp4(x, m) : encode8(x, m, cells);
     }
     *reinterpret_cast<uint32_t *>(packed + blk * (BS / 2) + part * 4) = word;
     if (part == 0) {
@@ -212,13 +234,13 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 
 // The partial block at the end (fewer than blocksize <= 256 elements): one
 // workgroup of 256 threads, one element per thread, exact division.
-template <bool BF16, bool DQ>
+template <bool BF16, bool DQ, bool FP4>
 __global__ __launch_bounds__(256) void quantize_tail_kernel(
     const void *__restrict__ w, int64_t numel, int64_t blk, int bs, uint8_t *__restrict__ packed,
     float *__restrict__ absmax, unsigned long long *__restrict__ partial_row, uint32_t *status) {
   __shared__ Cell cells[129];
   __shared__ uint32_t wmax[4];
-  build_cells(cells);
+  if (!FP4) build_cells(cells);
   const int t = threadIdx.x;
   const int64_t e = blk * bs + t;
   const bool valid = t < bs && e < numel;
@@ -235,10 +257,10 @@ __global__ __launch_bounds__(256) void quantize_tail_kernel(
   if ((t & 63) == 0) wmax[t >> 6] = m;
   __syncthreads();
   m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  int code = 7;
+  int code = FP4 ? 0 : 7;   // the +0 level
   if (m != 0 && m < 0x7f800000u) {
     bool unused = false;
-    code = classify(x / __uint_as_float(m), cells, unused);
+    code = FP4 ? fp4_code(x / __uint_as_float(m)) : classify(x / __uint_as_float(m), cells, unused);
   }
   if (!valid) code = 0;
   const int upper = __shfl_down(code, 1);
@@ -432,20 +454,28 @@ __global__ __launch_bounds__(64) void double_quant_kernel(const float *__restric
 }
 
 
-template <bool BF16, bool DQ>
-void launch_blocks(int lbs, dim3 g, hipStream_t stream, const void *w, int64_t nfull, uint8_t *packed,
-                   float *absmax_out, unsigned long long *partials, uint32_t *status) {
-  switch (lbs) {
-    case 5: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 4>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-    case 6: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 8>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-    case 7: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 16>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-    default: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 32>), g, dim3(256), 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+template <bool BF16, bool DQ, bool FP4>
+void launch_full(int lbs, int grid, int64_t numel, int64_t nfull, int bs, hipStream_t stream, const void *w,
+                 uint8_t *packed, float *absmax_out, unsigned long long *partials, uint32_t *status) {
+  if (nfull > 0) {
+    const dim3 g((unsigned)grid), b(256);
+    switch (lbs) {
+      case 5: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 4, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+      case 6: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 8, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+      case 7: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 16, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+      default: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 32, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
+    }
+  }
+  if (nfull * bs < numel) {   // the partial last block, with its own accumulator row
+    unsigned long long *row = partials ? partials + (int64_t)grid * kMeanSlots : nullptr;
+    hipLaunchKernelGGL((quantize_tail_kernel<BF16, DQ, FP4>), dim3(1), dim3(256), 0, stream, w, numel, nfull, bs,
+                       packed, absmax_out, row, status);
   }
 }
 
 }  // namespace
 
-hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs, uint8_t *packed,
+hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs, bool fp4, uint8_t *packed,
                            float *absmax_out, unsigned long long *partials, uint32_t *status,
                            int dq, int8_t *q_out, float *scale_out, float *mean_out,
                            hipStream_t stream) {
@@ -455,30 +485,18 @@ hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs,
   const int bpi = 256 / (bs / 8);   // blocks per quantize workgroup and iteration
   int grid = 0;
   if (nfull > 0) {
-    int64_t g64 = (nfull + bpi - 1) / bpi;
+    const int64_t g64 = (nfull + bpi - 1) / bpi;
     grid = (int)(g64 < kQuantGridMax ? g64 : kQuantGridMax);
-    const dim3 g((unsigned)grid);
-    if (w_is_bf16) {
-      if (dq) launch_blocks<true, true>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
-      else    launch_blocks<true, false>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
-    } else {
-      if (dq) launch_blocks<false, true>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
-      else    launch_blocks<false, false>(lbs, g, stream, w, nfull, packed, absmax_out, partials, status);
-    }
   }
-  int rows = grid;
-  if (nfull < nblocks) {
-    const dim3 g(1), b(256);
-    unsigned long long *row = partials ? partials + (int64_t)grid * kMeanSlots : nullptr;
-    if (w_is_bf16) {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<true, true>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<true, false>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
-    } else {
-      if (dq) hipLaunchKernelGGL((quantize_tail_kernel<false, true>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
-      else    hipLaunchKernelGGL((quantize_tail_kernel<false, false>), g, b, 0, stream, w, numel, nfull, bs, packed, absmax_out, row, status);
-    }
-    ++rows;
-  }
+  using L = void (*)(int, int, int64_t, int64_t, int, hipStream_t, const void *, uint8_t *, float *,
+                     unsigned long long *, uint32_t *);
+  static const L full[2][2][2] = {{{launch_full<false, false, false>, launch_full<false, false, true>},
+                                   {launch_full<false, true, false>, launch_full<false, true, true>}},
+                                  {{launch_full<true, false, false>, launch_full<true, false, true>},
+                                   {launch_full<true, true, false>, launch_full<true, true, true>}}};
+  full[w_is_bf16 ? 1 : 0][dq ? 1 : 0][fp4 ? 1 : 0](lbs, grid, numel, nfull, bs, stream, w, packed, absmax_out,
+                                                   partials, status);
+  const int rows = grid + (nfull < nblocks ? 1 : 0);
   if (dq) {
     hipLaunchKernelGGL(mean_reduce_kernel, dim3(1), dim3(kMeanThreads), 0, stream, partials, rows, (uint32_t)nblocks,
                        mean_out);

@@ -10,9 +10,11 @@ Files are safetensors (no code is executed on load).  Each weight ``name``
 stores ``name.packed`` (uint8), ``name.absmax_q`` (int8), ``name.absmax_scale``
 (fp32) and ``name.absmax_mean`` (fp32 [1]), or ``name.absmax`` (fp32) without
 double quantization; the file metadata records, per weight, rows, cols, block
-size and double quantization, and once the bit patterns of the 16 NF4 levels
-the codes index.  Loading checks every buffer size against the shape and
-refuses a file written with another level table.  The round trip is bit-exact.
+size, double quantization and the 4-bit data type (NF4 or FP4; the same
+paragraph has the data type travel with the state), and once the bit
+patterns of both 16-level tables the codes index.  Loading checks every
+buffer size against the shape and refuses a file written with another level
+table.  The round trip is bit-exact.
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ from typing import Dict
 
 import torch
 
-from ._lib import BLOCKSIZES, QTensor, nf4_codebook, nf4_sizes
+from ._lib import BLOCKSIZES, QUANT_TYPES, QTensor, nf4_levels, nf4_sizes
 
 FORMAT = "nf4-qtensor"
 VERSION = "1"
@@ -30,8 +32,8 @@ _DTYPES = {"packed": torch.uint8, "absmax": torch.float32, "absmax_q": torch.int
            "absmax_scale": torch.float32, "absmax_mean": torch.float32}
 
 
-def _codebook_hex() -> str:
-    return "".join(f"{b & 0xFFFFFFFF:08x}" for b in nf4_codebook().view(torch.int32).tolist())
+def _codebook_hex(quant_type: str = "nf4") -> str:
+    return "".join(f"{b & 0xFFFFFFFF:08x}" for b in nf4_levels(quant_type).view(torch.int32).tolist())
 
 
 def _expected_sizes(rows: int, cols: int, blocksize: int, dq: bool) -> Dict[str, int]:
@@ -50,7 +52,7 @@ def qtensor_state(name: str, q: QTensor) -> tuple[Dict[str, torch.Tensor], Dict[
         if t is not None:
             tensors[f"{name}.{f}"] = t.detach().to("cpu").contiguous()
     meta = {name: {"rows": q.rows, "cols": q.cols, "blocksize": q.blocksize,
-                   "double_quant": bool(q.double_quant)}}
+                   "double_quant": bool(q.double_quant), "quant_type": q.quant_type}}
     return tensors, meta
 
 
@@ -65,8 +67,8 @@ def save_qtensors(path: str, weights: Dict[str, QTensor]) -> None:
         t, m = qtensor_state(name, q)
         tensors.update(t)
         entries.update(m)
-    meta = {"format": FORMAT, "version": VERSION, "levels": _codebook_hex(),
-            "weights": json.dumps(entries)}
+    meta = {"format": FORMAT, "version": VERSION, "levels": _codebook_hex("nf4"),
+            "levels_fp4": _codebook_hex("fp4"), "weights": json.dumps(entries)}
     save_file(tensors, path, metadata=meta)
 
 
@@ -82,7 +84,7 @@ def load_qtensors(path: str, device="cpu") -> Dict[str, QTensor]:
         meta = f.metadata() or {}
         if meta.get("format") != FORMAT or meta.get("version") != VERSION:
             raise ValueError(f"{path}: not an {FORMAT} v{VERSION} file")
-        if meta.get("levels") != _codebook_hex():
+        if meta.get("levels") != _codebook_hex("nf4"):
             raise ValueError(f"{path}: written with a different NF4 level table")
         entries = json.loads(meta["weights"])
         keys = set(f.keys())
@@ -90,6 +92,11 @@ def load_qtensors(path: str, device="cpu") -> Dict[str, QTensor]:
             rows, cols, bs, dq = int(e["rows"]), int(e["cols"]), int(e["blocksize"]), bool(e["double_quant"])
             if bs not in BLOCKSIZES:
                 raise ValueError(f"{path}: {name} has block size {bs}; supported: {BLOCKSIZES}")
+            qt = e.get("quant_type", "nf4")
+            if qt not in QUANT_TYPES:
+                raise ValueError(f"{path}: {name} has quant_type {qt!r}; supported: {tuple(QUANT_TYPES)}")
+            if qt == "fp4" and meta.get("levels_fp4") != _codebook_hex("fp4"):
+                raise ValueError(f"{path}: written with a different FP4 level table")
             want = _expected_sizes(rows, cols, bs, dq)
             bufs = {}
             for fld, n in want.items():
@@ -100,7 +107,7 @@ def load_qtensors(path: str, device="cpu") -> Dict[str, QTensor]:
                 if t.dtype != _DTYPES[fld] or t.dim() != 1 or t.numel() != n:
                     raise ValueError(f"{path}: {key} is {t.dtype} {tuple(t.shape)}, expected {_DTYPES[fld]} ({n},)")
                 bufs[fld] = t.to(device)
-            out[name] = QTensor(rows, cols, dq, blocksize=bs, **bufs)
+            out[name] = QTensor(rows, cols, dq, blocksize=bs, quant_type=qt, **bufs)
     return out
 
 

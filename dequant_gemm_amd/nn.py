@@ -88,8 +88,8 @@ class NF4Linear(torch.nn.Module):
 
     @classmethod
     def from_weight(cls, weight: torch.Tensor, double_quant: bool = True,
-                    out_dtype: torch.dtype = torch.bfloat16) -> "NF4Linear":
-        """Quantizes a [out_features, in_features] bf16/fp32 device weight."""
+                    out_dtype: torch.dtype = torch.bfloat16, quant_type: str = "nf4") -> "NF4Linear":
+        """Quantizes a [out_features, in_features] bf16/fp32 device weight (NF4, or FP4)."""
         if weight.dtype not in (torch.bfloat16, torch.float32):
             raise TypeError("weight must be bfloat16 or float32")
         if weight.dim() != 2:
@@ -97,21 +97,22 @@ class NF4Linear(torch.nn.Module):
         w = weight.detach()
         if not w.is_contiguous():
             w = w.contiguous()
-        return cls(nf4_quantize(w, double_quant=double_quant), out_dtype)
+        return cls(nf4_quantize(w, double_quant=double_quant, quant_type=quant_type), out_dtype)
 
     @classmethod
     def from_linear(cls, linear: torch.nn.Linear, double_quant: bool = True,
-                    out_dtype: torch.dtype = torch.bfloat16) -> "NF4Linear":
+                    out_dtype: torch.dtype = torch.bfloat16, quant_type: str = "nf4") -> "NF4Linear":
         if linear.bias is not None:
             raise ValueError("NF4Linear has no bias; the layer to convert has one")
-        return cls.from_weight(linear.weight, double_quant, out_dtype)
+        return cls.from_weight(linear.weight, double_quant, out_dtype, quant_type)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return nf4_linear(x, self.qweight, self.out_dtype)
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"double_quant={self.qweight.double_quant}, out_dtype={self.out_dtype}")
+                f"quant_type={self.qweight.quant_type}, double_quant={self.qweight.double_quant}, "
+                f"out_dtype={self.out_dtype}")
 
 
 class _NF4LoraMatmul(torch.autograd.Function):
@@ -183,10 +184,11 @@ class NF4LoraLinear(torch.nn.Module):
 
     @classmethod
     def from_weight(cls, weight: torch.Tensor, r: int, alpha: float = None, double_quant: bool = True,
-                    out_dtype: torch.dtype = torch.bfloat16, seed: int = 0) -> "NF4LoraLinear":
+                    out_dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+                    quant_type: str = "nf4") -> "NF4LoraLinear":
         w = weight.detach()
-        return cls(nf4_quantize(w if w.is_contiguous() else w.contiguous(), double_quant=double_quant),
-                   r, alpha, out_dtype, seed)
+        return cls(nf4_quantize(w if w.is_contiguous() else w.contiguous(), double_quant=double_quant,
+                                quant_type=quant_type), r, alpha, out_dtype, seed)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.dtype != torch.bfloat16:
@@ -202,15 +204,16 @@ class NF4LoraLinear(torch.nn.Module):
 
 def quantize_linears(module: torch.nn.Module, double_quant: bool = True,
                      out_dtype: torch.dtype = torch.bfloat16,
-                     skip: Optional[set] = None) -> torch.nn.Module:
+                     skip: Optional[set] = None, quant_type: str = "nf4") -> torch.nn.Module:
     """Replaces every bias-free ``nn.Linear`` below ``module`` by an NF4Linear, in place.
 
-    ``skip`` holds qualified child names to leave dense.  Returns ``module``.
+    ``skip`` holds qualified child names to leave dense; ``quant_type`` is "nf4"
+    or "fp4".  Returns ``module``.
     """
     skip = skip or set()
     for name, child in list(module.named_modules()):
         for cname, c in list(child.named_children()):
             full = f"{name}.{cname}" if name else cname
             if isinstance(c, torch.nn.Linear) and c.bias is None and full not in skip:
-                setattr(child, cname, NF4Linear.from_linear(c, double_quant, out_dtype))
+                setattr(child, cname, NF4Linear.from_linear(c, double_quant, out_dtype, quant_type))
     return module

@@ -20,15 +20,22 @@
  *    scales are dequantized first, then used to dequantize the weights.
  *    Quantized-GEMM paragraph: weights dequantized on the fly, float32
  *    multiply, float32 outputs.  QuantState paragraph: the quantized data,
- *    absmax and shape travel together (here: nf4_qtensor).
+ *    absmax, data type and shape travel together (here: nf4_qtensor).
+ *    4-bit training paragraph: the 4-bit data type is NF4 or FP4, standard
+ *    floating-point 4-bit (quant_type NF4_QT_FP4 here).
  *
  * Exact semantics (the readings where the pages are silent):
  *  - weight W is logical [rows, cols] row-major, flattened e = r*cols + c;
  *    with B weights per block (64 by default; 32, 128 or 256), block b holds
  *    elements Bb .. Bb+B-1 (the last block may be partial);
  *  - a_b = max|x| over the block (fp32); n = fp32(x / a_b) (IEEE division);
- *    code = index of the nearest NF4 level, ties to the lower index; an
- *    all-zero block codes every element 7 (the level 0.0);
+ *    code = index of the nearest level, ties to the lower index; an all-zero
+ *    block codes every element as the +0 level (NF4 code 7, FP4 code 0);
+ *  - NF4 levels ascend with the code (nf4_codebook).  FP4 codes are the bit
+ *    patterns of the E2M1 4-bit float (bit 3 the sign, bits 2-1 the exponent
+ *    with bias 1, bit 0 the mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+ *    and a level is the value over 6, rounded once to fp32; ties to the lower
+ *    code then go toward zero, and zero takes code 0;
  *  - packed byte j = code[2j] | code[2j+1] << 4 (odd count: high nibble 0);
  *  - double quantization: mu = exact mean of all a_b rounded once to fp32;
  *    a'_b = fp32(a_b - mu); per group of 256 consecutive blocks
@@ -77,12 +84,19 @@ enum nf4_status {
   NF4_ERR_ALIGN = 5,        /* a device pointer is not 16-byte aligned */
   NF4_ERR_WORKSPACE = 6,    /* workspace smaller than nf4_sizes reports */
   NF4_ERR_UNSUPPORTED = 7,  /* valid but not supported, e.g. a GEMM with cols % 64 != 0 */
-  NF4_ERR_HIP = 8           /* a HIP launch failed */
+  NF4_ERR_HIP = 8,          /* a HIP launch failed */
+  NF4_ERR_QUANT_TYPE = 9    /* unknown nf4_quant_type value */
 };
 
 enum nf4_dtype {
   NF4_F32 = 0,
   NF4_BF16 = 1
+};
+
+/* The 4-bit data type of a quantized weight: its level table. */
+enum nf4_quant_type {
+  NF4_QT_NF4 = 0,   /* the NF4 levels (default) */
+  NF4_QT_FP4 = 1    /* E2M1 values over 6 */
 };
 
 /* Largest element count a quantized tensor may hold (2^36; a weight that size
@@ -113,6 +127,9 @@ enum nf4_dtype {
  *   absmax_q      nblocks int8     (double_quant == 1)
  *   absmax_scale  ngroups fp32     (double_quant == 1)
  *   absmax_mean   1 fp32           (double_quant == 1)
+ * quant_type (an nf4_quant_type) names the level table; every call that
+ * reads the struct rejects other values with NF4_ERR_QUANT_TYPE.  It is the
+ * last field so that a zero-initialised tail means NF4.
  * The struct is read during a call only; the library keeps no pointer to it.
  */
 typedef struct nf4_qtensor {
@@ -125,6 +142,7 @@ typedef struct nf4_qtensor {
   int8_t *absmax_q;
   float *absmax_scale;
   float *absmax_mean;
+  int32_t quant_type;
 } nf4_qtensor;
 
 /* A short English description of a status code (static storage). */
@@ -138,6 +156,13 @@ const char *nf4_status_string(int status);
  * normalised by the largest, rounded once to fp32.
  */
 int nf4_codebook(float *levels16);
+
+/*
+ * Copies the 16 levels of `quant_type` (an nf4_quant_type), indexed by code,
+ * into host memory `levels16`: NF4 as nf4_codebook; FP4 c[0] = +0 .. c[7] = 1
+ * and c[8 + i] = -c[i].  Errors: NF4_ERR_NULL, NF4_ERR_QUANT_TYPE.
+ */
+int nf4_levels(int quant_type, float *levels16);
 
 /*
  * Copies into host memory `thresholds15` the 15 decision thresholds the
@@ -161,7 +186,8 @@ int nf4_sizes(int64_t rows, int64_t cols, int blocksize, int double_quant,
 /*
  * Quantizes W (device, [rows, cols] row-major, dtype w_dtype = NF4_F32 or
  * NF4_BF16) into `out`, whose rows/cols/blocksize/double_quant must match the
- * arguments and whose buffers are sized per nf4_sizes.  "Zenbit" page,
+ * arguments and whose buffers are sized per nf4_sizes; out->quant_type picks
+ * the level table (NF4 or FP4).  "Zenbit" page,
  * zenbit.nf4 bullet; "bitsandbytes" page, NF4 and double-quantization
  * paragraphs.  `workspace` (device, >= workspace_bytes from nf4_sizes, may be
  * NULL when that is 0) is scratch for the fp32 absmax and the exact-mean

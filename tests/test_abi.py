@@ -49,6 +49,35 @@ def test_codebook_matches_oracle_bit_for_bit(L):
     assert got.view(np.uint32).tolist() == O.codebook().view(np.uint32).tolist()
 
 
+def test_levels_of_both_types_match_oracle_bit_for_bit(L):
+    for qt, want in (("nf4", O.codebook()), ("fp4", O.fp4_codebook())):
+        got = dg.nf4_levels(qt).numpy()
+        assert got.view(np.uint32).tolist() == want.view(np.uint32).tolist(), qt
+    out = (ctypes.c_float * 16)()
+    assert L.nf4_levels(2, out) == 9 and L.nf4_levels(-1, out) == 9
+    assert L.nf4_levels(0, None) == 1
+
+
+def test_qtensor_struct_layout():
+    """quant_type is the last field: the earlier fields keep their offsets."""
+    S = dg.QTensorStruct
+    assert (S.rows.offset, S.cols.offset, S.blocksize.offset, S.double_quant.offset, S.packed.offset) == (0, 8, 16, 20, 24)
+    assert (S.absmax_mean.offset, S.quant_type.offset, ctypes.sizeof(S)) == (56, 64, 72)
+    assert _qt().quant_type == 0 and dg.QTensorStruct(1, 1, 64, 0).quant_type == 0   # zero tail = NF4
+
+
+def test_quant_type_is_checked_by_every_call(L):
+    ws = dg.nf4_sizes(64, 64, 64, True)["workspace_bytes"]
+    for bad in (2, -1, 7):
+        q = _qt(qt=bad)
+        assert L.nf4_quantize(P, 1, 64, 64, 64, 1, ctypes.byref(q), P, ws, None, None) == 9
+        assert L.nf4_dequantize(ctypes.byref(q), P, 1, None) == 9
+        assert L.nf4_matmul_fwd(P, 4, ctypes.byref(q), P, 0, None) == 9
+        assert L.nf4_matmul_bwd_dx(P, 4, ctypes.byref(q), P, 0, None) == 9
+    with pytest.raises(ValueError):
+        dg.empty_qtensor(4, 64, True, "cpu", 64, "int4")
+
+
 def test_thresholds_are_the_exact_decision_boundaries(L):
     """Each t_i is the smallest fp32 whose exact nearest level is i+1 (ties to the lower)."""
     c = O.codebook()
@@ -91,8 +120,8 @@ def _status(name, L):
 P = 1 << 20  # a fake, 16-byte aligned "device" address; never dereferenced on the error paths
 
 
-def _qt(rows=64, cols=64, dq=1, packed=P, absmax=P, q=P, scale=P, mean=P, bs=64):
-    return dg.QTensorStruct(rows, cols, bs, dq, packed, absmax, q, scale, mean)
+def _qt(rows=64, cols=64, dq=1, packed=P, absmax=P, q=P, scale=P, mean=P, bs=64, qt=0):
+    return dg.QTensorStruct(rows, cols, bs, dq, packed, absmax, q, scale, mean, qt)
 
 
 def test_sizes_errors(L):
@@ -163,7 +192,7 @@ def test_gemm_errors(L, fn):
 
 
 def test_status_strings(L):
-    for s in range(9):
+    for s in range(10):
         assert L.nf4_status_string(s)
     assert L.nf4_status_string(99) == b"unknown status"
 

@@ -16,10 +16,10 @@ from dequant_gemm_amd import QTensor
 from dequant_gemm_amd.io import load_qtensor, load_qtensors, save_qtensor, save_qtensors
 
 
-def _oracle_qtensor(rows, cols, dq, seed):
+def _oracle_qtensor(rows, cols, dq, seed, quant_type="nf4"):
     W = synth.normal((rows, cols), 0.02, seed, torch.float32)
-    qo = O.quantize(W.numpy(), double_quant_on=dq)
-    q = QTensor(rows, cols, dq, torch.from_numpy(qo["packed"].copy()))
+    qo = O.quantize(W.numpy(), double_quant_on=dq, quant_type=quant_type)
+    q = QTensor(rows, cols, dq, torch.from_numpy(qo["packed"].copy()), quant_type=quant_type)
     if dq:
         q.absmax_q = torch.from_numpy(qo["absmax_q"].astype(np.int8))
         q.absmax_scale = torch.from_numpy(qo["scale"].astype(np.float32))
@@ -30,7 +30,8 @@ def _oracle_qtensor(rows, cols, dq, seed):
 
 
 def _same(a: QTensor, b: QTensor):
-    assert (a.rows, a.cols, a.double_quant, a.blocksize) == (b.rows, b.cols, b.double_quant, b.blocksize)
+    assert (a.rows, a.cols, a.double_quant, a.blocksize, a.quant_type) == \
+        (b.rows, b.cols, b.double_quant, b.blocksize, b.quant_type)
     for f in ("packed", "absmax", "absmax_q", "absmax_scale", "absmax_mean"):
         x, y = getattr(a, f), getattr(b, f)
         assert (x is None) == (y is None), f
@@ -56,6 +57,48 @@ def test_several_weights_and_ragged(tmp_path):
     assert set(back) == set(ws)
     for k in ws:
         _same(ws[k], back[k])
+
+
+def test_fp4_weights_keep_their_data_type(tmp_path):
+    ws = {"a": _oracle_qtensor(64, 128, True, 5, "fp4"), "b": _oracle_qtensor(33, 65, False, 6, "fp4"),
+          "c": _oracle_qtensor(64, 64, True, 7, "nf4")}
+    p = str(tmp_path / "mixed.safetensors")
+    save_qtensors(p, ws)
+    back = load_qtensors(p)
+    for k in ws:
+        _same(ws[k], back[k])
+    assert [back[k].quant_type for k in ("a", "b", "c")] == ["fp4", "fp4", "nf4"]
+    bad = str(tmp_path / "bad.safetensors")
+
+    def other_fp4_levels(m):
+        m["levels_fp4"] = "0" * 128
+        return m
+    _rewrite(p, bad, meta_fn=other_fp4_levels)
+    with pytest.raises(ValueError, match="FP4 level table"):
+        load_qtensors(bad)
+
+    def unknown_type(m):
+        e = json.loads(m["weights"])
+        e["a"]["quant_type"] = "int4"
+        m["weights"] = json.dumps(e)
+        return m
+    _rewrite(p, bad, meta_fn=unknown_type)
+    with pytest.raises(ValueError, match="quant_type"):
+        load_qtensors(bad)
+
+
+def test_entries_without_a_data_type_load_as_nf4(tmp_path):
+    p = str(tmp_path / "old.safetensors")
+    save_qtensor(p, _oracle_qtensor(64, 64, True, 8))
+    bad = str(tmp_path / "noqt.safetensors")
+
+    def drop(m):
+        e = json.loads(m["weights"])
+        del e["weight"]["quant_type"]
+        m["weights"] = json.dumps(e)
+        return m
+    _rewrite(p, bad, meta_fn=drop)
+    assert load_qtensor(bad).quant_type == "nf4"
 
 
 def _rewrite(src, dst, tensors_fn=None, meta_fn=None):
