@@ -13,7 +13,7 @@ libnf4.so on torch's current stream, inputs and outputs resident in HBM.
 step time (quantization included in the time).  The same JSON line carries
 per-kernel timings (HIP events around every launch of the timed steps), the
 dequantizer, the rank-64 adapter variants of both GEMMs, the decode-shape
-forward (M = 1, 4, 16 on a rotating pool of 64 quantized 4096x4096 weights,
+forward (M = 1, 4, 16 on a rotating pool of 512 quantized 4096x4096 weights,
 replayed from a HIP graph so host launch overhead does not count), the
 outlier-heavy large shape (M = K = 8192, N = 28672, fp32 Student-t weight), the
 32-layer bulk quantize/dequantize round trip, the prefill workload at block sizes
@@ -208,16 +208,18 @@ def bench_prefill(dg, steps, warmup):
     return res
 
 
-def bench_decode(dg, pool=64, reps=20):
+def bench_decode(dg, pool=512, reps=10):
     import synth
     d = torch.device("cuda:0")
     K, N = synth.DECODE_K, synth.DECODE_N
-    # a pool of 64 independently seeded quantized weights (554 MB, more than
-    # twice the 256 MB last-level cache), rotated call by call
+    # a pool of 512 independently seeded quantized weights (4.4 GB, 17x the 256 MB
+    # last-level cache), N(0, 0.02) drawn on the device with seed 1000 + p, rotated
+    # call by call.  The kernel's code loads are non-temporal; under a cyclic pool
+    # they leave part of the last-level cache holding earlier weights, so the pool
+    # is large enough that such hits are a few percent of the bytes.
     qs = []
-    for lo in range(0, pool, 16):
-        for Wp in synth.parallel(synth.decode_weight, range(lo, min(pool, lo + 16))):
-            qs.append(dg.nf4_quantize(Wp.to(d)))
+    for p in range(pool):
+        qs.append(dg.nf4_quantize(_device_normal((N, K), 0.02, 1000 + p, d)))
     torch.cuda.synchronize()
     out = {}
     for M in synth.DECODE_MS:
@@ -239,7 +241,7 @@ def bench_decode(dg, pool=64, reps=20):
                                "TFLOP/s": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
         del g
     # Context: the per-call floor of this measurement -- a one-element kernel replayed
-    # the same way (64 launches per graph).  No kernel can take less per call here.
+    # the same way (one launch per pool entry).  No kernel can take less per call here.
     t = torch.zeros(1, device=d)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -248,7 +250,7 @@ def bench_decode(dg, pool=64, reps=20):
     g.replay()
     torch.cuda.synchronize()
     out["decode_launch_floor"] = {"us": time_events(g.replay, reps) / pool * 1e3,
-                                  "what": "one-element kernel, 64 per HIP graph, per call"}
+                                  "what": f"one-element kernel, {pool} per HIP graph, per call"}
     return out
 
 

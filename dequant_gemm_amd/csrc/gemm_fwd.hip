@@ -39,6 +39,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kSmallCols = 16;
 constexpr int kSmallWaves = 8;
+constexpr int kNonTemporal = 2;    // buffer-load cache policy: bit 1 = nt (streaming)
 
 template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
@@ -121,8 +122,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
       ok[u] = (sc + u < s1) && (bi < kchunks);
       const uint32_t bic = ok[u] ? (uint32_t)bi : 0u;
       const uint32_t wo = wlane + bic * (kBlock / 2);
-      c[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, 0));
-      c[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo + 16, 0, 0));
+      // codes are read once per call: non-temporal (cache-policy bit nt).  The absmax
+      // state and X keep the default policy (nt on them measured slower).
+      c[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, kNonTemporal));
+      c[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo + 16, 0, kNonTemporal));
       const uint32_t rb = (elane + bic * kBlock) >> src.lbs;
       r[u] = load_abs(rb);
       if (BS32) r2[u] = load_abs(rb + 1);
