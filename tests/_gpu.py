@@ -24,10 +24,19 @@ def lib():
     return dg
 
 
+CONFIG = None   # the pytest config, set by conftest.py
+
+
 def note(msg: str):
-    """Progress line that pytest's capture does not swallow."""
-    sys.__stderr__.write(msg + "\n")
-    sys.__stderr__.flush()
+    """Progress line written past pytest's output capture (it names the case before a GPU step)."""
+    capman = CONFIG.pluginmanager.getplugin("capturemanager") if CONFIG is not None else None
+    if capman is None:
+        sys.__stderr__.write(msg + "\n")
+        sys.__stderr__.flush()
+        return
+    with capman.global_and_fixture_disabled():
+        sys.stderr.write(msg + "\n")
+        sys.stderr.flush()
 
 
 def u32(t: torch.Tensor) -> np.ndarray:

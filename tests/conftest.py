@@ -11,6 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU check")
+    import tests._gpu as g   # progress notes of the GPU tests go through pytest's capture manager
+    g.CONFIG = config
 
 
 def pytest_collection_modifyitems(config, items):
