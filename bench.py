@@ -10,8 +10,9 @@ Y = X W^T and the fused backward dX = dY W^, all through the C ABI of
 libnf4.so on torch's current stream, inputs and outputs resident in HBM.
 
 ``value`` is the step's GEMM throughput, 2 * 2*M*N*K flops per step over the
-step time (quantization included in the time).  The same JSON line carries
-per-kernel timings (HIP events around every launch of the timed steps), the
+step time (quantization included in the time; the timed steps run back to back
+with events only at the two ends).  The same JSON line carries per-kernel
+timings (HIP events around every launch of a second pass of as many steps), the
 dequantizer, the rank-64 adapter variants of both GEMMs, the decode-shape
 forward (M = 1, 4, 16 on a rotating pool of 512 quantized 4096x4096 weights,
 replayed from a HIP graph so host launch overhead does not count), the
@@ -135,13 +136,19 @@ def bench_prefill(dg, steps, warmup):
     for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
+    # The step time: exactly ``steps`` steps between two events, nothing else in
+    # the stream (events between the launches cost ~4 us each, ~2% of a step).
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    rec = [step(True) for _ in range(steps)]
+    for _ in range(steps):
+        step(False)
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
+    # Per-kernel durations: the same steps again, every launch bracketed by events.
+    rec = [step(True) for _ in range(steps)]
+    torch.cuda.synchronize()
     for marks in rec:
         for i, o in enumerate(ops):
             ev[o].append(marks[i].elapsed_time(marks[i + 1]))
@@ -499,7 +506,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first; the clock under sustained load settles after ~40 steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-large", action="store_true", help="skip the 8192x8192x28672 outlier-heavy shape")
