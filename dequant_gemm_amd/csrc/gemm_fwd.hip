@@ -122,8 +122,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
       ok[u] = (sc + u < s1) && (bi < kchunks);
       const uint32_t bic = ok[u] ? (uint32_t)bi : 0u;
       const uint32_t wo = wlane + bic * (kBlock / 2);
-      // codes are read once per call: non-temporal (cache-policy bit nt).  The absmax
-      // state and X keep the default policy (nt on them measured slower).
+      // codes are read once per call: non-temporal (cache-policy bit nt).  X, which
+      // every workgroup reads, and the absmax state keep the default policy (nt on the
+      // absmax state measured slower).
       c[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, kNonTemporal));
       c[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo + 16, 0, kNonTemporal));
       const uint32_t rb = (elane + bic * kBlock) >> src.lbs;
