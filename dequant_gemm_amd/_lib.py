@@ -115,6 +115,19 @@ def _require_device(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _require_out(out: torch.Tensor, numel: int, device: torch.device, name: str = "out"):
+    """An output buffer the kernels will fill: contiguous, on ``device``, exactly ``numel`` elements.
+
+    The C ABI takes raw pointers and cannot see buffer sizes; this is where a
+    too-small buffer is caught before anything is written.
+    """
+    _require_device(out, name)
+    if out.device != device:
+        raise ValueError(f"{name} is on {out.device}, the operands on {device}")
+    if out.numel() != numel:
+        raise ValueError(f"{name} has {out.numel()} elements, the result {numel}")
+
+
 def _quant_type_enum(quant_type: str) -> int:
     if quant_type not in QUANT_TYPES:
         raise ValueError(f"quant_type must be one of {tuple(QUANT_TYPES)} (got {quant_type!r})")
@@ -147,9 +160,33 @@ class QTensor:
 
     @property
     def device(self):
+        if self.packed is None:
+            raise ValueError("QTensor.packed is missing")
         return self.packed.device
 
+    def check(self):
+        """Buffer dtypes, devices and sizes against rows, cols, blocksize and double_quant."""
+        numel = self.rows * self.cols
+        nb = -(-numel // self.blocksize) if self.blocksize > 0 else 0
+        want = [("packed", self.packed, torch.uint8, -(-numel // 2))]
+        if self.double_quant:
+            want += [("absmax_q", self.absmax_q, torch.int8, nb),
+                     ("absmax_scale", self.absmax_scale, torch.float32, -(-nb // DQ_GROUP)),
+                     ("absmax_mean", self.absmax_mean, torch.float32, 1)]
+        else:
+            want.append(("absmax", self.absmax, torch.float32, nb))
+        for name, t, dt, n in want:
+            if t is None:
+                raise ValueError(f"QTensor.{name} is missing")
+            _require_device(t, f"QTensor.{name}")
+            if t.device != self.packed.device:
+                raise ValueError(f"QTensor.{name} is on {t.device}, packed on {self.packed.device}")
+            if t.dtype != dt or t.numel() < n:
+                raise ValueError(f"QTensor.{name} must be {dt} with at least {n} elements "
+                                 f"(got {t.dtype}, {t.numel()})")
+
     def struct(self) -> QTensorStruct:
+        self.check()
         return QTensorStruct(self.rows, self.cols, self.blocksize, int(self.double_quant),
                              _ptr(self.packed), _ptr(self.absmax), _ptr(self.absmax_q),
                              _ptr(self.absmax_scale), _ptr(self.absmax_mean),
@@ -226,6 +263,15 @@ def nf4_quantize(W: torch.Tensor, blocksize: int = BLOCKSIZE, double_quant: bool
     s = nf4_sizes(rows, cols, blocksize, double_quant)
     if workspace is None and s["workspace_bytes"]:
         workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=W.device)
+    if q.device != W.device:
+        raise ValueError(f"out is on {q.device}, W on {W.device}")
+    for t, nm in ((workspace, "workspace"), (status, "status")):
+        if t is not None:
+            _require_device(t, nm)
+            if t.device != W.device:
+                raise ValueError(f"{nm} is on {t.device}, W on {W.device}")
+    if status is not None and status.numel() * status.element_size() < 4:
+        raise ValueError("status must hold at least one uint32")
     st = q.struct()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nf4_quantize(W.data_ptr(), _dtype_enum(W.dtype), rows, cols, blocksize, int(double_quant),
@@ -237,7 +283,7 @@ def nf4_quantize(W: torch.Tensor, blocksize: int = BLOCKSIZE, double_quant: bool
 def nf4_dequantize(q: QTensor, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.device)
-    _require_device(out, "out")
+    _require_out(out, q.rows * q.cols, q.device)
     st = q.struct()
     _check(lib().nf4_dequantize(ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype), _stream(q.device)),
            "nf4_dequantize")
@@ -253,7 +299,9 @@ def nf4_matmul_fwd(X: torch.Tensor, q: QTensor, out_dtype: torch.dtype = torch.f
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, q.rows), dtype=out_dtype, device=X.device)
-    _require_device(out, "out")
+    _require_out(out, M * q.rows, X.device)
+    if q.device != X.device:
+        raise ValueError(f"the weight is on {q.device}, X on {X.device}")
     st = q.struct()
     _check(lib().nf4_matmul_fwd(X.data_ptr(), M, ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype),
                                 _stream(X.device)), "nf4_matmul_fwd")
@@ -269,16 +317,21 @@ def nf4_matmul_bwd_dx(dY: torch.Tensor, q: QTensor, out_dtype: torch.dtype = tor
     M = dY.shape[0]
     if out is None:
         out = torch.empty((M, q.cols), dtype=out_dtype, device=dY.device)
-    _require_device(out, "out")
+    _require_out(out, M * q.cols, dY.device)
+    if q.device != dY.device:
+        raise ValueError(f"the weight is on {q.device}, dY on {dY.device}")
     st = q.struct()
     _check(lib().nf4_matmul_bwd_dx(dY.data_ptr(), M, ctypes.byref(st), out.data_ptr(), _dtype_enum(out.dtype),
                                    _stream(dY.device)), "nf4_matmul_bwd_dx")
     return out
 
 
-def _lowrank_operands(U: torch.Tensor, V: torch.Tensor, M: int, cols: int, names: tuple) -> int:
+def _lowrank_operands(U: torch.Tensor, V: torch.Tensor, M: int, cols: int, names: tuple,
+                      device: torch.device) -> int:
     for t, nm in zip((U, V), names):
         _require_device(t, nm)
+        if t.device != device:
+            raise ValueError(f"{nm} is on {t.device}, the other operands on {device}")
         if t.dtype != torch.bfloat16 or t.dim() != 2:
             raise ValueError(f"{nm} must be a 2-D bf16 tensor")
     r = U.shape[1]
@@ -295,10 +348,12 @@ def nf4_matmul_fwd_lora(X: torch.Tensor, q: QTensor, U: torch.Tensor, B: torch.T
     if X.dtype != torch.bfloat16 or X.dim() != 2 or X.shape[1] != q.cols:
         raise ValueError("X must be bf16 [M, q.cols]")
     M = X.shape[0]
-    r = _lowrank_operands(U, B, M, q.rows, ("U", "B"))
+    r = _lowrank_operands(U, B, M, q.rows, ("U", "B"), X.device)
     if out is None:
         out = torch.empty((M, q.rows), dtype=out_dtype, device=X.device)
-    _require_device(out, "out")
+    _require_out(out, M * q.rows, X.device)
+    if q.device != X.device:
+        raise ValueError(f"the weight is on {q.device}, X on {X.device}")
     st = q.struct()
     _check(lib().nf4_matmul_fwd_lora(X.data_ptr(), M, ctypes.byref(st), U.data_ptr(), B.data_ptr(), r,
                                      out.data_ptr(), _dtype_enum(out.dtype), _stream(X.device)),
@@ -314,10 +369,12 @@ def nf4_matmul_bwd_dx_lora(dY: torch.Tensor, q: QTensor, V: torch.Tensor, At: to
     if dY.dtype != torch.bfloat16 or dY.dim() != 2 or dY.shape[1] != q.rows:
         raise ValueError("dY must be bf16 [M, q.rows]")
     M = dY.shape[0]
-    r = _lowrank_operands(V, At, M, q.cols, ("V", "At"))
+    r = _lowrank_operands(V, At, M, q.cols, ("V", "At"), dY.device)
     if out is None:
         out = torch.empty((M, q.cols), dtype=out_dtype, device=dY.device)
-    _require_device(out, "out")
+    _require_out(out, M * q.cols, dY.device)
+    if q.device != dY.device:
+        raise ValueError(f"the weight is on {q.device}, dY on {dY.device}")
     st = q.struct()
     _check(lib().nf4_matmul_bwd_dx_lora(dY.data_ptr(), M, ctypes.byref(st), V.data_ptr(), At.data_ptr(), r,
                                         out.data_ptr(), _dtype_enum(out.dtype), _stream(dY.device)),
