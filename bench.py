@@ -40,12 +40,21 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments and blank lines removed and spaces at line ends trimmed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def _source_hash(files):
+    """Hash of the kernels' code (comments excluded, so a comment edit keeps counters valid)."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -50,15 +50,13 @@ def compile_flags() -> list[str]:
     ]
 
 
-def _compile(src: str, asm_dir: str | None, defines=(), objdir=None) -> str:
+def _compile(src: str, asm_dir: str | None, objdir=None) -> str:
     obj = os.path.join(objdir or OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
-    _run(cmd)
+    _run([hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
         out = os.path.join(asm_dir, os.path.splitext(src)[0] + f"-{ARCH}.s")
-        _run([hipcc(), *compile_flags(), *[f"-D{d}" for d in defines], "--cuda-device-only", "-S",
-              os.path.join(CSRC, src), "-o", out])
+        _run([hipcc(), *compile_flags(), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out])
     return obj
 
 
@@ -72,16 +70,12 @@ def _run(cmd):
         sys.stderr.write(errs + "\n")
 
 
-def build(asm_dir: str | None = None, verbose: bool = True, defines=(), out: str | None = None) -> str:
-    """Compiles every source and links libnf4.so (or ``out``); returns its path.
-
-    ``defines`` are extra preprocessor definitions (tuning variants).
-    """
-    lib = out or LIB
-    objdir = OBJDIR if not defines else os.path.join(OBJDIR, "_".join(defines).replace("=", ""))
-    os.makedirs(objdir, exist_ok=True)
+def build(asm_dir: str | None = None, verbose: bool = True) -> str:
+    """Compiles every source and links libnf4.so; returns its path."""
+    lib = LIB
+    os.makedirs(OBJDIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm_dir, defines, objdir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, asm_dir), SOURCES))
     tmp = lib + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, lib)
@@ -93,7 +87,5 @@ def build(asm_dir: str | None = None, verbose: bool = True, defines=(), out: str
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", default=None, help="directory for the gfx950 assembly listings")
-    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor definition")
-    ap.add_argument("-o", dest="out", default=None, help="output library path (default: in-tree libnf4.so)")
     a = ap.parse_args()
-    build(a.asm, defines=a.defines, out=a.out)
+    build(a.asm)

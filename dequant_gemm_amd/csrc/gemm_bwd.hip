@@ -35,10 +35,6 @@ namespace {
 // step's MFMAs.
 namespace generic {
 
-#ifndef NF4_BWD_SCHED
-#define NF4_BWD_SCHED 0
-#endif
-
 constexpr int TM = 256, TK = 256, TN = 64;
 constexpr int ROWB = TN * 2 + 16;  // LDS row stride in bytes (64 bf16 + padding)
 
@@ -201,11 +197,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (more) store_b_part(cur ^ 1, j, c0, c1, t0, t1);
     }
     if (more) store_a(cur ^ 1);
-#if NF4_BWD_SCHED == 1
-    __builtin_amdgcn_iglp_opt(1);
-#elif NF4_BWD_SCHED == 2
-    __builtin_amdgcn_iglp_opt(0);
-#endif
     __syncthreads();
   }
 
