@@ -80,3 +80,28 @@ def assert_gemm_within_bound(out: torch.Tensor, ref: np.ndarray, bound: np.ndarr
         i = np.argwhere(bad)[0]
         pytest.fail(f"{where}: {n} elements outside 1e-4*(|A||B|); first {tuple(i)}: "
                     f"got {o[tuple(i)]!r} want {ref[tuple(i)]!r} bound {bound[tuple(i)]!r}")
+
+
+def assert_gemm_rows(out: torch.Tensor, a_bf16: torch.Tensor, wh64: np.ndarray, op: str, where: str,
+                     rows: int = 1024):
+    """Every element of a GEMM output against the oracle, in chunks of ``rows`` output rows.
+
+    ``out`` is the GPU result (any device), ``a_bf16`` the left operand (X for the
+    forward, dY for the backward) on the host, ``wh64`` the oracle's W^ as float64.
+    Each chunk takes the oracle's float64 product and its element-wise bound.
+    """
+    if op == "fwd":
+        prod, bound = O.matmul_fwd, O.fwd_bound
+    elif op == "bwd_dx":
+        prod, bound = O.matmul_bwd_dx, O.bwd_dx_bound
+    else:
+        raise ValueError(op)
+    out = out.detach().cpu()
+    M = a_bf16.shape[0]
+    assert out.shape[0] == M
+    for lo in range(0, M, rows):
+        hi = min(M, lo + rows)
+        a = a_bf16[lo:hi].float().numpy()
+        assert_gemm_within_bound(out[lo:hi], prod(a, wh64), bound(a, wh64), f"{where} rows {lo}..{hi - 1}")
+        note(f"{where}: rows {lo}..{hi - 1} of {M} within the bound")
+

@@ -15,6 +15,19 @@ def pytest_configure(config):
     g.CONFIG = config
 
 
+@pytest.fixture(scope="session")
+def large_oracle():
+    """The Large workload's weight (28672x8192 fp32, 0.02 * Student-t(4)) and the oracle's
+    quantization of it, computed once for the quantize and GEMM parity tests."""
+    import oracle as O
+    import synth
+    from tests._gpu import note
+    note("large weight 28672x8192 fp32: drawing; oracle quantize of 235M elements")
+    W = synth.large_weight()
+    qo = O.quantize(W.numpy().ravel(), double_quant_on=True)
+    return W, qo
+
+
 def pytest_collection_modifyitems(config, items):
     # GPU tests fail loudly when they run without a GPU; they are only deselected by -m.
     pass
