@@ -29,14 +29,15 @@ QUANT_TYPES = {"nf4": 0, "fp4": 1}     # nf4_quant_type: the level table
 STATUS_NAMES = {
     0: "NF4_OK", 1: "NF4_ERR_NULL", 2: "NF4_ERR_SHAPE", 3: "NF4_ERR_BLOCKSIZE", 4: "NF4_ERR_DTYPE",
     5: "NF4_ERR_ALIGN", 6: "NF4_ERR_WORKSPACE", 7: "NF4_ERR_UNSUPPORTED", 8: "NF4_ERR_HIP",
-    9: "NF4_ERR_QUANT_TYPE",
+    9: "NF4_ERR_QUANT_TYPE", 10: "NF4_ERR_SCRATCH",
 }
 
 EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_levels", "nf4_thresholds", "nf4_sizes", "nf4_quantize",
-           "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx", "nf4_matmul_fwd_lora",
+           "nf4_quantize_noalloc", "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx", "nf4_matmul_fwd_lora",
            "nf4_matmul_bwd_dx_lora")
 LORA_RANK_STEP = 16
 LORA_MAX_RANK = 1024
+NOALLOC_MAX_BLOCKS = 1 << 22     # NF4_NOALLOC_MAX_BLOCKS: blocks nf4_quantize_noalloc's scratch holds
 
 
 class QTensorStruct(ctypes.Structure):
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.nf4_sizes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64), ctypes.POINTER(sz)]
         L.nf4_quantize.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(QTensorStruct), vp, sz, vp, vp]
+        L.nf4_quantize_noalloc.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(QTensorStruct), vp, vp]
         L.nf4_dequantize.argtypes = [ctypes.POINTER(QTensorStruct), vp, i32, vp]
         L.nf4_matmul_fwd.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
         L.nf4_matmul_bwd_dx.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
@@ -278,6 +280,29 @@ def nf4_quantize(W: torch.Tensor, blocksize: int = BLOCKSIZE, double_quant: bool
                               ctypes.byref(st), _ptr(workspace), ws_bytes, _ptr(status), _stream(W.device)),
            "nf4_quantize")
     return q
+
+
+def nf4_quantize_noalloc(W: torch.Tensor, out: QTensor, status: Optional[torch.Tensor] = None) -> QTensor:
+    """``nf4_quantize`` into the caller's ``out`` without a workspace: the library's fixed
+    per-GPU scratch serves instead, so the C call allocates nothing (block size, double
+    quantization and quant_type come from ``out``)."""
+    _require_device(W, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows, cols]")
+    rows, cols = W.shape
+    if out.device != W.device:
+        raise ValueError(f"out is on {out.device}, W on {W.device}")
+    if status is not None:
+        _require_device(status, "status")
+        if status.device != W.device:
+            raise ValueError(f"status is on {status.device}, W on {W.device}")
+        if status.numel() * status.element_size() < 4:
+            raise ValueError("status must hold at least one uint32")
+    st = out.struct()
+    _check(lib().nf4_quantize_noalloc(W.data_ptr(), _dtype_enum(W.dtype), rows, cols, out.blocksize,
+                                      int(out.double_quant), ctypes.byref(st), _ptr(status), _stream(W.device)),
+           "nf4_quantize_noalloc")
+    return out
 
 
 def nf4_dequantize(q: QTensor, dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:

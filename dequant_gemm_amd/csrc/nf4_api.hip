@@ -1,6 +1,8 @@
 // nf4_api.hip -- the C ABI declared in include/nf4.h: argument validation,
 // buffer-size arithmetic and kernel dispatch.  Validation touches no HIP API,
 // so every error path can be exercised on a machine without a GPU.
+#include <mutex>
+
 #include "nf4.h"
 #include "nf4_launch.h"
 
@@ -60,6 +62,75 @@ nf4::AbsmaxSrc absmax_src(const nf4_qtensor *q) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 
+// Argument checks shared by both quantize entry points (no HIP call).
+int check_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blocksize, int double_quant,
+                   const nf4_qtensor *out, const uint32_t *d_status) {
+  if (!valid_blocksize(blocksize)) return NF4_ERR_BLOCKSIZE;
+  if (!W || !out) return NF4_ERR_NULL;
+  if (!valid_dtype(w_dtype)) return NF4_ERR_DTYPE;
+  int st = check_shape(rows, cols);
+  if (st) return st;
+  if (double_quant != 0 && double_quant != 1) return NF4_ERR_UNSUPPORTED;
+  if (!aligned16(W)) return NF4_ERR_ALIGN;
+  st = check_qtensor(out);
+  if (st) return st;
+  if (out->rows != rows || out->cols != cols || out->double_quant != double_quant ||
+      out->blocksize != blocksize)
+    return NF4_ERR_SHAPE;
+  if (d_status && !aligned16(d_status)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+// Queues the quantization of checked arguments; `ws` holds at least
+// quant_workspace_bytes(nblocks) bytes when double_quant is set.
+int launch_quantize_into(const void *W, int w_dtype, int64_t rows, int64_t cols, int blocksize, int double_quant,
+                         const nf4_qtensor *out, void *ws, uint32_t *d_status, void *stream) {
+  unsigned long long *partials = nullptr;
+  float *absmax = out->absmax;
+  if (double_quant) {
+    partials = reinterpret_cast<unsigned long long *>(ws);
+    absmax = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + nf4::absmax_ws_offset());
+  }
+  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, rows * cols, log2_of(blocksize),
+                                         out->quant_type == NF4_QT_FP4, out->packed, absmax,
+                                         partials, d_status, double_quant, out->absmax_q,
+                                         out->absmax_scale, out->absmax_mean,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- fixed scratch
+//
+// nf4_quantize_noalloc's scratch: the same layout as nf4_quantize's workspace
+// (exact-mean rows, then the fp32 absmax of every block), sized for
+// NF4_NOALLOC_MAX_BLOCKS blocks.  One copy per GPU, kept for the life of the
+// process and shared by every call on that GPU.  In host code `scratch` names
+// a host-side stand-in, never the device memory: the device address is taken
+// once per device with hipGetSymbolAddress and only that address is passed on.
+constexpr size_t kScratchBytes = nf4::quant_workspace_bytes(NF4_NOALLOC_MAX_BLOCKS);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once taken
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with that device current) and cached.
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,6 +147,7 @@ const char *nf4_status_string(int status) {
     case NF4_ERR_UNSUPPORTED: return "unsupported (e.g. GEMM needs cols % 64 == 0)";
     case NF4_ERR_HIP: return "HIP launch failed";
     case NF4_ERR_QUANT_TYPE: return "quant_type must be NF4_QT_NF4 or NF4_QT_FP4";
+    case NF4_ERR_SCRATCH: return "more blocks than nf4_quantize_noalloc's fixed scratch holds (NF4_NOALLOC_MAX_BLOCKS)";
     default: return "unknown status";
   }
 }
@@ -117,36 +189,27 @@ int nf4_sizes(int64_t rows, int64_t cols, int blocksize, int double_quant, int64
 int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols, int blocksize,
                  int double_quant, const nf4_qtensor *out, void *workspace, size_t workspace_bytes,
                  uint32_t *d_status, void *stream) {
-  if (!valid_blocksize(blocksize)) return NF4_ERR_BLOCKSIZE;
-  if (!W || !out) return NF4_ERR_NULL;
-  if (!valid_dtype(w_dtype)) return NF4_ERR_DTYPE;
-  int st = check_shape(rows, cols);
+  int st = check_quantize(W, w_dtype, rows, cols, blocksize, double_quant, out, d_status);
   if (st) return st;
-  if (double_quant != 0 && double_quant != 1) return NF4_ERR_UNSUPPORTED;
-  if (!aligned16(W)) return NF4_ERR_ALIGN;
-  st = check_qtensor(out);
-  if (st) return st;
-  if (out->rows != rows || out->cols != cols || out->double_quant != double_quant ||
-      out->blocksize != blocksize)
-    return NF4_ERR_SHAPE;
-  if (d_status && !aligned16(d_status)) return NF4_ERR_ALIGN;
-  const int64_t numel = rows * cols;
-  const int64_t nb = nblocks_of(numel, blocksize);
-  unsigned long long *partials = nullptr;
-  float *absmax = out->absmax;
+  const int64_t nb = nblocks_of(rows * cols, blocksize);
   if (double_quant) {
-    const size_t need = nf4::quant_workspace_bytes(nb);
-    if (workspace_bytes < need) return NF4_ERR_WORKSPACE;
+    if (workspace_bytes < nf4::quant_workspace_bytes(nb)) return NF4_ERR_WORKSPACE;
     if (!workspace) return NF4_ERR_NULL;
     if (!aligned16(workspace)) return NF4_ERR_ALIGN;
-    partials = reinterpret_cast<unsigned long long *>(workspace);
-    absmax = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + nf4::absmax_ws_offset());
   }
-  return hip_status(nf4::launch_quantize(W, w_dtype == NF4_BF16, numel, log2_of(blocksize),
-                                         out->quant_type == NF4_QT_FP4, out->packed, absmax,
-                                         partials, d_status, double_quant, out->absmax_q,
-                                         out->absmax_scale, out->absmax_mean,
-                                         reinterpret_cast<hipStream_t>(stream)));
+  return launch_quantize_into(W, w_dtype, rows, cols, blocksize, double_quant, out, workspace, d_status, stream);
+}
+
+int nf4_quantize_noalloc(const void *W, int w_dtype, int64_t rows, int64_t cols, int blocksize,
+                         int double_quant, const nf4_qtensor *out, uint32_t *d_status, void *stream) {
+  int st = check_quantize(W, w_dtype, rows, cols, blocksize, double_quant, out, d_status);
+  if (st) return st;
+  if (!double_quant)   // without double quantization the kernels use no scratch at all
+    return launch_quantize_into(W, w_dtype, rows, cols, blocksize, 0, out, nullptr, d_status, stream);
+  if (nblocks_of(rows * cols, blocksize) > NF4_NOALLOC_MAX_BLOCKS) return NF4_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return NF4_ERR_HIP;
+  return launch_quantize_into(W, w_dtype, rows, cols, blocksize, 1, out, ws, d_status, stream);
 }
 
 int nf4_dequantize(const nf4_qtensor *q, void *out, int out_dtype, void *stream) {

@@ -17,10 +17,9 @@ namespace nf4 {
 constexpr int kQuantGridMax = 2048;
 constexpr int kMeanSlots = 16;
 constexpr size_t kPartialBytes = (size_t)(kQuantGridMax + 1) * kMeanSlots * sizeof(unsigned long long);
-inline size_t absmax_ws_offset() { return (kPartialBytes + 255) & ~(size_t)255; }
-inline size_t quant_workspace_bytes(int64_t nblocks) {
-  size_t b = absmax_ws_offset() + (size_t)nblocks * sizeof(float);
-  return (b + 255) & ~(size_t)255;
+constexpr size_t absmax_ws_offset() { return (kPartialBytes + 255) & ~(size_t)255; }
+constexpr size_t quant_workspace_bytes(int64_t nblocks) {
+  return (absmax_ws_offset() + (size_t)nblocks * sizeof(float) + 255) & ~(size_t)255;
 }
 
 // `lbs`: log2 of the block size (5..8); `fp4`: the FP4 level table instead of NF4's.

@@ -85,7 +85,8 @@ enum nf4_status {
   NF4_ERR_WORKSPACE = 6,    /* workspace smaller than nf4_sizes reports */
   NF4_ERR_UNSUPPORTED = 7,  /* valid but not supported, e.g. a GEMM with cols % 64 != 0 */
   NF4_ERR_HIP = 8,          /* a HIP launch failed */
-  NF4_ERR_QUANT_TYPE = 9    /* unknown nf4_quant_type value */
+  NF4_ERR_QUANT_TYPE = 9,   /* unknown nf4_quant_type value */
+  NF4_ERR_SCRATCH = 10      /* the tensor needs more than the fixed scratch of nf4_quantize_noalloc */
 };
 
 enum nf4_dtype {
@@ -200,6 +201,29 @@ int nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
                  int blocksize, int double_quant, const nf4_qtensor *out,
                  void *workspace, size_t workspace_bytes, uint32_t *d_status,
                  void *stream);
+
+/*
+ * nf4_quantize without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * nf4_quantize; the double-quantization scratch (exact-mean rows and the fp32
+ * absmax of every block) lives in a fixed buffer inside the library, one per
+ * GPU, sized for NF4_NOALLOC_MAX_BLOCKS blocks (about 16.3 MiB), held until
+ * the process ends.  A tensor with more blocks, with double_quant set, is
+ * refused with NF4_ERR_SCRATCH before anything is launched; without double
+ * quantization no scratch is used and every size nf4_quantize takes is
+ * accepted.  Calls no allocating routine.  The buffer is shared by every call
+ * on a GPU and keeps the last call's contents (the kernels overwrite every
+ * byte they later read, so nothing needs clearing between calls); calls whose
+ * execution overlaps on one GPU (different streams, different threads) race
+ * on it and must be serialised by the caller.  The first call on each device
+ * looks the buffer's device address up (thread-safe); NF4_ERR_HIP if that
+ * fails.
+ */
+#define NF4_NOALLOC_MAX_BLOCKS ((int64_t)1 << 22)
+int nf4_quantize_noalloc(const void *W, int w_dtype, int64_t rows, int64_t cols,
+                         int blocksize, int double_quant, const nf4_qtensor *out,
+                         uint32_t *d_status, void *stream);
 
 /*
  * Writes the dequantized weight W^ (device, [rows, cols] row-major) in

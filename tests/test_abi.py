@@ -166,6 +166,31 @@ def test_quantize_errors(L):
     assert L.nf4_quantize(P, 1, 64, 64, 64, 1, None, P, ws, None, None) == 1
 
 
+def test_quantize_noalloc_errors(L):
+    """The allocation-free quantize checks as nf4_quantize does, and refuses a tensor with
+    more blocks than its fixed scratch holds, all before any HIP call."""
+    q = _qt()
+    call = lambda **k: L.nf4_quantize_noalloc(k.get("W", P), k.get("dt", 1), k.get("rows", 64),
+                                              k.get("cols", 64), k.get("bs", 64), k.get("dq", 1),
+                                              ctypes.byref(k.get("q", q)), k.get("status", None), None)
+    assert call(W=None) == 1
+    assert call(dt=7) == 4
+    assert call(bs=48) == 3
+    assert call(rows=0) == 2
+    assert call(W=P + 2) == 5
+    assert call(q=_qt(rows=32)) == 2
+    assert call(q=_qt(q=None)) == 1
+    assert call(status=P + 4) == 5
+    assert L.nf4_quantize_noalloc(P, 1, 64, 64, 64, 1, None, None, None) == 1
+    # the scratch limit: NF4_NOALLOC_MAX_BLOCKS blocks with double quantization
+    limit = dg.NOALLOC_MAX_BLOCKS
+    header = open(HEADER).read()
+    assert re.search(r"#define NF4_NOALLOC_MAX_BLOCKS \(\(int64_t\)1 << 22\)", header)
+    for bs in (32, 64, 256):
+        rows, cols = limit * bs // 4096 + 1, 4096          # limit + 4096 / bs blocks
+        assert call(rows=rows, cols=cols, bs=bs, q=_qt(rows=rows, cols=cols, bs=bs)) == 10
+
+
 def test_dequantize_errors(L):
     assert L.nf4_dequantize(None, P, 1, None) == 1
     assert L.nf4_dequantize(ctypes.byref(_qt()), None, 1, None) == 1
@@ -192,7 +217,7 @@ def test_gemm_errors(L, fn):
 
 
 def test_status_strings(L):
-    for s in range(10):
+    for s in range(11):
         assert L.nf4_status_string(s)
     assert L.nf4_status_string(99) == b"unknown status"
 
