@@ -12,11 +12,11 @@ namespace nf4 {
 
 // Workspace layout for quantization with double quantization: one row of
 // kMeanSlots exact-mean accumulators per quantize workgroup (at most
-// kQuantGridMax) plus one for the partial tail block, then the fp32 absmax of
-// every block.
+// kQuantGridMax; the last workgroup's row also holds the partial block at the
+// end), then the fp32 absmax of every block.
 constexpr int kQuantGridMax = 2048;
 constexpr int kMeanSlots = 16;
-constexpr size_t kPartialBytes = (size_t)(kQuantGridMax + 1) * kMeanSlots * sizeof(unsigned long long);
+constexpr size_t kPartialBytes = (size_t)kQuantGridMax * kMeanSlots * sizeof(unsigned long long);
 constexpr size_t absmax_ws_offset() { return (kPartialBytes + 255) & ~(size_t)255; }
 constexpr size_t quant_workspace_bytes(int64_t nblocks) {
   return (absmax_ws_offset() + (size_t)nblocks * sizeof(float) + 255) & ~(size_t)255;

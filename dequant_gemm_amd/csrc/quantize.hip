@@ -7,14 +7,16 @@
 // quantized to 8 bits with their own meta-scales).
 //
 // Kernels, in launch order:
-//   quantize_blocks_kernel   full 64-blocks: absmax, codes, packing; with double
-//                            quantization also one row of exact-mean
-//                            accumulators per workgroup (plain stores)
-//   quantize_tail_kernel     the one partial block at the end, if any (its own
-//                            accumulator row)
-//   mean_reduce_kernel       one workgroup: sums the rows and forms the exact
-//                            mean, one rounding
-//   double_quant_kernel      int8 absmax and one fp32 scale per 256 blocks
+//   quantize_blocks_kernel   absmax, codes and packing of every block (the
+//                            last workgroup also takes the partial block at
+//                            the end, if any); with double quantization also
+//                            one row of exact-mean accumulators per workgroup
+//                            (plain stores) and the fp32 absmax of every block
+//   mean_dq_kernel           double quantization: each workgroup sums all the
+//                            rows itself and forms the exact mean (one
+//                            rounding; integer sums, so every workgroup gets
+//                            the same bits), then quantizes its share of the
+//                            256-block groups to int8 with one fp32 scale each
 //
 // Exact mean.  Every finite fp32 is an integer number of 2^-149 units: a value
 // with biased exponent e and 24-bit significand m is m * 2^(max(e,1)-1) units.
@@ -36,15 +38,19 @@ namespace {
 // more than 2e-4 away from a cell edge, so for n in cell j
 //   code(n) = base_j + (n >= thr_j).
 // A fast path forms n from one reciprocal per block (n' within 2^-22
-// relative of the exact quotient); values n' within 2^-20 relative of the
-// threshold of their cell are re-done with the IEEE division.
+// relative of the exact quotient); each value n' within 2^-20 relative of the
+// threshold of its cell is redone with the IEEE division.
 
 struct Cell {
   float thr;   // threshold inside the cell, +inf if none
-  float lo;    // thr - tolerance
-  float hi;    // thr + tolerance
   int base;    // code of the cell's lower edge
 };
+
+// |n - thr| < |thr| * 2^-20: n is too close to the threshold for the fast
+// quotient to decide (false for thr = +inf, where both sides are infinite).
+__device__ __forceinline__ bool near_thr(float n, float thr) {
+  return fabsf(n - thr) < fabsf(thr) * 0x1p-20f;
+}
 
 __device__ void build_cells(Cell *tab) {
   for (int j = threadIdx.x; j < 129; j += blockDim.x) {
@@ -63,14 +69,6 @@ __device__ void build_cells(Cell *tab) {
     Cell c;
     c.thr = thr;
     c.base = base;
-    if (thr == __builtin_inff()) {
-      c.lo = thr;
-      c.hi = thr;
-    } else {
-      const float tol = fabsf(thr) * 0x1p-20f;
-      c.lo = thr - tol;
-      c.hi = thr + tol;
-    }
     tab[j] = c;
   }
 }
@@ -80,26 +78,30 @@ __device__ __forceinline__ int classify(float n, const Cell *tab, bool &near) {
   int j = (int)f;
   j = j < 0 ? 0 : (j > 128 ? 128 : j);
   const Cell c = tab[j];
-  near |= (n > c.lo) && (n < c.hi);
+  near = near_thr(n, c.thr);
   return c.base + (n >= c.thr ? 1 : 0);
 }
 
 // Codes of eight values of one block with absmax bits `m` (finite, non-zero).
+// An element whose fast quotient is near its cell's threshold is redone with
+// the IEEE division on its own (the others keep the fast result).
 __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const Cell *cells) {
   const float a = __uint_as_float(m);
   int code[8];
-  bool near = false;
-  if (m >= 0x01000000u && m < 0x7e000000u) {  // 2^-125 <= a < 2^125: 1/a is a normal float
-    const float r = __builtin_amdgcn_rcpf(a);
+  bool near[8];
+  const bool fast = m >= 0x01000000u && m < 0x7e000000u;  // 2^-125 <= a < 2^125: 1/a is a normal float
+  const float r = __builtin_amdgcn_rcpf(a);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = classify(x[i] * r, cells, near);
-  } else {
-    near = true;
+  for (int i = 0; i < 8; ++i) {
+    code[i] = classify(x[i] * r, cells, near[i]);
+    near[i] = near[i] || !fast;
   }
-  if (near) {
-    bool unused = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = classify(x[i] / a, cells, unused);
+  for (int i = 0; i < 8; ++i) {
+    if (near[i]) {
+      bool unused;
+      code[i] = classify(x[i] / a, cells, unused);
+    }
   }
   uint32_t word = 0;
 #pragma unroll
@@ -107,24 +109,75 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
   return word;
 }
 
-// FP4 code of a normalised value n: the magnitude index counts the
-// thresholds |n| lies above (a tie goes to the smaller magnitude, the lower
-// code), then the sign; zero of either sign takes code 0 (+0).
-__device__ __forceinline__ int fp4_code(float n) {
-  const float an = fabsf(n);
-  int mi = 0;
+// FP4: the normalised magnitude |n| in [0, 1] is cut into 25 cells of width
+// 1/24 centred on multiples of 1/24.  The seven decision thresholds (the
+// largest fp32 values not above the midpoints of adjacent magnitudes 1/24,
+// 3/24, 5/24, 7/24, 10/24, 14/24, 20/24) each sit at a cell's centre, so a cell
+// holds at most one and every one is 1/48 from its cell's edges; then
+//   magnitude index(|n|) = base_j + (|n| > thr_j)
+// (strictly above: a tie goes to the smaller magnitude, the lower code).  The
+// sign is applied after; zero of either sign takes code 0 (+0).
+constexpr int kFp4Cells = 25;
+
+__device__ void build_cells_fp4(Cell *tab) {
+  for (int j = threadIdx.x; j < kFp4Cells; j += blockDim.x) {
+    const float lo = ((float)j - 0.5f) * (1.0f / 24.0f);
+    const float hi = ((float)j + 0.5f) * (1.0f / 24.0f);
+    int base = 0;
+    float thr = __builtin_inff();
 #pragma unroll
-  for (int i = 0; i < 7; ++i) mi += an > fp4_threshold(i) ? 1 : 0;
+    for (int i = 0; i < 7; ++i) {
+      const float t = fp4_threshold(i);
+      if (t < lo)
+        ++base;
+      else if (t < hi)
+        thr = t;
+    }
+    Cell c;
+    c.thr = thr;
+    c.base = base;
+    tab[j] = c;
+  }
+}
+
+__device__ __forceinline__ int classify_fp4(float n, const Cell *tab, bool &near) {
+  const float an = fabsf(n);
+  int j = (int)(an * 24.0f + 0.5f);
+  j = j > kFp4Cells - 1 ? kFp4Cells - 1 : j;
+  const Cell c = tab[j];
+  near = near_thr(an, c.thr);
+  const int mi = c.base + (an > c.thr ? 1 : 0);
   return (n < 0.f && mi > 0) ? 8 + mi : mi;
 }
 
 // FP4 codes of eight values of one block with absmax bits `m` (finite,
-// non-zero): exact IEEE division, then the thresholds.
-__device__ __forceinline__ uint32_t encode8_fp4(const float x[8], uint32_t m) {
+// non-zero): one reciprocal per block (n' within 2^-22 relative of the exact
+// quotient); each value within 2^-20 relative of its cell's threshold, and
+// every value of a block whose reciprocal is not a normal float, is redone
+// with the IEEE division.  (With bf16 weights the quotient lands exactly on
+// the threshold 1/8 for a few elements in a thousand, so the redo is per
+// element.)
+__device__ __forceinline__ uint32_t encode8_fp4(const float x[8], uint32_t m, const Cell *cells) {
   const float a = __uint_as_float(m);
+  int code[8];
+  bool near[8];
+  const bool fast = m >= 0x01000000u && m < 0x7e000000u;
+  const float r = __builtin_amdgcn_rcpf(a);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    code[i] = classify_fp4(x[i] * r, cells, near[i]);
+    near[i] = near[i] || !fast;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (near[i]) {
+      bool unused;
+      code[i] = classify_fp4(x[i] / a, cells, unused);
+    }
+  }
   uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= (uint32_t)fp4_code(x[i] / a) << (4 * i);
+  for (int i = 0; i < 8; ++i) word |= (uint32_t)code[i] << (4 * i);
   return word;
 }
 
@@ -146,13 +199,14 @@ __device__ __forceinline__ void add_to_slots(unsigned long long *slot, int e, un
 
 template <bool BF16, bool DQ, int LPB, bool FP4>
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(
-    const void *__restrict__ w, int64_t nfull, uint8_t *__restrict__ packed,
+    const void *__restrict__ w, int64_t numel, int64_t nfull, uint8_t *__restrict__ packed,
     float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status) {
   constexpr int BS = 8 * LPB;        // weights per block
   constexpr int BPI = 256 / LPB;     // blocks per workgroup and iteration
   __shared__ Cell cells[129];
   __shared__ unsigned long long lbuck[256];
   __shared__ unsigned long long lslot[kMeanSlots];
+  __shared__ uint32_t wmax[4];
   const int part = threadIdx.x % LPB;
   const int slot = threadIdx.x / LPB;
   const int64_t stride = (int64_t)gridDim.x * BPI;
@@ -165,11 +219,19 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
       v = p[1];
     }
   };
+  auto add_absmax = [&](uint32_t m) {   // this block's absmax into the exponent sums
+    const uint32_t e = m >> 23;
+    const unsigned long long sig = (m & 0x7fffffu) | (e ? 0x800000u : 0u);
+    atomicAdd(&lbuck[e], sig);
+  };
   bool bad = false;
   int64_t blk = (int64_t)blockIdx.x * BPI + slot;
   uint4 cu = make_uint4(0, 0, 0, 0), cv = cu;
   if (blk < nfull) load(blk, cu, cv);   // in flight while the level table is built
-  if (!FP4) build_cells(cells);
+  if (FP4)
+    build_cells_fp4(cells);
+  else
+    build_cells(cells);
   if (DQ) {
     lbuck[threadIdx.x] = 0ull;
     if (threadIdx.x < kMeanSlots) lslot[threadIdx.x] = 0ull;
@@ -208,19 +270,50 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     } else if (m == 0) {
       word = kZeroWord;  // all-zero block
     } else {
-      word = FP4 ? encode8_fp4(x, m) : encode8(x, m, cells);
+      word = FP4 ? encode8_fp4(x, m, cells) : encode8(x, m, cells);
     }
     *reinterpret_cast<uint32_t *>(packed + blk * (BS / 2) + part * 4) = word;
     if (part == 0) {
       absmax[blk] = __uint_as_float(m);
-      if (DQ && m < 0x7f800000u) {
-        const uint32_t e = m >> 23;
-        const unsigned long long sig = (m & 0x7fffffu) | (e ? 0x800000u : 0u);
-        atomicAdd(&lbuck[e], sig);
-      }
+      if (DQ && m < 0x7f800000u) add_absmax(m);
     }
     cu = nu;
     cv = nv;
+  }
+
+  // The partial block at the end (fewer than BS <= 256 elements), in the last
+  // workgroup: one element per thread, exact division.
+  if (blockIdx.x == gridDim.x - 1 && nfull * BS < numel) {
+    const int t = threadIdx.x;
+    const int64_t e = nfull * BS + t;
+    const bool valid = t < BS && e < numel;
+    float x = 0.f;
+    if (valid) {
+      if (BF16)
+        x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(w)[e] << 16);
+      else
+        x = reinterpret_cast<const float *>(w)[e];
+    }
+    uint32_t m = __float_as_uint(x) & 0x7fffffffu;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
+    if ((t & 63) == 0) wmax[t >> 6] = m;
+    __syncthreads();
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    int code = FP4 ? 0 : 7;   // the +0 level
+    if (m != 0 && m < 0x7f800000u) {
+      bool unused = false;
+      const float n = x / __uint_as_float(m);
+      code = FP4 ? classify_fp4(n, cells, unused) : classify(n, cells, unused);
+    }
+    if (!valid) code = 0;
+    const int upper = __shfl_down(code, 1);
+    if (valid && (t & 1) == 0) packed[e / 2] = (uint8_t)(code | (upper << 4));
+    if (t == 0) {
+      absmax[nfull] = __uint_as_float(m);
+      if (m >= 0x7f800000u) bad = true;
+      else if (DQ) add_absmax(m);
+    }
   }
   if (DQ) {
     __syncthreads();
@@ -230,58 +323,6 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     if (threadIdx.x < kMeanSlots) partials[(int64_t)blockIdx.x * kMeanSlots + threadIdx.x] = lslot[threadIdx.x];
   }
   if (bad && status) atomicOr(status, 1u);
-}
-
-// The partial block at the end (fewer than blocksize <= 256 elements): one
-// workgroup of 256 threads, one element per thread, exact division.
-template <bool BF16, bool DQ, bool FP4>
-__global__ __launch_bounds__(256) void quantize_tail_kernel(
-    const void *__restrict__ w, int64_t numel, int64_t blk, int bs, uint8_t *__restrict__ packed,
-    float *__restrict__ absmax, unsigned long long *__restrict__ partial_row, uint32_t *status) {
-  __shared__ Cell cells[129];
-  __shared__ uint32_t wmax[4];
-  if (!FP4) build_cells(cells);
-  const int t = threadIdx.x;
-  const int64_t e = blk * bs + t;
-  const bool valid = t < bs && e < numel;
-  float x = 0.f;
-  if (valid) {
-    if (BF16)
-      x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(w)[e] << 16);
-    else
-      x = reinterpret_cast<const float *>(w)[e];
-  }
-  uint32_t m = __float_as_uint(x) & 0x7fffffffu;
-#pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
-  if ((t & 63) == 0) wmax[t >> 6] = m;
-  __syncthreads();
-  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  int code = FP4 ? 0 : 7;   // the +0 level
-  if (m != 0 && m < 0x7f800000u) {
-    bool unused = false;
-    code = FP4 ? fp4_code(x / __uint_as_float(m)) : classify(x / __uint_as_float(m), cells, unused);
-  }
-  if (!valid) code = 0;
-  const int upper = __shfl_down(code, 1);
-  if (valid && (t & 1) == 0) packed[(blk * bs + t) / 2] = (uint8_t)(code | (upper << 4));
-  if (DQ && t < kMeanSlots) {
-    // this block's accumulator row: the digits of its absmax alone
-    const uint32_t ex = m >> 23;
-    const unsigned long long sig = (m & 0x7fffffu) | (ex ? 0x800000u : 0u);
-    const int sh = (ex > 0 ? (int)ex : 1) - 1;
-    const unsigned long long lo = sig << (sh & 31);     // below 2^55
-    unsigned long long d = 0;
-    if (m < 0x7f800000u) {
-      if (t == (sh >> 5)) d = (uint32_t)lo;
-      if (t == (sh >> 5) + 1) d = lo >> 32;
-    }
-    partial_row[t] = d;
-  }
-  if (t == 0) {
-    absmax[blk] = __uint_as_float(m);
-    if (m >= 0x7f800000u && status) atomicOr(status, 1u);
-  }
 }
 
 // Exact mean of all block absmax values, rounded once to fp32 (nearest-even),
@@ -355,25 +396,23 @@ __device__ float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nbloc
   return __uint_as_float(bits);
 }
 
-// One workgroup of 1024 threads: thread t sums the 16-byte piece t % 8 (slots
-// 2(t%8) and 2(t%8)+1) of rows t/8, t/8 + 128, ... (at most 2049 rows: all of a
-// thread's seventeen loads in flight at once), the 128 partial sums of each
-// slot are added through LDS in two stages, and one thread resolves the
-// carries and forms the mean.  Integer sums: the order does not matter.
-// (Two dependent rounds of 8-byte loads took ~8.4 us.)  (Spreading the loads over
-// several workgroups that meet through an arrival counter measured slower: the
-// fence, the atomic and the re-read cost more than the loads.)
+// The exact mean of the rows' total, in every thread of a workgroup of 1024
+// threads: thread t sums the 16-byte piece t % 8 (slots 2(t%8) and 2(t%8)+1)
+// of rows t/8, t/8 + 128, ... (at most 2048 rows: all of a thread's loads in
+// flight at once), the 128 partial sums of each slot are added through LDS in
+// two stages, and one thread resolves the carries and forms the mean, which
+// it hands to the others through LDS.  Integer sums: the order does not
+// matter, so every workgroup that runs this gets the same bits.
 constexpr int kMeanThreads = 1024;
 
-__global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigned long long *__restrict__ partials,
-                                                                  int nrows, uint32_t nblocks,
-                                                                  float *__restrict__ mean_out) {
+__device__ float mean_of_rows(const unsigned long long *__restrict__ partials, int nrows, uint32_t nblocks) {
   static_assert(kMeanSlots == 16, "a row is eight 16-byte pieces of two slots");
   constexpr int RL = kMeanThreads / 8;                          // 128 rows per pass
-  constexpr int P = (kQuantGridMax + 1 + RL - 1) / RL;          // passes for the most rows (17)
+  constexpr int P = (kQuantGridMax + RL - 1) / RL;              // passes for the most rows (16)
   __shared__ unsigned long long red[RL][kMeanSlots];
+  __shared__ unsigned long long slot_sum[kMeanSlots];
+  __shared__ float mean_lds;
   const int t = threadIdx.x, pc = t & 7, rl = t >> 3;           // slots 2pc, 2pc+1 of rows rl + 128 i
-  // every load of the thread in flight at once: one memory round trip
   ulonglong2 v[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) {
@@ -381,7 +420,7 @@ __global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigne
     v[i] = r < nrows ? reinterpret_cast<const ulonglong2 *>(partials + (int64_t)r * kMeanSlots)[pc]
                      : make_ulonglong2(0ull, 0ull);
   }
-  unsigned long long a0 = 0, a1 = 0;   // every row slot is below 2^41 and there are at most 2049 rows
+  unsigned long long a0 = 0, a1 = 0;   // every row slot is below 2^41 and there are at most 2048 rows
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     a0 += v[i].x;
@@ -400,6 +439,13 @@ __global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigne
   __syncthreads();
   if (t < 16 * 16) red[t >> 4][t & 15] = w;
   __syncthreads();
+  if (t < kMeanSlots) {          // slot t over the 16 partial rows
+    unsigned long long slot = 0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) slot += red[g][t];
+    slot_sum[t] = slot;
+  }
+  __syncthreads();
   if (t == 0) {
     // S * 2^32: digit 0 is zero, digit i + 1 is slot i after the carries
     uint32_t num[kMeanWords];
@@ -407,69 +453,84 @@ __global__ __launch_bounds__(kMeanThreads) void mean_reduce_kernel(const unsigne
     unsigned long long carry = 0;
 #pragma unroll
     for (int i = 0; i < kMeanWords - 1; ++i) {
-      unsigned long long slot = 0;
-      if (i < kMeanSlots) {
-#pragma unroll
-        for (int g = 0; g < 16; ++g) slot += red[g][i];
-      }
-      const unsigned long long cur = slot + carry;
+      const unsigned long long cur = (i < kMeanSlots ? slot_sum[i] : 0ull) + carry;
       num[i + 1] = (uint32_t)cur;
       carry = cur >> 32;
     }
-    *mean_out = mean_from_digits(num, nblocks);
+    mean_lds = mean_from_digits(num, nblocks);
   }
+  __syncthreads();
+  return mean_lds;
 }
 
-// One wave per group of 256 absmax values.
-__global__ __launch_bounds__(64) void double_quant_kernel(const float *__restrict__ absmax,
-                                                          int64_t nblocks,
-                                                          const float *__restrict__ mean,
-                                                          int8_t *__restrict__ q_out,
-                                                          float *__restrict__ scale_out) {
-  const int lane = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * kGroup + lane * 4;
-  const float mu = *mean;
-  float ac[4];
-  float m = 0.f;
+// Double quantization with the mean formed in place: every workgroup (1024
+// threads) computes the exact mean from the rows, workgroup 0 stores it, and
+// wave w of workgroup b quantizes groups b * 16 + w, b * 16 + w + 16 * grid,
+// ... of 256 absmax values: a' = fp32(a - mu), s = fp32(max|a'| / 127),
+// q = clamp(rint(fp32(a' / s)), -127, 127); an all-zero group has s = 0, q = 0.
+__global__ __launch_bounds__(kMeanThreads) void mean_dq_kernel(const unsigned long long *__restrict__ partials,
+                                                              int nrows, const float *__restrict__ absmax,
+                                                              int64_t nblocks, int8_t *__restrict__ q_out,
+                                                              float *__restrict__ scale_out,
+                                                              float *__restrict__ mean_out) {
+  const float mu = mean_of_rows(partials, nrows, (uint32_t)nblocks);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
+  const int lane = threadIdx.x & 63;
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  const int64_t step = (int64_t)gridDim.x * (kMeanThreads / 64);
+  for (int64_t g = (int64_t)blockIdx.x * (kMeanThreads / 64) + (threadIdx.x >> 6); g < ngroups; g += step) {
+    const int64_t base = g * kGroup + lane * 4;
+    float ac[4];
+    float m = 0.f;
+    if (base + 3 < nblocks) {
+      const float4 a = *reinterpret_cast<const float4 *>(absmax + base);
+      ac[0] = __fsub_rn(a.x, mu); ac[1] = __fsub_rn(a.y, mu);
+      ac[2] = __fsub_rn(a.z, mu); ac[3] = __fsub_rn(a.w, mu);
+    } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ac[i] = (base + i < nblocks) ? __fsub_rn(absmax[base + i], mu) : 0.f;
-    m = fmaxf(m, fabsf(ac[i]));
-  }
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
-  const float s = __fdiv_rn(m, 127.0f);
-  if (lane == 0) scale_out[blockIdx.x] = s;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (base + i >= nblocks) break;
-    int qv = 0;
-    if (m != 0.f) {
-      float r = rintf(__fdiv_rn(ac[i], s));
-      r = fminf(fmaxf(r, -127.f), 127.f);
-      qv = (int)r;
+      for (int i = 0; i < 4; ++i) ac[i] = (base + i < nblocks) ? __fsub_rn(absmax[base + i], mu) : 0.f;
     }
-    q_out[base + i] = (int8_t)qv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(ac[i]));
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+    const float s = __fdiv_rn(m, 127.0f);
+    if (lane == 0) scale_out[g] = s;
+    int qv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[i] = 0;
+      if (m != 0.f) {
+        float r = rintf(__fdiv_rn(ac[i], s));
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        qv[i] = (int)r;
+      }
+    }
+    if (base + 3 < nblocks) {
+      *reinterpret_cast<uint32_t *>(q_out + base) =
+          (uint32_t)(qv[0] & 0xff) | (uint32_t)(qv[1] & 0xff) << 8 | (uint32_t)(qv[2] & 0xff) << 16 |
+          (uint32_t)(qv[3] & 0xff) << 24;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (base + i < nblocks) q_out[base + i] = (int8_t)qv[i];
+    }
   }
 }
 
+// Workgroups of the double-quantization launch: each one re-derives the mean
+// from the rows (at most 2048 x 128 bytes), so they are kept few.
+constexpr int kDqGridMax = 256;
 
 template <bool BF16, bool DQ, bool FP4>
-void launch_full(int lbs, int grid, int64_t numel, int64_t nfull, int bs, hipStream_t stream, const void *w,
-                 uint8_t *packed, float *absmax_out, unsigned long long *partials, uint32_t *status) {
-  if (nfull > 0) {
-    const dim3 g((unsigned)grid), b(256);
-    switch (lbs) {
-      case 5: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 4, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-      case 6: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 8, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-      case 7: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 16, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-      default: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 32, FP4>), g, b, 0, stream, w, nfull, packed, absmax_out, partials, status); break;
-    }
-  }
-  if (nfull * bs < numel) {   // the partial last block, with its own accumulator row
-    unsigned long long *row = partials ? partials + (int64_t)grid * kMeanSlots : nullptr;
-    hipLaunchKernelGGL((quantize_tail_kernel<BF16, DQ, FP4>), dim3(1), dim3(256), 0, stream, w, numel, nfull, bs,
-                       packed, absmax_out, row, status);
+void launch_blocks(int lbs, int grid, int64_t numel, int64_t nfull, hipStream_t stream, const void *w,
+                   uint8_t *packed, float *absmax_out, unsigned long long *partials, uint32_t *status) {
+  const dim3 g((unsigned)grid), b(256);
+  switch (lbs) {
+    case 5: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 4, FP4>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, partials, status); break;
+    case 6: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 8, FP4>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, partials, status); break;
+    case 7: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 16, FP4>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, partials, status); break;
+    default: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 32, FP4>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, partials, status); break;
   }
 }
 
@@ -483,25 +544,23 @@ hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs,
   const int64_t nblocks = (numel + bs - 1) / bs;
   const int64_t nfull = numel / bs;
   const int bpi = 256 / (bs / 8);   // blocks per quantize workgroup and iteration
-  int grid = 0;
-  if (nfull > 0) {
-    const int64_t g64 = (nfull + bpi - 1) / bpi;
-    grid = (int)(g64 < kQuantGridMax ? g64 : kQuantGridMax);
-  }
-  using L = void (*)(int, int, int64_t, int64_t, int, hipStream_t, const void *, uint8_t *, float *,
+  // at least one workgroup: the last one also takes the partial block at the end
+  const int64_t g64 = (nfull + bpi - 1) / bpi;
+  const int grid = (int)(g64 < 1 ? 1 : (g64 < kQuantGridMax ? g64 : kQuantGridMax));
+  using L = void (*)(int, int, int64_t, int64_t, hipStream_t, const void *, uint8_t *, float *,
                      unsigned long long *, uint32_t *);
-  static const L full[2][2][2] = {{{launch_full<false, false, false>, launch_full<false, false, true>},
-                                   {launch_full<false, true, false>, launch_full<false, true, true>}},
-                                  {{launch_full<true, false, false>, launch_full<true, false, true>},
-                                   {launch_full<true, true, false>, launch_full<true, true, true>}}};
-  full[w_is_bf16 ? 1 : 0][dq ? 1 : 0][fp4 ? 1 : 0](lbs, grid, numel, nfull, bs, stream, w, packed, absmax_out,
-                                                   partials, status);
-  const int rows = grid + (nfull < nblocks ? 1 : 0);
+  static const L blocks[2][2][2] = {{{launch_blocks<false, false, false>, launch_blocks<false, false, true>},
+                                     {launch_blocks<false, true, false>, launch_blocks<false, true, true>}},
+                                    {{launch_blocks<true, false, false>, launch_blocks<true, false, true>},
+                                     {launch_blocks<true, true, false>, launch_blocks<true, true, true>}}};
+  blocks[w_is_bf16 ? 1 : 0][dq ? 1 : 0][fp4 ? 1 : 0](lbs, grid, numel, nfull, stream, w, packed, absmax_out,
+                                                     partials, status);
   if (dq) {
-    hipLaunchKernelGGL(mean_reduce_kernel, dim3(1), dim3(kMeanThreads), 0, stream, partials, rows, (uint32_t)nblocks,
-                       mean_out);
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-    hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ngroups), dim3(64), 0, stream, absmax_out, nblocks, mean_out, q_out, scale_out);
+    const int64_t dq_need = (ngroups + kMeanThreads / 64 - 1) / (kMeanThreads / 64);
+    const int dq_grid = (int)(dq_need < kDqGridMax ? dq_need : kDqGridMax);
+    hipLaunchKernelGGL(mean_dq_kernel, dim3((unsigned)dq_grid), dim3(kMeanThreads), 0, stream, partials, grid,
+                       absmax_out, nblocks, q_out, scale_out, mean_out);
   }
   return hipGetLastError();
 }
