@@ -15,7 +15,9 @@ with events only at the two ends).  The same JSON line carries per-kernel
 timings (HIP events around every launch of a second pass of as many steps), the
 dequantizer, the rank-64 adapter variants of both GEMMs, the decode-shape
 forward (M = 1, 4, 16 on a rotating pool of 512 quantized 4096x4096 weights,
-replayed from a HIP graph so host launch overhead does not count), the
+replayed from a HIP graph so host launch overhead does not count; and each
+dispatch's own duration from a rocprofv3 kernel trace of a child process), a
+plain HBM read stream (the achievable bandwidth), the
 outlier-heavy large shape (M = K = 8192, N = 28672, fp32 Student-t weight), the
 32-layer bulk quantize/dequantize round trip, the prefill workload at block sizes
 32, 128 and 256, a roofline entry for the dominant
@@ -395,6 +397,93 @@ def bench_blocksizes(dg, reps=5):
     return {"blocksize_variants": out}
 
 
+def bench_read_stream(reps=5, gib=4):
+    """The achievable HBM read bandwidth: a plain read stream (libnf4_bench) over a 4 GiB buffer
+    (16x the 256 MB last-level cache), best of a few launch shapes."""
+    import ctypes
+    from dequant_gemm_amd.build import BENCH_LIB
+    if not os.path.exists(BENCH_LIB):
+        raise RuntimeError(f"{BENCH_LIB} is missing: build with `python -m dequant_gemm_amd.build`")
+    L = ctypes.CDLL(BENCH_LIB)
+    L.nf4bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    L.nf4bench_read_stream.restype = ctypes.c_int
+    d = torch.device("cuda:0")
+    nbytes = gib << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=d)
+    shapes = ((1024, 256), (2048, 256), (4096, 256), (1024, 512), (2048, 512), (1024, 1024))
+    sink = torch.empty(max(g * b for g, b in shapes), dtype=torch.int32, device=d)
+    stream = torch.cuda.current_stream(d).cuda_stream
+    best = None
+    for grid, block in shapes:
+        assert grid * block <= sink.numel()
+        call = lambda: L.nf4bench_read_stream(src.data_ptr(), nbytes, sink.data_ptr(), grid, block, stream)
+        if call() != 0:
+            raise RuntimeError("nf4bench_read_stream failed")
+        torch.cuda.synchronize()
+        ms = time_events(call, reps)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbps > best["GB/s"]:
+            best = {"GB/s": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "grid": grid, "block": block,
+                    "bytes": nbytes, "what": "plain 16-byte-load read stream, best launch shape"}
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"hbm_read_stream": best}
+
+
+DECODE_TRACE_KERNELS = ("fwd_small_kernel",)   # the small-M forward's kernel names
+DECODE_TRACE_POOL, DECODE_TRACE_ROUNDS = 64, 4
+
+
+def decode_kernel_trace(timeout_s=300):
+    """Decode kernel durations from the profiler: a child process runs the decode calls
+    (M = 1, 4, 16 over a pool of 64 quantized 4096x4096 weights, eager launches) under
+    `rocprofv3 --kernel-trace`; each dispatch's begin-to-end time excludes launch gaps.
+    Runs before this process touches the GPU."""
+    import csv
+    import glob
+    import shutil
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return {"decode_kernel_trace": None, "decode_kernel_trace_error": "rocprofv3 not found"}
+    out = tempfile.mkdtemp(prefix="nf4_decode_trace_")
+    cmd = [prof, "--kernel-trace", "--output-format", "csv", "-d", out, "-o", "decode", "--",
+           sys.executable, os.path.abspath(__file__), "--op", "decode_trace"]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout_s, cwd="/tmp",
+                           env=dict(os.environ, TMPDIR="/tmp"))
+        files = glob.glob(os.path.join(out, "**", "*kernel_trace.csv"), recursive=True)
+        if not files:
+            return {"decode_kernel_trace": None,
+                    "decode_kernel_trace_error": f"no trace (rc {r.returncode}): {r.stderr[-300:]}"}
+        rows = [x for x in csv.DictReader(open(files[0]))
+                if any(k in x["Kernel_Name"] for k in DECODE_TRACE_KERNELS)]
+        rows.sort(key=lambda x: int(x["Start_Timestamp"]))
+        per_m = DECODE_TRACE_POOL * DECODE_TRACE_ROUNDS
+        import synth
+        if len(rows) != per_m * len(synth.DECODE_MS):
+            return {"decode_kernel_trace": None,
+                    "decode_kernel_trace_error": f"expected {per_m * len(synth.DECODE_MS)} dispatches, got {len(rows)}"}
+        res = {}
+        K, N = synth.DECODE_K, synth.DECODE_N
+        for i, M in enumerate(synth.DECODE_MS):
+            # the first round over the pool is a warm-up
+            d = [(int(x["End_Timestamp"]) - int(x["Start_Timestamp"])) * 1e-3
+                 for x in rows[i * per_m + DECODE_TRACE_POOL:(i + 1) * per_m]]
+            us = float(np.median(d))
+            b = M * K * 2 + wq_bytes(N, K) + M * N * 4
+            res[f"decode_m{M}"] = {"kernel_us_median": us, "kernel_us_min": float(np.min(d)),
+                                   "GB/s": b / (us * 1e-6) / 1e9, "frac_hbm": b / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                                   "dispatches": len(d)}
+        return {"decode_kernel_trace": res}
+    except (subprocess.TimeoutExpired, OSError, KeyError, ValueError) as e:
+        return {"decode_kernel_trace": None, "decode_kernel_trace_error": repr(e)[:300]}
+    finally:
+        shutil.rmtree(out, ignore_errors=True)
+
+
 def cpu_baseline(target_s=12.0):
     """The oracle, as it stands, on a bounded sample of the prefill workload."""
     import oracle as O
@@ -466,6 +555,22 @@ def run_single_op(dg, op, steps, warmup):
         src = torch.empty(1 << 28, dtype=torch.float32, device=d).fill_(1.0)
         dst = torch.empty_like(src)
         fn = lambda i: dst.copy_(src)
+    elif op == "decode_trace":
+        # the decode calls for the kernel trace: a pool of quantized 4096x4096 weights, M = 1, 4, 16,
+        # eager launches, a fixed number of rounds over the pool per M
+        import synth as S
+        K, N = S.DECODE_K, S.DECODE_N
+        qs = [dg.nf4_quantize(_device_normal((N, K), 0.02, 1000 + p, d)) for p in range(DECODE_TRACE_POOL)]
+        for M in S.DECODE_MS:
+            X = S.decode_x(M).to(d)
+            Y = torch.empty((M, N), dtype=torch.float32, device=d)
+            torch.cuda.synchronize()
+            for _ in range(DECODE_TRACE_ROUNDS):
+                for q in qs:
+                    dg.nf4_matmul_fwd(X, q, out=Y)
+            torch.cuda.synchronize()
+        print(json.dumps({"op": op, "calls_per_m": DECODE_TRACE_POOL * DECODE_TRACE_ROUNDS}), flush=True)
+        return
     elif op == "decode":
         K, N = synth.DECODE_K, synth.DECODE_N
         qs = [dg.nf4_quantize(w.to(d)) for w in synth.parallel(synth.decode_weight, range(16))]
@@ -522,13 +627,18 @@ def main():
     ap.add_argument("--no-large", action="store_true", help="skip the 8192x8192x28672 outlier-heavy shape")
     ap.add_argument("--no-bulk", action="store_true", help="skip the 32-layer quantize/dequantize round trip")
     ap.add_argument("--no-blocksizes", action="store_true", help="skip the block-size 32/128/256 variants")
-    ap.add_argument("--op", default=None, choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "copy"],
+    ap.add_argument("--no-decode-trace", action="store_true",
+                    help="skip the profiler run that takes the decode kernels' own durations")
+    ap.add_argument("--op", default=None,
+                    choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "decode_trace", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the NF4 path here is built and timed on a single "
               "MI355X (no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    # the profiler child runs first, while this process has not touched the GPU
+    trace = decode_kernel_trace() if not (a.op or a.no_decode or a.no_decode_trace) else None
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
@@ -543,6 +653,9 @@ def main():
     ops = pre["ops"]
     if not a.no_decode:
         ops.update(bench_decode(dg))
+    if trace is not None:
+        ops.update(trace)
+    ops.update(bench_read_stream())
     if not a.no_large:
         ops.update(bench_large(dg))
     if not a.no_bulk:

@@ -24,6 +24,9 @@ LIB = os.path.join(PKG, "libnf4.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["nf4_api.hip", "quantize.hip", "dequantize.hip", "gemm_fwd.hip", "gemm_bwd.hip"]
+# the benchmark's HBM read stream, a library of its own (include/nf4_bench.h)
+BENCH_SOURCES = ["bench_stream.hip"]
+BENCH_LIB = os.path.join(PKG, "libnf4_bench.so")
 HEADERS = ["nf4_common.h", "nf4_launch.h"]
 
 ARCH = "gfx950"
@@ -71,14 +74,16 @@ def _run(cmd):
 
 
 def build(asm_dir: str | None = None, verbose: bool = True) -> str:
-    """Compiles every source and links libnf4.so; returns its path."""
+    """Compiles every source and links libnf4.so (and the benchmark's libnf4_bench.so); returns
+    the path of libnf4.so."""
     lib = LIB
     os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm_dir), SOURCES))
-    tmp = lib + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, lib)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES + BENCH_SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, asm_dir), SOURCES + BENCH_SOURCES))
+    for out, part in ((lib, objs[:len(SOURCES)]), (BENCH_LIB, objs[len(SOURCES):])):
+        tmp = out + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *part])
+        os.replace(tmp, out)
     if verbose:
         print(f"built {lib}")
     return lib

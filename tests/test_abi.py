@@ -242,3 +242,28 @@ def test_lowrank_gemm_errors(L, fn):
     # M == 0: a successful no-op once the rank is valid
     assert f(None, 0, ctypes.byref(q), None, None, 32, None, 0, None) == 0
     assert f(None, 0, ctypes.byref(q), None, None, 17, None, 0, None) == 7
+
+
+def test_bench_stream_library_exports_and_refuses_bad_arguments():
+    """libnf4_bench (include/nf4_bench.h): every declared call is exported, and every bad
+    argument is refused with status 1 before anything is launched."""
+    from dequant_gemm_amd.build import BENCH_LIB
+    if not os.path.exists(BENCH_LIB):
+        pytest.fail("libnf4_bench.so is not built (run `python -m dequant_gemm_amd.build`)")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "nf4_bench.h")).read(), flags=re.S)
+    declared = set(re.findall(r"\b(nf4bench_[a-z0-9_]+)\s*\(", text))
+    out = subprocess.run(["nm", "-D", "--defined-only", BENCH_LIB], capture_output=True, text=True).stdout
+    assert declared and declared <= set(re.findall(r"\bT (nf4bench_[a-z0-9_]+)$", out, flags=re.M))
+    B = ctypes.CDLL(BENCH_LIB)
+    f = B.nf4bench_read_stream
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 1 << 20, P, 256, 256, None) == 1
+    assert f(P, 1 << 20, None, 256, 256, None) == 1
+    assert f(P, 0, P, 256, 256, None) == 1
+    assert f(P, (1 << 20) + 8, P, 256, 256, None) == 1     # not a multiple of 16
+    assert f(P + 4, 1 << 20, P, 256, 256, None) == 1        # misaligned source
+    assert f(P, 1 << 20, P + 4, 256, 256, None) == 1        # misaligned sink
+    assert f(P, 1 << 20, P, 256, 100, None) == 1            # block size
+    assert f(P, 1 << 20, P, 0, 256, None) == 1              # grid
+    assert f(P, 1 << 20, P, 65537, 256, None) == 1
