@@ -15,7 +15,7 @@ from ._lib import (  # noqa: F401
     BLOCKSIZE, BLOCKSIZES, DQ_GROUP, EXPORTS, LIB_PATH, NF4Error, QTensor, QTensorStruct, QUANT_TYPES,
     LORA_MAX_RANK, LORA_RANK_STEP, empty_qtensor, lib, nf4_codebook, nf4_levels, nf4_dequantize, nf4_matmul_bwd_dx,
     nf4_matmul_bwd_dx_lora, nf4_matmul_fwd, nf4_matmul_fwd_lora, nf4_quantize, nf4_quantize_noalloc, nf4_sizes, nf4_thresholds,
-    NOALLOC_MAX_BLOCKS,
+    NOALLOC_MAX_BLOCKS, nf4_adapter_matmul,
 )
 from .io import load_qtensor, load_qtensors, save_qtensor, save_qtensors  # noqa: F401,E402
 from .nn import NF4Linear, NF4LoraLinear, nf4_linear, quantize_linears  # noqa: F401,E402

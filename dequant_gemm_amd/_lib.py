@@ -34,7 +34,7 @@ STATUS_NAMES = {
 
 EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_levels", "nf4_thresholds", "nf4_sizes", "nf4_quantize",
            "nf4_quantize_noalloc", "nf4_dequantize", "nf4_matmul_fwd", "nf4_matmul_bwd_dx", "nf4_matmul_fwd_lora",
-           "nf4_matmul_bwd_dx_lora")
+           "nf4_matmul_bwd_dx_lora", "nf4_adapter_matmul")
 LORA_RANK_STEP = 16
 LORA_MAX_RANK = 1024
 NOALLOC_MAX_BLOCKS = 1 << 22     # NF4_NOALLOC_MAX_BLOCKS: blocks nf4_quantize_noalloc's scratch holds
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.nf4_matmul_bwd_dx.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, i32, vp]
         L.nf4_matmul_fwd_lora.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, vp, i64, vp, i32, vp]
         L.nf4_matmul_bwd_dx_lora.argtypes = [vp, i64, ctypes.POINTER(QTensorStruct), vp, vp, i64, vp, i32, vp]
+        L.nf4_adapter_matmul.argtypes = [i32, i32, i64, i64, i64, ctypes.c_float, vp, i64, vp, i64, vp, i32, i64, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -405,3 +406,39 @@ def nf4_matmul_bwd_dx_lora(dY: torch.Tensor, q: QTensor, V: torch.Tensor, At: to
                                         out.data_ptr(), _dtype_enum(out.dtype), _stream(dY.device)),
            "nf4_matmul_bwd_dx_lora")
     return out
+
+
+def _row_strided(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a 2-D device bf16 tensor whose rows are contiguous."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D bf16 tensor")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name} must have contiguous rows (stride 1 along its last dimension)")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def nf4_adapter_matmul(A: torch.Tensor, B: torch.Tensor, trans_a: bool = False, trans_b: bool = False,
+                       alpha: float = 1.0, out_dtype: torch.dtype = torch.float32,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = alpha op(A) op(B) (the adapter's dense products), op the identity or the transpose.
+
+    A and B are 2-D bf16 device tensors with contiguous rows; op(A) is A.T when
+    ``trans_a`` (A stored [K, M]), op(B) is B.T when ``trans_b`` (B stored [N, K]).
+    """
+    lda, ldb = _row_strided(A, "A"), _row_strided(B, "B")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    Kb, N = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+    if Kb != K:
+        raise ValueError(f"op(A) is [{M}, {K}] and op(B) is [{Kb}, {N}]: reduction sizes differ")
+    if A.device != B.device:
+        raise ValueError(f"A is on {A.device}, B on {B.device}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _require_out(out, M * N, A.device)
+    _check(lib().nf4_adapter_matmul(int(trans_a), int(trans_b), M, N, K, float(alpha), A.data_ptr(), lda,
+                                    B.data_ptr(), ldb, out.data_ptr(), _dtype_enum(out.dtype), N,
+                                    _stream(A.device)), "nf4_adapter_matmul")
+    return out
+

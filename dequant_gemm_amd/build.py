@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnf4.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["nf4_api.hip", "quantize.hip", "dequantize.hip", "gemm_fwd.hip", "gemm_bwd.hip"]
+SOURCES = ["nf4_api.hip", "quantize.hip", "dequantize.hip", "gemm_fwd.hip", "gemm_bwd.hip", "adapter.hip"]
 # the benchmark's HBM read stream, a library of its own (include/nf4_bench.h)
 BENCH_SOURCES = ["bench_stream.hip"]
 BENCH_LIB = os.path.join(PKG, "libnf4_bench.so")

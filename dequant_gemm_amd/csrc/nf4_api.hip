@@ -281,4 +281,25 @@ int nf4_matmul_bwd_dx_lora(const void *dY, int64_t M, const nf4_qtensor *q, cons
                                        dx_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int nf4_adapter_matmul(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                       int64_t lda, const void *B, int64_t ldb, void *C, int c_dtype, int64_t ldc, void *stream) {
+  if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return NF4_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return NF4_ERR_SHAPE;
+  if (!valid_dtype(c_dtype)) return NF4_ERR_DTYPE;
+  // stored shapes: A [M, K] or [K, M]; B [K, N] or [N, K]; rows of `ld` elements
+  const int64_t a_rows = trans_a ? K : M, a_cols = trans_a ? M : K;
+  const int64_t b_rows = trans_b ? N : K, b_cols = trans_b ? K : N;
+  if (lda < a_cols || ldb < b_cols || ldc < N || lda < 1 || ldb < 1 || ldc < 1) return NF4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NF4_OK;
+  if (!A || !B || !C) return NF4_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return NF4_ERR_ALIGN;
+  const int64_t lim = ((int64_t)1 << 31) / 2;   // 32-bit byte offsets into each stored operand
+  if (a_rows > lim / lda || b_rows > lim / ldb) return NF4_ERR_UNSUPPORTED;
+  if (((M + 63) / 64) * ((N + 63) / 64) > kMaxDim) return NF4_ERR_UNSUPPORTED;
+  const bool va = a_cols % 8 == 0 && lda % 8 == 0;   // 16-byte loads of whole rows
+  const bool vb = b_cols % 8 == 0 && ldb % 8 == 0;
+  return hip_status(nf4::launch_adapter_gemm(trans_a, trans_b, M, N, K, alpha, A, lda, va, B, ldb, vb, C, ldc,
+                                             c_dtype == NF4_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

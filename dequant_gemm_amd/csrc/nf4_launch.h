@@ -39,4 +39,9 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
                          const AbsmaxSrc &src, const LowRank &lr, void *dx, int dx_is_bf16,
                          hipStream_t stream);
 
+// C = alpha op(A) op(B), bf16 operands, fp32 accumulation (adapter.hip).
+hipError_t launch_adapter_gemm(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void *a,
+                               int64_t lda, bool va, const void *b, int64_t ldb, bool vb, void *c, int64_t ldc,
+                               bool c_bf16, hipStream_t stream);
+
 }  // namespace nf4

@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-from ._lib import (LORA_MAX_RANK, LORA_RANK_STEP, QTensor, nf4_matmul_bwd_dx, nf4_matmul_bwd_dx_lora,
+from ._lib import (LORA_MAX_RANK, LORA_RANK_STEP, QTensor, nf4_adapter_matmul, nf4_matmul_bwd_dx, nf4_matmul_bwd_dx_lora,
                    nf4_matmul_fwd, nf4_matmul_fwd_lora, nf4_quantize)
 
 
@@ -118,11 +118,11 @@ class NF4Linear(torch.nn.Module):
 class _NF4LoraMatmul(torch.autograd.Function):
     """y = x W^T + s (x A^T) B^T with the adapter term added inside the fused GEMM.
 
-    The down projection U = bf16(s * x A^T) and, in the backward, V = bf16(s * dy B)
-    are small dense products computed by torch in fp32 and rounded once; the
-    fused kernels then add U B^T (forward) and V A (backward) in their fp32
-    accumulators.  The adapter's own gradients, dA = V^T x and dB = dy^T U
-    (with s folded into U and V), are small dense products left to torch.
+    Every product runs in libnf4: the down projection U = bf16(s x A^T)
+    (nf4_adapter_matmul), the fused forward adding U B^T; in the backward
+    V = bf16(s dy B), the fused input gradient adding V A, and the adapter's
+    gradients dA = V^T x and dB = dy^T U (nf4_adapter_matmul, bf16 outputs).
+    torch supplies memory and the stream.
     """
 
     @staticmethod
@@ -131,26 +131,24 @@ class _NF4LoraMatmul(torch.autograd.Function):
         x2 = x.reshape(-1, q.cols)
         if not x2.is_contiguous():
             x2 = x2.contiguous()
-        xa = x2.float() @ lora_a.float().t()                 # [M, r] in fp32
-        u = (xa * scaling).to(torch.bfloat16)
+        u = nf4_adapter_matmul(x2, lora_a, trans_b=True, alpha=scaling, out_dtype=torch.bfloat16)   # [M, r]
         y = nf4_matmul_fwd_lora(x2, q, u, lora_b.contiguous(), out_dtype)
-        ctx.save_for_backward(x2, lora_a, lora_b, xa)
+        ctx.save_for_backward(x2, lora_a, lora_b, u)
         ctx.q, ctx.lead, ctx.scaling = q, lead, scaling
         return y.reshape(*lead, q.rows)
 
     @staticmethod
     def backward(ctx, gy):
-        x2, lora_a, lora_b, xa = ctx.saved_tensors
+        x2, lora_a, lora_b, u = ctx.saved_tensors
         q, s = ctx.q, ctx.scaling
         g2 = gy.reshape(-1, q.rows)
-        g32 = g2.float()
         gb = g2 if g2.dtype == torch.bfloat16 else g2.to(torch.bfloat16)
         if not gb.is_contiguous():
             gb = gb.contiguous()
-        v32 = (g32 @ lora_b.float()) * s                    # [M, r]
-        dx = nf4_matmul_bwd_dx_lora(gb, q, v32.to(torch.bfloat16), lora_a.t().contiguous(), torch.bfloat16)
-        d_a = (v32.t() @ x2.float()).to(lora_a.dtype)       # [r, K]
-        d_b = ((g32.t() @ xa) * s).to(lora_b.dtype)         # [N, r]
+        v = nf4_adapter_matmul(gb, lora_b.contiguous(), alpha=s, out_dtype=torch.bfloat16)         # [M, r]
+        dx = nf4_matmul_bwd_dx_lora(gb, q, v, lora_a.t().contiguous(), torch.bfloat16)
+        d_a = nf4_adapter_matmul(v, x2, trans_a=True, out_dtype=lora_a.dtype)                        # [r, K]
+        d_b = nf4_adapter_matmul(gb, u, trans_a=True, out_dtype=lora_b.dtype)                        # [N, r]
         return dx.reshape(*ctx.lead, q.cols), d_a, d_b, None, None, None
 
 

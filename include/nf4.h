@@ -277,12 +277,38 @@ int nf4_matmul_fwd_lora(const void *X, int64_t M, const nf4_qtensor *q,
  * adapter's contribution added in the same accumulators.  For the adapter of
  * nf4_matmul_fwd_lora, V = dY B (device bf16 [M, r]) and At = A^T (device
  * bf16 [K, r] with K = q->cols), both row-major.  dY, dX, dx_dtype and the
- * shape rules as nf4_matmul_bwd_dx; r as nf4_matmul_fwd_lora.  The gradients
- * of the adapter itself are small dense products left to the caller.
+ * shape rules as nf4_matmul_bwd_dx; r as nf4_matmul_fwd_lora.  The
+ * adapter's own products (U, V and its gradients) are nf4_adapter_matmul.
  */
 int nf4_matmul_bwd_dx_lora(const void *dY, int64_t M, const nf4_qtensor *q,
                            const void *V, const void *At, int64_t r, void *dX,
                            int dx_dtype, void *stream);
+
+/*
+ * C = alpha op(A) op(B): the dense products of a low-rank adapter on the
+ * frozen 4-bit weight ("bitsandbytes" page, 4-bit/LoRA paragraph: a frozen
+ * 4-bit base weight with small trainable adapters).  For an adapter with down
+ * projection Ad [r, K] and up projection Bu [N, r] (scale s) on input X [M, K]
+ * and output gradient dY [M, N]:
+ *   U  = s X Ad^T  (trans_a 0, trans_b 1)   the activation nf4_matmul_fwd_lora adds
+ *   V  = s dY Bu   (trans_a 0, trans_b 0)   the activation nf4_matmul_bwd_dx_lora adds
+ *   dAd = V^T X    (trans_a 1, trans_b 0)   gradient of the down projection
+ *   dBu = dY^T U   (trans_a 1, trans_b 0)   gradient of the up projection
+ * op(A) is [M, K]: A (trans_a = 0, stored [M, K]) or A^T (trans_a = 1, stored
+ * [K, M]); op(B) is [K, N]: B (trans_b = 0, stored [K, N]) or B^T (trans_b =
+ * 1, stored [N, K]).  A and B are device bf16, row-major with row strides lda
+ * and ldb elements (at least the stored row length); C is device [M, N] with
+ * row stride ldc >= N in c_dtype: NF4_F32, or NF4_BF16 = one round-to-nearest-
+ * even rounding of the fp32 value.  Products accumulate in fp32 on the bf16
+ * matrix cores; alpha multiplies the fp32 sum once.  M or N == 0 is a
+ * successful no-op; K >= 1.  Errors: NF4_ERR_UNSUPPORTED (trans flag not 0 or
+ * 1, a stored operand of 2^31 bytes or more), NF4_ERR_SHAPE (negative size,
+ * K < 1, a stride shorter than its row), NF4_ERR_DTYPE, NF4_ERR_NULL,
+ * NF4_ERR_ALIGN (A, B and C 16-byte aligned).
+ */
+int nf4_adapter_matmul(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void *A, int64_t lda, const void *B,
+                       int64_t ldb, void *C, int c_dtype, int64_t ldc, void *stream);
 
 #ifdef __cplusplus
 }

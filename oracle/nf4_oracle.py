@@ -51,6 +51,9 @@ the design notes of the repository):
   gradient dY W^ + (dY B) A.  The fused calls take the bf16 down-projected
   activation U = X A^T (or V = dY B) as given and add U B^T (or V A) in the
   same accumulation; the bound adds the adapter product's magnitude term.
+  The adapter's own products, with a scale s: U = s X A^T, V = s dY B and
+  the gradients of the adapter weights dA = V^T X, dB = dY^T U (the
+  gradient of the forward's U B^T term; U and V as the layer used them).
 * R8 FP4 codebook: the standard 4-bit float E2M1 (one sign bit, two exponent
   bits with bias 1, one mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
   A code is the format's own bit pattern (bit 3 the sign), its level the
@@ -81,6 +84,7 @@ __all__ = [
     "quantize", "dequantize", "nblocks_of", "ngroups_of",
     "matmul_fwd", "matmul_bwd_dx", "fwd_bound", "bwd_dx_bound", "gemm_violations", "ppf_stdlib",
     "matmul_fwd_lora", "matmul_bwd_dx_lora", "fwd_lora_bound", "bwd_dx_lora_bound",
+    "adapter_down", "adapter_down_grad", "adapter_grad_down", "adapter_grad_up", "product_bound",
 ]
 
 DELTA = 0.9677083          # R1: QLoRA's offset, the 7-digit literal
@@ -437,6 +441,31 @@ def fwd_lora_bound(x, w_hat, u, b) -> np.ndarray:
 def bwd_dx_lora_bound(dy, w_hat, v, a_t) -> np.ndarray:
     return bwd_dx_bound(dy, w_hat) + GEMM_RTOL * (np.abs(np.asarray(v, np.float64)) @
                                                   np.abs(np.asarray(a_t, np.float64)).T)
+
+
+def adapter_down(x: np.ndarray, a: np.ndarray, s: float) -> np.ndarray:
+    """U = s X A^T in float64; X [M,K], A [r,K] ([bnb-lora], R7)."""
+    return float(s) * (np.asarray(x, np.float64) @ np.asarray(a, np.float64).T)
+
+
+def adapter_down_grad(dy: np.ndarray, b: np.ndarray, s: float) -> np.ndarray:
+    """V = s dY B in float64; dY [M,N], B [N,r] ([bnb-lora], R7)."""
+    return float(s) * (np.asarray(dy, np.float64) @ np.asarray(b, np.float64))
+
+
+def adapter_grad_down(v: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """dA = V^T X in float64; V [M,r], X [M,K] -> [r,K] ([bnb-lora], R7)."""
+    return np.asarray(v, np.float64).T @ np.asarray(x, np.float64)
+
+
+def adapter_grad_up(dy: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """dB = dY^T U in float64; dY [M,N], U [M,r] -> [N,r] ([bnb-lora], R7)."""
+    return np.asarray(dy, np.float64).T @ np.asarray(u, np.float64)
+
+
+def product_bound(p: np.ndarray, q: np.ndarray, s: float = 1.0) -> np.ndarray:
+    """1e-4 |s| (|P| |Q|) for a product s P Q of two matrices given as P [m,k], Q [k,n] (R6's bound)."""
+    return GEMM_RTOL * abs(float(s)) * (np.abs(np.asarray(p, np.float64)) @ np.abs(np.asarray(q, np.float64)))
 
 
 def gemm_violations(out: np.ndarray, ref: np.ndarray, bound: np.ndarray) -> int:

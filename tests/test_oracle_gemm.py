@@ -156,3 +156,89 @@ def test_lora_bound_rejects_mistakes():
     sq = _bf16(rng, (r, r), 0.1)
     assert O.gemm_violations(O.matmul_fwd(x, w)[:, :r] + u @ sq.astype(np.float64),
                              O.matmul_fwd_lora(x, w[:r], u, sq), O.fwd_lora_bound(x, w[:r], u, sq)) > 0
+
+
+# ------------------------------------------------------------------ the adapter's own products (R7)
+
+def test_adapter_products_against_exact_rationals():
+    rng = np.random.default_rng(13)
+    M, N, K, r, s = 3, 4, 32, 16, 0.5
+    x, a = _bf16(rng, (M, K)), _bf16(rng, (r, K), 0.1)
+    dy, b = _bf16(rng, (M, N)), _bf16(rng, (N, r), 0.1)
+    u, v = _bf16(rng, (M, r)), _bf16(rng, (M, r))
+    F = lambda t: Fraction(float(t))
+    S = F(s)
+    tol = lambda terms: Fraction(len(terms)) * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+    U, V = O.adapter_down(x, a, s), O.adapter_down_grad(dy, b, s)
+    dA, dB = O.adapter_grad_down(v, x), O.adapter_grad_up(dy, u)
+    for i in range(M):
+        for t in range(r):
+            terms = [S * F(x[i, k]) * F(a[t, k]) for k in range(K)]
+            assert abs(F(U[i, t]) - sum(terms)) <= tol(terms)
+            terms = [S * F(dy[i, j]) * F(b[j, t]) for j in range(N)]
+            assert abs(F(V[i, t]) - sum(terms)) <= tol(terms)
+    for t in range(r):
+        for k in range(K):
+            terms = [F(v[i, t]) * F(x[i, k]) for i in range(M)]
+            assert abs(F(dA[t, k]) - sum(terms)) <= tol(terms)
+    for j in range(N):
+        for t in range(r):
+            terms = [F(dy[i, j]) * F(u[i, t]) for i in range(M)]
+            assert abs(F(dB[j, t]) - sum(terms)) <= tol(terms)
+
+
+def test_adapter_gradients_are_the_derivatives_of_the_forward_term():
+    """The adapter term of the forward, T(A, B) = sum(dY * ((s X A^T) B^T)), is linear in A
+    and in B, so a unit change of one entry changes T by exactly that entry's gradient:
+    d/dA_tk = (V^T X)_tk with V = s dY B, and d/dB_jt = (dY^T U)_jt with U = s X A^T.
+    Checked in exact rationals from the forward's definition alone."""
+    rng = np.random.default_rng(14)
+    M, N, K, r, s = 3, 5, 6, 4, 0.25
+    x, a = _bf16(rng, (M, K)), _bf16(rng, (r, K), 0.1)
+    dy, b = _bf16(rng, (M, N)), _bf16(rng, (N, r), 0.1)
+    F = lambda t: Fraction(float(t))
+    X = [[F(x[i, k]) for k in range(K)] for i in range(M)]
+    DY = [[F(dy[i, j]) for j in range(N)] for i in range(M)]
+
+    def T(A, B):
+        U = [[F(s) * sum(X[i][k] * A[t][k] for k in range(K)) for t in range(r)] for i in range(M)]
+        return sum(DY[i][j] * sum(U[i][t] * B[j][t] for t in range(r)) for i in range(M) for j in range(N))
+
+    A0 = [[F(a[t, k]) for k in range(K)] for t in range(r)]
+    B0 = [[F(b[j, t]) for t in range(r)] for j in range(N)]
+    base = T(A0, B0)
+    V = O.adapter_down_grad(dy, b, s)
+    U = O.adapter_down(x, a, s)
+    dA, dB = O.adapter_grad_down(V, x), O.adapter_grad_up(dy, U)
+    for t in range(r):
+        for k in range(K):
+            A1 = [row[:] for row in A0]
+            A1[t][k] += 1
+            assert abs(float(T(A1, B0) - base) - dA[t, k]) <= 1e-12 * (1 + abs(dA[t, k]))
+    for j in range(N):
+        for t in range(r):
+            B1 = [row[:] for row in B0]
+            B1[j][t] += 1
+            assert abs(float(T(A0, B1) - base) - dB[j, t]) <= 1e-12 * (1 + abs(dB[j, t]))
+
+
+def test_adapter_product_bound_rejects_mistakes():
+    rng = np.random.default_rng(15)
+    M, K, r = 64, 512, 32
+    x, a = _bf16(rng, (M, K)), _bf16(rng, (r, K), 0.1)
+    ref = O.adapter_down(x, a, 2.0)
+    bound = O.product_bound(x, a.T, 2.0)
+    # fp32 accumulation passes
+    assert O.gemm_violations((x.astype(np.float32) @ a.T.astype(np.float32)) * np.float32(2.0), ref, bound) == 0
+    # a missing scale and a sign error fail
+    assert O.gemm_violations(ref / 2.0, ref, bound) > 0
+    assert O.gemm_violations(-ref, ref, bound) > 0
+    # a gradient whose reduction pairs the wrong rows (V^T against X with its rows reversed) fails
+    v = _bf16(rng, (M, r))
+    right = O.adapter_grad_down(v, x)
+    assert O.gemm_violations(v.astype(np.float64).T @ x[::-1].astype(np.float64), right,
+                             O.product_bound(v.T, x)) > 0
+    # and so does dB from U with its columns reversed
+    dy, u = _bf16(rng, (M, 48)), _bf16(rng, (M, r))
+    assert O.gemm_violations(O.adapter_grad_up(dy, u[:, ::-1]), O.adapter_grad_up(dy, u),
+                             O.product_bound(dy.T, u)) > 0
