@@ -40,8 +40,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kSmallCols = 16;
 constexpr int kSmallWaves = 8;
 constexpr int kNonTemporal = 2;    // buffer-load cache policy: bit 1 = nt (streaming)
+constexpr size_t kSmallXldsBytes = 131328;   // X staged in LDS: at most 16 rows of 4096 (+16 bytes)
 
-template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4>
+template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4, bool XLDS>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     const uint16_t *__restrict__ X, int M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ Y) {
@@ -110,6 +111,27 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   const uint32_t elane = (uint32_t)col * (uint32_t)K;      // its first flat element, relative to n0 K
   const uint32_t xlane = mvalid ? (uint32_t)col * (uint32_t)K * 2 : 0x80000000u;
 
+  // XLDS: X [M, K] staged in LDS by buffer-to-LDS loads issued before any
+  // weight load (row m at m * (2K + 16) bytes, padded against bank
+  // conflicts), one 1 KiB piece per wave instruction; fragments are then read
+  // from LDS by the lanes whose X row exists.  Against per-lane X loads from
+  // L2 (each instruction touching 64 different 128-byte lines) this took a
+  // 4096x4096 call from 5.83 / 7.88 to 5.66 / 7.16 us at M = 4 / 16.  The
+  // launcher uses it only when every wave owns at least one superchunk (the
+  // hand-over barrier is inside the first iteration) and K % 512 == 0.
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  const uint32_t xstride = (uint32_t)(K * 2 + 16);
+  if (XLDS) {
+    const int cpr = (int)(K / 8);                   // 16-byte pieces per X row, a multiple of 64
+    const int total = M * cpr;
+    for (int c0 = 64 * wave; c0 < total; c0 += 64 * kSmallWaves) {
+      const int m = c0 / cpr, ch0 = c0 - m * cpr;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void *)(xs + m * xstride + 16 * ch0), 16,
+                                               (uint32_t)((m * K + (int64_t)(ch0 + lane) * 8) * 2), 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int sc = s0; sc < s1; sc += 2) {
     uint4 c[2][2];
@@ -130,15 +152,38 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
       const uint32_t rb = (elane + bic * kBlock) >> src.lbs;
       r[u] = load_abs(rb);
       if (BS32) r2[u] = load_abs(rb + 1);
-      const uint32_t xo = xlane + bic * (kBlock * 2);
+      if (!XLDS) {
+        const uint32_t xo = xlane + bic * (kBlock * 2);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        xa[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * j, 0, 0));
+        for (int j = 0; j < 8; ++j)
+          xa[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * j, 0, 0));
+      }
       // every load before any arithmetic, chunk 0's before chunk 1's (left to itself
       // the compiler sinks the X loads next to their MFMAs to save registers, or
       // puts both chunks' absmax loads last; either serialises the latencies)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (XLDS) {
+      if (sc == s0) {
+        // the X pieces were issued before this iteration's weight loads: two
+        // chunks of two code loads and the absmax state (1 or 2 loads per block)
+        constexpr int kAfterX = 2 * (2 + (DQ ? 2 : 1) * (BS32 ? 2 : 1));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterX));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int bi = 4 * (sc + u) + kg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xa[u][j] = make_uint4(0u, 0u, 0u, 0u);
+        if (mvalid && ok[u]) {
+          const uint8_t *xp = xs + col * xstride + (uint32_t)bi * (kBlock * 2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xa[u][j] = *reinterpret_cast<const uint4 *>(xp + 16 * j);
+        }
+      }
     }
     // (a chunk past the wave's range has ok = false: a zero table, so its
     // MFMAs add exact zeros; no branch, so no load is sunk into one)
@@ -193,6 +238,219 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
         reinterpret_cast<float *>(Y)[(int64_t)mm * N + n] = acc[rr];
     }
   }
+}
+
+// ----------------------------------------------------------------- small M, many weight rows
+//
+// For weights of many 16-row groups (at least six per CU) the small-M kernel
+// above re-reads X for every group, which at M = 16 and N = 28672, K = 8192
+// is 458 MB through L2 per call.  Here a workgroup of 16 waves owns a
+// contiguous run of row groups and keeps X in registers for all of them: wave
+// w and lane group kg = l/16 form slot s = 4w + kg, which takes the 64-blocks
+// s, s + 64, ... of every weight row (XJ = 1 or 2 of them, K <= 8192); lane l
+// feeds MFMA 16x16x32 with A = X row l%16 (zeros past M) and B = weight row
+// l%16 of the group, MFMA w of a block taking elements 8w .. 8w+7 on both
+// sides.  Units (row group, block round) are double buffered: the next unit's
+// codes and absmax are in flight while the current one is dequantized.  After
+// the last unit of a row group, the adapter term (if any) is added, the 16
+// waves' partial sums go through LDS (double buffered, one barrier per row
+// group) and wave t % 16 adds them and stores.  Measured on the 28672 x 8192
+// weight (three weights rotating, per call): 40.3 / 47.1 / 78.2 us with the
+// kernel above against 37.5 / 38.6 / 44.4 us at M = 1 / 4 / 16; with fewer
+// row groups per workgroup (4096 x 4096: one, 11008 x 4096: two or three) it
+// was slower, so the launcher uses it from six row groups per CU on.
+constexpr int kRowsWaves = 16;
+constexpr int kRowsGrid = 256;             // one workgroup per CU of the MI355X
+constexpr int64_t kRowsMinGroups = 6 * kRowsGrid;
+
+struct DecUnit {
+  uint4 c0, c1;      // 64 codes
+  int q, q2;         // int8 absmax (q2: second 32-block, block size 32)
+  float s, s2;       // group scale (or fp32 absmax without double quantization)
+};
+
+template <int XJ, bool DQ, bool BS32, bool FP4>
+__global__ __launch_bounds__(64 * kRowsWaves) void fwd_rows_kernel(
+    const uint16_t *__restrict__ X, int M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    AbsmaxSrc src, LowRank lr, void *__restrict__ Y, int y_bf16, int rg_base, int rg_extra) {
+  constexpr int kDecWaves = kRowsWaves;
+  constexpr int kDecSlots = 4 * kRowsWaves;
+  __shared__ f32x4 red[2][kDecWaves][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, kg = lane >> 4;
+  const int slot = 4 * wave + kg;
+  const int bid = blockIdx.x;
+  const int g0 = bid * rg_base + (bid < rg_extra ? bid : rg_extra);
+  const int T = rg_base + (bid < rg_extra ? 1 : 0);
+  const int KB = (int)(K >> 6);
+  static_assert(XJ == 1 || XJ == 2, "one or two 64-blocks per lane and row");
+  constexpr int J = XJ;
+  const int U = T * J;
+  const float mu = DQ ? *src.mean : 0.f;
+  const int64_t n0 = (int64_t)g0 * 16;
+  const int64_t rows = (N - n0 < (int64_t)T * 16) ? N - n0 : (int64_t)T * 16;
+  const uint32_t rowb = (uint32_t)(K / 2);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(packed + n0 * (K / 2)), (short)0, (int)(rows * rowb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(X), (short)0, (int)(M * K * 2), 0x00020000);
+  const int lbs = src.lbs;
+  const int64_t nblocks = (N * K + (1 << lbs) - 1) >> lbs;
+  const int64_t fb = (n0 * K) >> lbs;         // first block of the workgroup (n0 K is a multiple of 1024)
+  const int64_t fg = fb >> 8;
+  const int fbo = (int)(fb & 255);
+  const int64_t blks = nblocks - fb;
+  auto nrec = [](int64_t bytes) { return (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff); };
+  __amdgpu_buffer_rsrc_t ars, srs;
+  if (DQ) {
+    srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src.scale + fg), (short)0,
+                                            nrec(4 * (((nblocks + 255) >> 8) - fg)), 0x00020000);
+  } else {
+    ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src.absmax + fb), (short)0, nrec(4 * blks),
+                                            0x00020000);
+  }
+  __amdgpu_buffer_rsrc_t qrs;                 // int8 absmax from the workgroup's first block
+  if (DQ)
+    qrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(src.q + fb), (short)0, nrec(blks), 0x00020000);
+  const uint32_t xrow = col < M ? (uint32_t)col * (uint32_t)K * 2 : 0x80000000u;
+  // Y as one range (the launcher keeps M N 4 below 2^31)
+  const __amdgpu_buffer_rsrc_t yrs =
+      __builtin_amdgcn_make_buffer_rsrc(Y, (short)0, (int)((int64_t)M * N * (y_bf16 ? 2 : 4)), 0x00020000);
+
+  auto load_abs = [&](uint32_t rb, int &q, float &s) {
+    if (DQ) {
+      q = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, rb, 0, 0);
+      s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, ((uint32_t)fbo + rb) >> 8 << 2, 0, 0));
+    } else {
+      q = 0;
+      s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, rb << 2, 0, 0));
+    }
+  };
+  // unit u = (row group t, block round j); XJ > 0 gives j at compile time
+  auto load_unit = [&](int u, DecUnit &d) {
+    const int uc = u < U ? u : U - 1;
+    const int t = uc / J, j = uc - t * J;
+    const int b = slot + kDecSlots * j;
+    const bool ok = b < KB;
+    const uint32_t bc = ok ? (uint32_t)b : 0u;
+    const uint32_t r = (uint32_t)(t * 16 + col);
+    const uint32_t wo = ok ? r * rowb + bc * 32 : 0x80000000u;
+    d.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, 2));
+    d.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo + 16, 0, 2));
+    const uint32_t rb = (r * (uint32_t)K + bc * 64) >> lbs;
+    load_abs(rb, d.q, d.s);
+    if (BS32) load_abs(rb + 1, d.q2, d.s2);
+  };
+  auto unit_ok = [&](int u) {
+    const int t = u / J, j = u - t * J;
+    return slot + kDecSlots * j < KB;
+  };
+
+  // resident X
+  uint4 xr[XJ][8];
+  {
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int b = slot + kDecSlots * j;
+      const uint32_t xo = b < KB ? xrow + (uint32_t)b * 128 : 0x80000000u;
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        xr[j][w] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * w, 0, 0));
+    }
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const DecUnit &d, const uint4 *xa, bool ok) {
+    const float ah = ok ? (DQ ? __fadd_rn(__fmul_rn((float)d.q, d.s), mu) : d.s) : 0.f;
+    const Lut t = make_lut<FP4>(ah);
+    Lut t2;
+    if (BS32) t2 = make_lut<FP4>(ok ? (DQ ? __fadd_rn(__fmul_rn((float)d.q2, d.s2), mu) : d.s2) : 0.f);
+    const uint32_t words[8] = {d.c0.x, d.c0.y, d.c0.z, d.c0.w, d.c1.x, d.c1.y, d.c1.z, d.c1.w};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t bw[4];
+      Sel4 sa, sb;
+      const Lut &tw = (BS32 && w >= 4) ? t2 : t;
+      select8(words[w], sa, sb);
+      lookup4(sa, tw, bw[0], bw[1]);
+      lookup4(sb, tw, bw[2], bw[3]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[w]), as_bf16x8(bw), acc, 0, 0, 0);
+    }
+  };
+  // end of row group t: adapter term, partial sums through LDS; wave t % 16
+  // adds the 16 parts and stores (row group t's outputs: rows m < M of
+  // columns n0 + 16t .. +15)
+  auto finish = [&](int t) {
+    if (lr.r > 0) {
+      const int64_t nt = n0 + (int64_t)t * 16;                     // wave-uniform
+      const int64_t nlast = N - 1 - nt;                            // lanes past N read row N-1
+      const uint16_t *vbase = lr.v + nt * lr.r;
+      const uint32_t vrow = (uint32_t)((col < nlast ? col : nlast) * lr.r);
+      for (int s = wave; 32 * s < lr.r; s += kDecWaves) {
+        const int rk = 32 * s + 8 * kg;
+        uint4 av = make_uint4(0u, 0u, 0u, 0u), bv = make_uint4(0u, 0u, 0u, 0u);
+        if (rk < lr.r) {
+          bv = *reinterpret_cast<const uint4 *>(vbase + vrow + rk);
+          if (col < M) av = *reinterpret_cast<const uint4 *>(lr.u + col * lr.r + rk);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+      }
+    }
+    red[t & 1][wave][lane] = acc;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    if (wave == (t & (kDecWaves - 1))) {
+      f32x4 s = red[t & 1][0][lane];
+#pragma unroll 5
+      for (int w = 1; w < kDecWaves; ++w) {
+        const f32x4 o = red[t & 1][w][lane];
+        s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+      }
+      // element (m, nt + col) of Y; rows past M and columns past N get an
+      // offset beyond the descriptor's range, where stores are dropped
+      const uint32_t nt = (uint32_t)(n0 + 16 * t);
+      const bool cok = nt + (uint32_t)col < (uint32_t)N;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        const uint32_t e = (uint32_t)m * (uint32_t)N + nt + (uint32_t)col;
+        const bool ok = cok && m < M;
+        const float v = s[r];     // a scalar copy: bit_cast of a vector element reads element 0 here
+        if (y_bf16)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu), yrs,
+                                                ok ? 2 * e : 0x80000000u, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), yrs, ok ? 4 * e : 0x80000000u, 0,
+                                                0);
+      }
+    }
+  };
+
+  DecUnit A, B;
+  load_unit(0, A);
+  load_unit(1, B);
+  if (XJ == 2) {
+    for (int t = 0; t < T; ++t) {
+      compute(A, xr[0], unit_ok(2 * t));
+      load_unit(2 * t + 2, A);
+      compute(B, xr[XJ - 1], unit_ok(2 * t + 1));
+      load_unit(2 * t + 3, B);
+      finish(t);
+    }
+  } else {
+    for (int t = 0; t < T; t += 2) {
+      compute(A, xr[0], unit_ok(t));
+      load_unit(t + 2, A);
+      finish(t);
+      if (t + 1 < T) {
+        compute(B, xr[0], unit_ok(t + 1));
+        finish(t + 1);
+      }
+      load_unit(t + 3, B);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ----------------------------------------------------------------- large M
@@ -544,18 +802,46 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
                       const AbsmaxSrc &src, const LowRank &lr, void *y, int y_is_bf16, hipStream_t stream) {
   const uint16_t *X = reinterpret_cast<const uint16_t *>(x);
   const int sel = (y_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (lr.r > 0 ? 1 : 0);
-  if (M <= 16) {
+  const int64_t row_groups = (N + 15) / 16;
+  // the kernel's 32-bit offsets: a workgroup's codes, and Y as a whole
+  const int64_t rows_codes = (row_groups / kRowsGrid + 1) * 16 * (K / 2);
+  if (M <= 16 && K <= 8192 && K % 64 == 0 && row_groups >= kRowsMinGroups && rows_codes < (int64_t(1) << 31) &&
+      M * N * 4 < (int64_t(1) << 31)) {
+    // many weight rows: one 16-wave workgroup per CU over a run of row groups, X in registers
+    using R_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *, int,
+                         int, int);
+#define NF4_ROWS(XJ, FP4) {{fwd_rows_kernel<XJ, false, false, FP4>, fwd_rows_kernel<XJ, false, true, FP4>}, \
+                           {fwd_rows_kernel<XJ, true, false, FP4>, fwd_rows_kernel<XJ, true, true, FP4>}}
+    static const R_t rows[2][2][2][2] = {{NF4_ROWS(1, false), NF4_ROWS(1, true)}, {NF4_ROWS(2, false), NF4_ROWS(2, true)}};
+#undef NF4_ROWS
+    const int grid = kRowsGrid;
+    const int base = (int)(row_groups / grid), extra = (int)(row_groups % grid);
+    hipLaunchKernelGGL(rows[K <= 4096 ? 0 : 1][src.qt ? 1 : 0][src.dq ? 1 : 0][src.lbs == 5 ? 1 : 0], dim3(grid),
+                       dim3(64 * kRowsWaves), 0, stream, X, (int)M, N, K, packed, src, lr, y, y_is_bf16 ? 1 : 0, base,
+                       extra);
+  } else if (M <= 16) {
     using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *);
-#define NF4_SMALL(BS32, FP4)                                                                                  \
-    {fwd_small_kernel<false, false, false, BS32, FP4>, fwd_small_kernel<false, false, true, BS32, FP4>,        \
-     fwd_small_kernel<false, true, false, BS32, FP4>,  fwd_small_kernel<false, true, true, BS32, FP4>,         \
-     fwd_small_kernel<true, false, false, BS32, FP4>,  fwd_small_kernel<true, false, true, BS32, FP4>,         \
-     fwd_small_kernel<true, true, false, BS32, FP4>,   fwd_small_kernel<true, true, true, BS32, FP4>}
-    static const K_t kern[2][2][8] = {{NF4_SMALL(false, false), NF4_SMALL(true, false)},
-                                      {NF4_SMALL(false, true), NF4_SMALL(true, true)}};
+#define NF4_SMALL(BS32, FP4, XL)                                                                              \
+    {fwd_small_kernel<false, false, false, BS32, FP4, XL>, fwd_small_kernel<false, false, true, BS32, FP4, XL>, \
+     fwd_small_kernel<false, true, false, BS32, FP4, XL>,  fwd_small_kernel<false, true, true, BS32, FP4, XL>,  \
+     fwd_small_kernel<true, false, false, BS32, FP4, XL>,  fwd_small_kernel<true, false, true, BS32, FP4, XL>,  \
+     fwd_small_kernel<true, true, false, BS32, FP4, XL>,   fwd_small_kernel<true, true, true, BS32, FP4, XL>}
+    static const K_t kern[2][2][8] = {{NF4_SMALL(false, false, false), NF4_SMALL(true, false, false)},
+                                      {NF4_SMALL(false, true, false), NF4_SMALL(true, true, false)}};
+    static const K_t kern_xlds[2][8] = {NF4_SMALL(false, false, true), NF4_SMALL(false, true, true)};
 #undef NF4_SMALL
     const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols)), b(64 * kSmallWaves);
-    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr, y);
+    // X staged in LDS (M >= 4, block sizes of 64 or more): it must fit, K must be a
+    // multiple of 512, and every wave must own at least one superchunk of 256
+    const int64_t nsc = (K + 255) / 256, per = (nsc + kSmallWaves - 1) / kSmallWaves;
+    const size_t xbytes = (size_t)M * (size_t)(2 * K + 16);
+    const bool xlds = M >= 4 && src.lbs != 5 && K % 512 == 0 && (kSmallWaves - 1) * per < nsc &&
+                      xbytes <= kSmallXldsBytes;
+    if (xlds)
+      hipLaunchKernelGGL(kern_xlds[src.qt ? 1 : 0][sel], g, b, xbytes, stream, X, (int)M, N, K, packed, src, lr, y);
+    else
+      hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr,
+                         y);
   } else {
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);

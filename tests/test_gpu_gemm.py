@@ -178,9 +178,11 @@ def large(large_oracle):
     q = dg.nf4_quantize(W.to(d))
     Y = dg.nf4_matmul_fwd(X.to(d), q)
     dX = dg.nf4_matmul_bwd_dx(dY.to(d), q)
+    # decode on the same weight: the first M rows of X
+    dec = {M: dg.nf4_matmul_fwd(X[:M].to(d), q) for M in synth.DECODE_MS}
     torch.cuda.synchronize()
-    out = {"X": X, "dY": dY, "Y": Y.cpu(), "dX": dX.cpu()}
-    del Y, dX, q
+    out = {"X": X, "dY": dY, "Y": Y.cpu(), "dX": dX.cpu(), "dec": {M: y.cpu() for M, y in dec.items()}}
+    del Y, dX, q, dec
     torch.cuda.empty_cache()
     note("large: oracle W^ (235M elements)")
     out["wh"] = O.bf16_bits_to_f32(O.dequantize(qo)).reshape(W.shape).astype(np.float64)
@@ -195,3 +197,10 @@ def test_large_fwd_every_element(large):
 def test_large_bwd_every_element(large):
     """All 8192 x 8192 outputs of dX (reduction over 28672) against the oracle."""
     assert_gemm_rows(large["dX"], large["dY"], large["wh"], "bwd_dx", "large bwd")
+
+
+def test_large_decode_every_element(large):
+    """Decode (M = 1, 4, 16) on the 28672 x 8192 weight: all outputs against the oracle."""
+    for M, y in large["dec"].items():
+        x = large["X"][:M].float().numpy()
+        assert_gemm_within_bound(y, O.matmul_fwd(x, large["wh"]), O.fwd_bound(x, large["wh"]), f"large decode M={M}")
