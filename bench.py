@@ -197,6 +197,7 @@ def bench_prefill(dg, steps, warmup):
     torch.cuda.synchronize()
     ms_naive = time_events(naive, 10)
     res["ops"]["naive_dequant_then_matmul_fwd"] = {"ms": ms_naive, "TFLOP/s": flop / (ms_naive * 1e-3) / 1e12}
+    res["ops"].update(_dense_gemm_reference(X, dY, Wh, flop))
     # the same GEMMs with a rank-64 low-rank adapter term fused in (U, B / V, A^T bf16)
     r = 64
     U = synth.normal((M, r), 1.0, 2100).to(d)
@@ -272,6 +273,28 @@ def bench_decode(dg, pool=512, reps=10):
     return out
 
 
+def _dense_gemm_reference(X, dY, Wh, flop, reps=10):
+    """Context for the matrix-core bar: the platform's own dense bf16 GEMM (hipBLASLt through
+    torch.matmul, bf16 in and out) on the same shapes with the weight already dense bf16, in
+    the faster of two weight layouts (as stored [N, K], and transposed to [K, N])."""
+    Wt = Wh.t().contiguous()
+    cands = {"fwd": [lambda: torch.matmul(X, Wh.t()), lambda: torch.matmul(X, Wt)],
+             "bwd_dx": [lambda: torch.matmul(dY, Wh), lambda: torch.matmul(dY, Wt.t())]}
+    out = {}
+    for name, fns in cands.items():
+        best = None
+        for fn in fns:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ms = time_events(fn, reps)
+            best = ms if best is None else min(best, ms)
+        tf = flop / (best * 1e-3) / 1e12
+        out[f"dense_bf16_{name}_hipblaslt"] = {"ms": best, "TFLOP/s": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
+    del Wt
+    return out
+
+
 def _device_normal(shape, std, seed, d, dtype=torch.bfloat16):
     g = torch.Generator(device=d)
     g.manual_seed(seed)
@@ -306,14 +329,52 @@ def bench_large(dg, reps=5):
     ms_f = time_events(fwd, reps)
     ms_b = time_events(bwd, reps)
     flop = 2.0 * M * N * K
+    dec = _large_decode(dg, q, X, W, ws, reps)
     bq = N * K * 4 + wq_bytes(N, K)
     out = {"large_quantize_f32": {"ms": ms_q, "GB/s": bq / (ms_q * 1e-3) / 1e9,
                                   "frac_hbm": bq / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
     for name, ms in (("large_fwd", ms_f), ("large_bwd_dx", ms_b)):
         tf = flop / (ms * 1e-3) / 1e12
         out[name] = {"ms": ms, "TFLOP/s": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS}
-    del W, X, dY, q, ws, Y, dX
+    out.update(dec)
+    Wh = dg.nf4_dequantize(q)
+    out.update({"large_" + k: v for k, v in _dense_gemm_reference(X, dY, Wh, flop, reps).items()})
+    del W, X, dY, q, ws, Y, dX, Wh
     torch.cuda.empty_cache()
+    return out
+
+
+LARGE_DECODE_COPIES = 3       # 3 x 121 MB rotating: more than the 256 MB last-level cache
+
+
+def _large_decode(dg, q, X, W, ws, reps, rounds=8):
+    """Decode (M = 1, 4, 16: the first rows of X) on the 28672 x 8192 weight: three quantized
+    copies rotating call by call, one HIP graph of ``rounds`` passes over them, per call."""
+    import synth
+    d = X.device
+    N, K = q.rows, q.cols
+    qs = [q] + [dg.nf4_quantize(W, out=dg.empty_qtensor(N, K, True, d), workspace=ws)
+                for _ in range(LARGE_DECODE_COPIES - 1)]
+    out = {}
+    for M in synth.DECODE_MS:
+        Xm = X[:M].contiguous()
+        Y = torch.empty((M, N), dtype=torch.float32, device=d)
+        for qq in qs:
+            dg.nf4_matmul_fwd(Xm, qq, out=Y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(rounds):
+                for qq in qs:
+                    dg.nf4_matmul_fwd(Xm, qq, out=Y)
+        g.replay()
+        torch.cuda.synchronize()
+        us = time_events(g.replay, reps) / (rounds * len(qs)) * 1e3
+        b = M * K * 2 + wq_bytes(N, K) + M * N * 4
+        out[f"large_decode_m{M}"] = {"us": us, "GB/s": b / (us * 1e-6) / 1e9,
+                                     "frac_hbm": b / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+        del g
+    del qs
     return out
 
 
@@ -571,6 +632,18 @@ def run_single_op(dg, op, steps, warmup):
             torch.cuda.synchronize()
         print(json.dumps({"op": op, "calls_per_m": DECODE_TRACE_POOL * DECODE_TRACE_ROUNDS}), flush=True)
         return
+    elif op == "decode_large":
+        # decode at M = 1, 4, 16 on three rotating quantized 28672 x 8192 weights, ``steps`` calls each
+        M0, K, N = synth.LARGE_M, synth.LARGE_K, synth.LARGE_N
+        qs = [dg.nf4_quantize(_device_normal((N, K), 0.02, 4100 + p, d)) for p in range(LARGE_DECODE_COPIES)]
+        for M in synth.DECODE_MS:
+            X = _device_normal((M, K), 1.0, 4001, d)
+            Y = torch.empty((M, N), dtype=torch.float32, device=d)
+            for i in range(warmup + steps):
+                dg.nf4_matmul_fwd(X, qs[i % len(qs)], out=Y)
+            torch.cuda.synchronize()
+        print(json.dumps({"op": op, "calls_per_m": warmup + steps}), flush=True)
+        return
     elif op == "decode":
         K, N = synth.DECODE_K, synth.DECODE_N
         qs = [dg.nf4_quantize(w.to(d)) for w in synth.parallel(synth.decode_weight, range(16))]
@@ -630,7 +703,7 @@ def main():
     ap.add_argument("--no-decode-trace", action="store_true",
                     help="skip the profiler run that takes the decode kernels' own durations")
     ap.add_argument("--op", default=None,
-                    choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "decode_trace", "copy"],
+                    choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "decode_large", "decode_trace", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

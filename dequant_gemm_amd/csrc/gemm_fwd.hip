@@ -40,7 +40,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kSmallCols = 16;
 constexpr int kSmallWaves = 8;
 constexpr int kNonTemporal = 2;    // buffer-load cache policy: bit 1 = nt (streaming)
-constexpr size_t kSmallXldsBytes = 131328;   // X staged in LDS: at most 16 rows of 4096 (+16 bytes)
+constexpr size_t kSmallXldsBytes = 131456;   // X staged in LDS: at most 16 rows of 4096 (+16 bytes), a zero pad
 
 template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4, bool XLDS>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
@@ -121,7 +121,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   // hand-over barrier is inside the first iteration) and K % 512 == 0.
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   const uint32_t xstride = (uint32_t)(K * 2 + 16);
+  const uint32_t xzero = (uint32_t)M * xstride;     // 128 zero bytes after the M rows
   if (XLDS) {
+    if (threadIdx.x < 8) *reinterpret_cast<uint4 *>(xs + xzero + 16 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
     const int cpr = (int)(K / 8);                   // 16-byte pieces per X row, a multiple of 64
     const int total = M * cpr;
     for (int c0 = 64 * wave; c0 < total; c0 += 64 * kSmallWaves) {
@@ -170,19 +172,18 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
         // chunks of two code loads and the absmax state (1 or 2 loads per block)
         constexpr int kAfterX = 2 * (2 + (DQ ? 2 : 1) * (BS32 ? 2 : 1));
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterX));
+        __builtin_amdgcn_s_waitcnt(lgkm_imm(0));      // the zero pad's stores
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        // lanes whose X row or chunk does not exist read the zero pad (no
+        // branch, no register zeroing)
         const int bi = 4 * (sc + u) + kg;
+        const uint32_t xo = (mvalid && ok[u]) ? col * xstride + (uint32_t)bi * (kBlock * 2) : xzero;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xa[u][j] = make_uint4(0u, 0u, 0u, 0u);
-        if (mvalid && ok[u]) {
-          const uint8_t *xp = xs + col * xstride + (uint32_t)bi * (kBlock * 2);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xa[u][j] = *reinterpret_cast<const uint4 *>(xp + 16 * j);
-        }
+        for (int j = 0; j < 8; ++j) xa[u][j] = *reinterpret_cast<const uint4 *>(xs + xo + 16 * j);
       }
     }
     // (a chunk past the wave's range has ok = false: a zero table, so its
@@ -358,6 +359,11 @@ __global__ __launch_bounds__(64 * kRowsWaves) void fwd_rows_kernel(
       for (int w = 0; w < 8; ++w)
         xr[j][w] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * w, 0, 0));
     }
+    // into the K order of the weight fragments (once; reused for every row group)
+#pragma unroll
+    for (int j = 0; j < XJ; ++j)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) xr[j][w] = xfrag_even_odd(xr[j][w]);
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void fwd_rows_kernel(
       uint32_t bw[4];
       Sel4 sa, sb;
       const Lut &tw = (BS32 && w >= 4) ? t2 : t;
-      select8(words[w], sa, sb);
+      select8_even_odd(words[w], sa, sb);
       lookup4(sa, tw, bw[0], bw[1]);
       lookup4(sb, tw, bw[2], bw[3]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[w]), as_bf16x8(bw), acc, 0, 0, 0);
@@ -834,7 +840,7 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
     // X staged in LDS (M >= 4, block sizes of 64 or more): it must fit, K must be a
     // multiple of 512, and every wave must own at least one superchunk of 256
     const int64_t nsc = (K + 255) / 256, per = (nsc + kSmallWaves - 1) / kSmallWaves;
-    const size_t xbytes = (size_t)M * (size_t)(2 * K + 16);
+    const size_t xbytes = (size_t)M * (size_t)(2 * K + 16) + 128;
     const bool xlds = M >= 4 && src.lbs != 5 && K % 512 == 0 && (kSmallWaves - 1) * per < nsc &&
                       xbytes <= kSmallXldsBytes;
     if (xlds)

@@ -299,6 +299,25 @@ __device__ __forceinline__ void select8(uint32_t d, Sel4 &a, Sel4 &b) {
   b.hi = b.lo ^ 0x10101010u;
 }
 
+// The same selectors without putting the elements back in order: (a) for the
+// even elements 0, 2, 4, 6 and (b) for the odd elements 1, 3, 5, 7.  Looked up,
+// they give a B fragment in the K order 0, 2, 4, 6, 1, 3, 5, 7, which an A
+// fragment must match (xfrag_even_odd); two byte permutes fewer per eight codes.
+__device__ __forceinline__ void select8_even_odd(uint32_t d, Sel4 &a, Sel4 &b) {
+  const uint32_t even = d & 0x0f0f0f0fu;
+  const uint32_t odd = (d >> 4) & 0x0f0f0f0fu;
+  a.lo = even + (d & 0x08080808u);
+  b.lo = odd + (odd & 0x08080808u);
+  a.hi = a.lo ^ 0x10101010u;
+  b.hi = b.lo ^ 0x10101010u;
+}
+
+// Eight consecutive bf16 values (element order) -> K order 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ __forceinline__ uint4 xfrag_even_odd(uint4 x) {
+  return make_uint4(perm(x.y, x.x, 0x05040100u), perm(x.w, x.z, 0x05040100u), perm(x.y, x.x, 0x07060302u),
+                    perm(x.w, x.z, 0x07060302u));
+}
+
 // Four selected codes -> their bf16 values as two bf16x2 words (element order).
 __device__ __forceinline__ void lookup4(const Sel4 &s, const Lut &t, uint32_t &w0, uint32_t &w1) {
   const uint32_t lo = perm(t.lo[1], t.lo[0], s.lo) & perm(t.lo[3], t.lo[2], s.hi);
