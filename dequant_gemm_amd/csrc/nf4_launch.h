@@ -12,9 +12,10 @@ namespace nf4 {
 
 // Workspace layout for quantization with double quantization: one row of
 // kMeanSlots exact-mean accumulators per quantize workgroup (at most
-// kQuantGridMax; the last workgroup's row also holds the partial block at the
-// end), then the fp32 absmax of every block.
-constexpr int kQuantGridMax = 2048;
+// kQuantGridMax workgroups of kQuantThreads; the last workgroup's row also
+// holds the partial block at the end), then the fp32 absmax of every block.
+constexpr int kQuantThreads = 1024;
+constexpr int kQuantGridMax = 512;
 constexpr int kMeanSlots = 16;
 constexpr size_t kPartialBytes = (size_t)kQuantGridMax * kMeanSlots * sizeof(unsigned long long);
 constexpr size_t absmax_ws_offset() { return (kPartialBytes + 255) & ~(size_t)255; }

@@ -91,16 +91,20 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
   bool near[8];
   const bool fast = m >= 0x01000000u && m < 0x7e000000u;  // 2^-125 <= a < 2^125: 1/a is a normal float
   const float r = __builtin_amdgcn_rcpf(a);
+  bool any = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     code[i] = classify(x[i] * r, cells, near[i]);
     near[i] = near[i] || !fast;
+    any = any || near[i];
   }
+  if (any) {                // rare: one branch around the per-element redo
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (near[i]) {
-      bool unused;
-      code[i] = classify(x[i] / a, cells, unused);
+    for (int i = 0; i < 8; ++i) {
+      if (near[i]) {
+        bool unused;
+        code[i] = classify(x[i] / a, cells, unused);
+      }
     }
   }
   uint32_t word = 0;
@@ -163,16 +167,20 @@ __device__ __forceinline__ uint32_t encode8_fp4(const float x[8], uint32_t m, co
   bool near[8];
   const bool fast = m >= 0x01000000u && m < 0x7e000000u;
   const float r = __builtin_amdgcn_rcpf(a);
+  bool any = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     code[i] = classify_fp4(x[i] * r, cells, near[i]);
     near[i] = near[i] || !fast;
+    any = any || near[i];
   }
+  if (any) {                // rare: one branch around the per-element redo
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (near[i]) {
-      bool unused;
-      code[i] = classify_fp4(x[i] / a, cells, unused);
+    for (int i = 0; i < 8; ++i) {
+      if (near[i]) {
+        bool unused;
+        code[i] = classify_fp4(x[i] / a, cells, unused);
+      }
     }
   }
   uint32_t word = 0;
@@ -198,15 +206,16 @@ __device__ __forceinline__ void add_to_slots(unsigned long long *slot, int e, un
 }
 
 template <bool BF16, bool DQ, int LPB, bool FP4>
-__global__ __launch_bounds__(256) void quantize_blocks_kernel(
+__global__ __launch_bounds__(kQuantThreads) void quantize_blocks_kernel(
     const void *__restrict__ w, int64_t numel, int64_t nfull, uint8_t *__restrict__ packed,
     float *__restrict__ absmax, unsigned long long *__restrict__ partials, uint32_t *status) {
   constexpr int BS = 8 * LPB;        // weights per block
-  constexpr int BPI = 256 / LPB;     // blocks per workgroup and iteration
+  constexpr int BPI = kQuantThreads / LPB;     // blocks per workgroup and iteration
+  constexpr int kWaves = kQuantThreads / 64;
   __shared__ Cell cells[129];
   __shared__ unsigned long long lbuck[256];
   __shared__ unsigned long long lslot[kMeanSlots];
-  __shared__ uint32_t wmax[4];
+  __shared__ uint32_t wmax[kWaves];
   const int part = threadIdx.x % LPB;
   const int slot = threadIdx.x / LPB;
   const int64_t stride = (int64_t)gridDim.x * BPI;
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
   else
     build_cells(cells);
   if (DQ) {
-    lbuck[threadIdx.x] = 0ull;
+    if (threadIdx.x < 256) lbuck[threadIdx.x] = 0ull;
     if (threadIdx.x < kMeanSlots) lslot[threadIdx.x] = 0ull;
   }
   __syncthreads();
@@ -257,8 +266,19 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     // absmax on the magnitude bits: integer order equals float order for
     // non-negative floats, and NaN/inf compare above every finite value
     uint32_t m = 0;
+    if (BF16) {
+      // eight bf16 magnitudes as four pairs of 16-bit integers, their maximum
+      // shifted into the fp32 position (the fp32 bits of a bf16 value are its
+      // bits << 16)
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      const u16x2 p0 = __builtin_bit_cast(u16x2, cu.x & 0x7fff7fffu), p1 = __builtin_bit_cast(u16x2, cu.y & 0x7fff7fffu);
+      const u16x2 p2 = __builtin_bit_cast(u16x2, cu.z & 0x7fff7fffu), p3 = __builtin_bit_cast(u16x2, cu.w & 0x7fff7fffu);
+      const u16x2 pm = __builtin_elementwise_max(__builtin_elementwise_max(p0, p1), __builtin_elementwise_max(p2, p3));
+      m = (uint32_t)(pm.x > pm.y ? pm.x : pm.y) << 16;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
+      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
+    }
 #pragma unroll
     for (int sh = 1; sh < LPB; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
 
@@ -299,7 +319,9 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     for (int sh = 1; sh < 64; sh <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
     if ((t & 63) == 0) wmax[t >> 6] = m;
     __syncthreads();
-    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    m = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) m = max(m, wmax[i]);
     int code = FP4 ? 0 : 7;   // the +0 level
     if (m != 0 && m < 0x7f800000u) {
       bool unused = false;
@@ -317,8 +339,10 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
   }
   if (DQ) {
     __syncthreads();
-    const unsigned long long v = lbuck[threadIdx.x];
-    if (v) add_to_slots(lslot, threadIdx.x, v);
+    if (threadIdx.x < 256) {
+      const unsigned long long v = lbuck[threadIdx.x];
+      if (v) add_to_slots(lslot, threadIdx.x, v);
+    }
     __syncthreads();
     if (threadIdx.x < kMeanSlots) partials[(int64_t)blockIdx.x * kMeanSlots + threadIdx.x] = lslot[threadIdx.x];
   }
@@ -326,25 +350,47 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 }
 
 // Exact mean of all block absmax values, rounded once to fp32 (nearest-even),
-// from the total S (in 2^-149 units) given as 32-bit digits: digit[i] has
-// weight 2^(32 i).  S is divided by the block count with 32 extra quotient
-// bits -- enough to reach below the smallest subnormal -- and rounded on the
-// remainder.
+// from N = S * 2^32 (S the total in 2^-149 units) given as 32-bit digits:
+// num[i] has weight 2^(32 i), num[0] = 0.  The quotient N / nblocks is wanted
+// to 24 significant bits, a round bit and a sticky bit.  Let T be the three
+// digits from the highest non-zero one down (T >= 2^64) and R the digits below
+// them, so N = T 2^k + R with k = 32 (top - 2) and R < 2^k (for top < 2, k < 0
+// and R = 0).  With T = Q nblocks + rem, the true quotient is
+// Q 2^k + (rem 2^k + R) / nblocks, the last term below 2^k: the quotient's bits
+// from position k up are Q's, and Q has at least 33 bits (T >= 2^64,
+// nblocks < 2^32), so its top 24 bits and the round bit all come from Q, and
+// the sticky bit is Q's lower bits or a non-zero rem or R.  Three digit steps
+// of long division instead of one per digit, and no indexing of the digits
+// by a run-time value.
 constexpr int kMeanWords = 13;   // S * 2^32 as 32-bit digits (S < 2^(10*32 + 24))
 
-__device__ float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nblocks) {
+__host__ __device__ inline float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nblocks) {
   constexpr int W = kMeanWords;
-  // long division by nblocks, one 32-bit digit at a time: the digit
-  // cur / nblocks (< 2^32 since rem < nblocks) is estimated in fp64 -- cur is
-  // below nblocks * 2^32, so its rounding moves the estimate by less than one
-  // -- and corrected exactly with an integer multiply-subtract
-  uint32_t q[W];
-  unsigned long long rem = 0;
+  int top = -1;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if (num[i]) top = i;
+  if (top < 0) return 0.f;
+  uint32_t t[3] = {0u, 0u, 0u};   // T's digits, low to high
+  bool rnz = false;               // R != 0
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    if (i == top) t[2] = num[i];
+    if (i == top - 1) t[1] = num[i];
+    if (i == top - 2) t[0] = num[i];
+    if (i < top - 2 && num[i]) rnz = true;
+  }
+  const int k = 32 * (top - 2);
+  // T / nblocks one 32-bit digit at a time: the digit cur / nblocks (< 2^32
+  // since rem < nblocks) is estimated in fp64 -- cur is below nblocks * 2^32,
+  // so its rounding moves the estimate by less than one -- and corrected
+  // exactly with an integer multiply-subtract
   const double inv = 1.0 / (double)nblocks;
-  int top = W - 1;            // digits above the highest non-zero one give zero quotient digits
-  while (top > 0 && num[top] == 0) q[top--] = 0;
-  for (int i = top; i >= 0; --i) {
-    const unsigned long long cur = (rem << 32) | num[i];
+  uint32_t q[3];
+  unsigned long long rem = 0;
+#pragma unroll
+  for (int i = 2; i >= 0; --i) {
+    const unsigned long long cur = (rem << 32) | t[i];
     long long qe = (long long)((double)cur * inv);
     long long r = (long long)(cur - (unsigned long long)qe * nblocks);
     if (r < 0) {
@@ -357,34 +403,29 @@ __device__ float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nbloc
     q[i] = (uint32_t)qe;
     rem = (unsigned long long)r;
   }
-  int L = 0;
-#pragma unroll
-  for (int i = 0; i < W; ++i)
-    if (q[i]) L = 32 * i + (32 - __clz(q[i]));
-  if (L == 0) return 0.f;
-  int p = L - 24 > 32 ? L - 24 : 32;  // lsb kept: 24 bits, or the 2^-149 unit
-  auto bits_at = [&](int pos) -> unsigned long long {  // 64 bits of q starting at bit pos
-    const int w = pos >> 5, b = pos & 31;
-    unsigned long long lo = 0, mid = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      if (i == w) lo = q[i];
-      if (i == w + 1) mid = q[i];
-      if (i == w + 2) hi = q[i];
-    }
-    const unsigned long long x = lo | (mid << 32);
-    return b ? (x >> b) | (hi << (64 - b)) : x;
+  const unsigned long long lo = ((unsigned long long)q[1] << 32) | q[0];
+  const unsigned long long hi = q[2];
+  const int lq = q[2] ? 64 + 32 - __builtin_clz(q[2])
+                      : (q[1] ? 32 + 32 - __builtin_clz(q[1]) : 32 - __builtin_clz(q[0]));   // >= 33
+  // lsb kept: 24 bits below the leading one, or the 2^-149 unit (position 32 of the quotient)
+  int p = lq + k - 24 > 32 ? lq + k - 24 : 32;
+  const int pq = p - k;           // the same position in Q, >= 9
+  auto bits_at = [&](int pos) -> unsigned long long {   // bits pos .. pos+63 of Q (zeros past 96)
+    if (pos >= 96) return 0ull;
+    if (pos >= 64) return hi >> (pos - 64);
+    if (pos == 0) return lo;
+    return (lo >> pos) | (hi << (64 - pos));
   };
-  uint32_t kept = (uint32_t)(bits_at(p) & 0xffffffu);
-  const uint32_t round = (uint32_t)(bits_at(p - 1) & 1u);
-  // sticky: any set bit below p-1, or a non-zero remainder
-  bool sticky = rem != 0;
-  const int sb = p - 1;
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    if (32 * i + 32 <= sb) sticky |= q[i] != 0;
-    else if (32 * i < sb) sticky |= (q[i] & ((1u << (sb - 32 * i)) - 1u)) != 0;
-  }
+  uint32_t kept = (uint32_t)(bits_at(pq) & 0xffffffu);
+  const uint32_t round = (uint32_t)(bits_at(pq - 1) & 1u);
+  const int sb = pq - 1;          // sticky: Q's bits below sb, rem, R
+  bool sticky = rem != 0 || rnz;
+  if (sb >= 96)
+    sticky = sticky || lo != 0 || hi != 0;
+  else if (sb >= 64)
+    sticky = sticky || lo != 0 || (hi & ((1ull << (sb - 64)) - 1ull)) != 0;
+  else if (sb > 0)
+    sticky = sticky || (lo & ((1ull << sb) - 1ull)) != 0;
   if (round && (sticky || (kept & 1u))) ++kept;
   if (kept == (1u << 24)) {
     kept >>= 1;
@@ -393,12 +434,14 @@ __device__ float mean_from_digits(const uint32_t num[kMeanWords], uint32_t nbloc
   // value = kept * 2^(p - 181)
   const uint32_t bits = kept >= (1u << 23) ? (((uint32_t)(p - 31) << 23) | (kept & 0x7fffffu))
                                            : kept;  // subnormal (p == 32)
-  return __uint_as_float(bits);
+  float f;
+  __builtin_memcpy(&f, &bits, 4);
+  return f;
 }
 
 // The exact mean of the rows' total, in every thread of a workgroup of 1024
 // threads: thread t sums the 16-byte piece t % 8 (slots 2(t%8) and 2(t%8)+1)
-// of rows t/8, t/8 + 128, ... (at most 2048 rows: all of a thread's loads in
+// of rows t/8, t/8 + 128, ... (at most 512 rows: all of a thread's loads in
 // flight at once), the 128 partial sums of each slot are added through LDS in
 // two stages, and one thread resolves the carries and forms the mean, which
 // it hands to the others through LDS.  Integer sums: the order does not
@@ -408,7 +451,7 @@ constexpr int kMeanThreads = 1024;
 __device__ float mean_of_rows(const unsigned long long *__restrict__ partials, int nrows, uint32_t nblocks) {
   static_assert(kMeanSlots == 16, "a row is eight 16-byte pieces of two slots");
   constexpr int RL = kMeanThreads / 8;                          // 128 rows per pass
-  constexpr int P = (kQuantGridMax + RL - 1) / RL;              // passes for the most rows (16)
+  constexpr int P = (kQuantGridMax + RL - 1) / RL;              // passes for the most rows (4)
   __shared__ unsigned long long red[RL][kMeanSlots];
   __shared__ unsigned long long slot_sum[kMeanSlots];
   __shared__ float mean_lds;
@@ -420,7 +463,7 @@ __device__ float mean_of_rows(const unsigned long long *__restrict__ partials, i
     v[i] = r < nrows ? reinterpret_cast<const ulonglong2 *>(partials + (int64_t)r * kMeanSlots)[pc]
                      : make_ulonglong2(0ull, 0ull);
   }
-  unsigned long long a0 = 0, a1 = 0;   // every row slot is below 2^41 and there are at most 2048 rows
+  unsigned long long a0 = 0, a1 = 0;   // a row slot is below 96 * 2^32 and there are at most 512 rows
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     a0 += v[i].x;
@@ -473,23 +516,38 @@ __global__ __launch_bounds__(kMeanThreads) void mean_dq_kernel(const unsigned lo
                                                               int64_t nblocks, int8_t *__restrict__ q_out,
                                                               float *__restrict__ scale_out,
                                                               float *__restrict__ mean_out) {
-  const float mu = mean_of_rows(partials, nrows, (uint32_t)nblocks);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
   const int lane = threadIdx.x & 63;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   const int64_t step = (int64_t)gridDim.x * (kMeanThreads / 64);
-  for (int64_t g = (int64_t)blockIdx.x * (kMeanThreads / 64) + (threadIdx.x >> 6); g < ngroups; g += step) {
+  const int64_t g0 = (int64_t)blockIdx.x * (kMeanThreads / 64) + (threadIdx.x >> 6);
+  // the lane's four absmax values of group g (zeros past the last block)
+  auto load4 = [&](int64_t g) {
     const int64_t base = g * kGroup + lane * 4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (base + 3 < nblocks) {
+      a = *reinterpret_cast<const float4 *>(absmax + base);
+    } else {
+      if (base < nblocks) a.x = absmax[base];
+      if (base + 1 < nblocks) a.y = absmax[base + 1];
+      if (base + 2 < nblocks) a.z = absmax[base + 2];
+    }
+    return a;
+  };
+  // the first group's values are in flight while the mean is formed
+  float4 pre = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (g0 < ngroups) pre = load4(g0);
+  const float mu = mean_of_rows(partials, nrows, (uint32_t)nblocks);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
+  for (int64_t g = g0; g < ngroups; g += step) {
+    const int64_t base = g * kGroup + lane * 4;
+    const float4 a = g == g0 ? pre : load4(g);
     float ac[4];
     float m = 0.f;
-    if (base + 3 < nblocks) {
-      const float4 a = *reinterpret_cast<const float4 *>(absmax + base);
-      ac[0] = __fsub_rn(a.x, mu); ac[1] = __fsub_rn(a.y, mu);
-      ac[2] = __fsub_rn(a.z, mu); ac[3] = __fsub_rn(a.w, mu);
-    } else {
+    ac[0] = __fsub_rn(a.x, mu); ac[1] = __fsub_rn(a.y, mu);
+    ac[2] = __fsub_rn(a.z, mu); ac[3] = __fsub_rn(a.w, mu);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ac[i] = (base + i < nblocks) ? __fsub_rn(absmax[base + i], mu) : 0.f;
-    }
+    for (int i = 0; i < 4; ++i)
+      if (base + i >= nblocks) ac[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(ac[i]));
 #pragma unroll
@@ -519,13 +577,13 @@ __global__ __launch_bounds__(kMeanThreads) void mean_dq_kernel(const unsigned lo
 }
 
 // Workgroups of the double-quantization launch: each one re-derives the mean
-// from the rows (at most 2048 x 128 bytes), so they are kept few.
+// from the rows (at most 512 x 128 bytes), so they are kept few.
 constexpr int kDqGridMax = 256;
 
 template <bool BF16, bool DQ, bool FP4>
 void launch_blocks(int lbs, int grid, int64_t numel, int64_t nfull, hipStream_t stream, const void *w,
                    uint8_t *packed, float *absmax_out, unsigned long long *partials, uint32_t *status) {
-  const dim3 g((unsigned)grid), b(256);
+  const dim3 g((unsigned)grid), b(kQuantThreads);
   switch (lbs) {
     case 5: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 4, FP4>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, partials, status); break;
     case 6: hipLaunchKernelGGL((quantize_blocks_kernel<BF16, DQ, 8, FP4>), g, b, 0, stream, w, numel, nfull, packed, absmax_out, partials, status); break;
@@ -543,7 +601,7 @@ hipError_t launch_quantize(const void *w, int w_is_bf16, int64_t numel, int lbs,
   const int bs = 1 << lbs;
   const int64_t nblocks = (numel + bs - 1) / bs;
   const int64_t nfull = numel / bs;
-  const int bpi = 256 / (bs / 8);   // blocks per quantize workgroup and iteration
+  const int bpi = kQuantThreads / (bs / 8);   // blocks per quantize workgroup and iteration
   // at least one workgroup: the last one also takes the partial block at the end
   const int64_t g64 = (nfull + bpi - 1) / bpi;
   const int grid = (int)(g64 < 1 ? 1 : (g64 < kQuantGridMax ? g64 : kQuantGridMax));

@@ -100,7 +100,7 @@ def test_sizes_closed_forms(L, rows, cols, dq, bs):
     assert s["nblocks"] == nb
     assert s["ngroups"] == -(-nb // 256)
     if dq:
-        assert s["workspace_bytes"] >= 1025 * 128 + 4 * nb
+        assert s["workspace_bytes"] >= 512 * 128 + 4 * nb
     else:
         assert s["workspace_bytes"] == 0
 
