@@ -419,9 +419,15 @@ def bench_bulk(dg, reps=3):
     return res
 
 
-def bench_blocksizes(dg, reps=5):
+def bench_blocksizes(dg, reps=4, rounds=5):
     """The prefill workload with 32, 128 and 256 weights per absmax block, at 64
-    without double quantization (fp32 absmax per block), and with the FP4 level table."""
+    without double quantization (fp32 absmax per block), and with the FP4 level table.
+
+    The GEMMs of each variant are timed interleaved with the same GEMM on the plain block-size-64
+    weight (``rounds`` alternations of ``reps`` calls) and reported from the medians, with the
+    ratio to the plain weight's time: the clock drifts by several percent under these
+    power-limited kernels, and the first variant timed after a change of workload ran up to 25%
+    slow when each variant was timed once on its own."""
     import synth
     d = torch.device("cuda:0")
     M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
@@ -432,6 +438,8 @@ def bench_blocksizes(dg, reps=5):
     dX = torch.empty((M, K), dtype=torch.float32, device=d)
     Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
     flop = 2.0 * M * N * K
+    q64 = dg.nf4_quantize(W)
+    plain = {"fwd": lambda: dg.nf4_matmul_fwd(X, q64, out=Y), "bwd_dx": lambda: dg.nf4_matmul_bwd_dx(dY, q64, out=dX)}
     out = {}
     for name, bs, dq, qt in (("bs32", 32, True, "nf4"), ("bs128", 128, True, "nf4"), ("bs256", 256, True, "nf4"),
                              ("bs64_no_double_quant", 64, False, "nf4"), ("fp4_bs64", 64, True, "fp4")):
@@ -445,15 +453,25 @@ def bench_blocksizes(dg, reps=5):
         torch.cuda.synchronize()
         nb = -(-N * K // bs)
         wq = N * K // 2 + (nb + 4 * (-(-nb // 256)) + 4 if dq else 4 * nb)
-        ms = {k: time_events(fn, reps) for k, fn in fns.items()}
+        ms = {"quantize": time_events(fns["quantize"], reps)}
+        ratio = {}
+        for g in ("fwd", "bwd_dx"):
+            tv, tp = [], []
+            for _ in range(rounds):
+                tp.append(time_events(plain[g], reps))
+                tv.append(time_events(fns[g], reps))
+            ms[g] = float(np.median(tv))
+            ratio[g] = ms[g] / float(np.median(tp))
         ms["dequantize"] = time_graph(lambda: dg.nf4_dequantize(q, out=Wh), reps)
         out[name] = {
             "quantize_GB/s": (N * K * 2 + wq) / (ms["quantize"] * 1e-3) / 1e9,
             "dequantize_GB/s": (wq + N * K * 2) / (ms["dequantize"] * 1e-3) / 1e9,
             "fwd_TFLOP/s": flop / (ms["fwd"] * 1e-3) / 1e12,
             "bwd_dx_TFLOP/s": flop / (ms["bwd_dx"] * 1e-3) / 1e12,
+            "fwd_time_vs_bs64": ratio["fwd"],
+            "bwd_dx_time_vs_bs64": ratio["bwd_dx"],
             "bits_per_weight": 8.0 * wq / (N * K)}
-    del W, X, dY, Y, dX, Wh
+    del W, X, dY, Y, dX, Wh, q64
     torch.cuda.empty_cache()
     return {"blocksize_variants": out}
 
@@ -653,7 +671,9 @@ def run_single_op(dg, op, steps, warmup):
     else:
         M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
         W = synth.prefill_weight().to(d)
-        q = dg.nf4_quantize(W)
+        bs = 32 if op.endswith("_bs32") else 64
+        op = op[:-5] if op.endswith("_bs32") else op
+        q = dg.nf4_quantize(W, blocksize=bs)
         if op == "fwd":
             X = synth.prefill_x().to(d)
             Y = torch.empty((M, N), dtype=torch.float32, device=d)
@@ -703,7 +723,8 @@ def main():
     ap.add_argument("--no-decode-trace", action="store_true",
                     help="skip the profiler run that takes the decode kernels' own durations")
     ap.add_argument("--op", default=None,
-                    choices=["fwd", "bwd_dx", "quantize", "dequantize", "decode", "decode_large", "decode_trace", "copy"],
+                    choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "decode", "decode_large",
+                             "decode_trace", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -338,9 +338,12 @@ template <bool DX_BF16, bool DQ, bool LR, bool GBS, bool FP4>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dx_kernel(
     const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ dX, int tiles_m, int tiles_k) {
-  __shared__ __attribute__((aligned(1024))) uint8_t as0[ATILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t as1[ATILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t as2[ATILE];
+  // the dY stages first (larger alignment places them at the lowest LDS
+  // addresses), so that their fragment reads fold the tile offsets into the
+  // 16-bit immediate of the LDS read instead of forming each address
+  __shared__ __attribute__((aligned(4096))) uint8_t as0[ATILE];
+  __shared__ __attribute__((aligned(4096))) uint8_t as1[ATILE];
+  __shared__ __attribute__((aligned(4096))) uint8_t as2[ATILE];
   __shared__ __attribute__((aligned(1024))) uint8_t bs[NWAVE * BTILE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
