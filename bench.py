@@ -77,6 +77,56 @@ def measured_traffic(kernel):
     return None
 
 
+# kernels whose HBM-side traffic is recorded: kernel name -> (profiling op, source files)
+TRAFFIC_KERNELS = {
+    "fwd_large_kernel": ("fwd", ["dequant_gemm_amd/csrc/gemm_fwd.hip", "dequant_gemm_amd/csrc/nf4_common.h"]),
+    "bwd_dx_kernel": ("bwd_dx", ["dequant_gemm_amd/csrc/gemm_bwd.hip", "dequant_gemm_amd/csrc/nf4_common.h"]),
+}
+COPY_BYTES = 1 << 30   # the calibration copy of run_single_op("copy")
+
+
+def write_traffic(pmc_dir):
+    """Write profiles/traffic.json from rocprofv3 counter runs (never by hand).
+
+    ``pmc_dir`` holds the CSV output of ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``
+    (one counter per run) of ``bench.py --op <op>`` for op = copy and each op in
+    TRAFFIC_KERNELS, in ``pmc_<COUNTER>_<op>/<op>_counter_collection.csv``.  The per-dispatch
+    KiB of each kernel (mean over its dispatches) are scaled by what the same counter reads
+    for the plain 1 GiB copy, and stored with the hash of the kernel's sources.
+    """
+    import csv
+
+    def mean_kib(counter, op, name):
+        f = os.path.join(pmc_dir, f"pmc_{counter}_{op}", f"{op}_counter_collection.csv")
+        per = {}
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name in r["Kernel_Name"]:
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not per:
+            raise ValueError(f"no {counter} rows for {name} in {f}")
+        return sum(per.values()) / len(per), len(per)
+
+    cf, _ = mean_kib("FETCH_SIZE", "copy", "copyBuffer")
+    cw, _ = mean_kib("WRITE_SIZE", "copy", "copyBuffer")
+    ff, wf = COPY_BYTES / 1024 / cf, COPY_BYTES / 1024 / cw
+    out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                      "python3 bench.py --op <op> --steps 4 --warmup 1",
+           "kernels": {}}
+    for name, (op, files) in TRAFFIC_KERNELS.items():
+        fk, n1 = mean_kib("FETCH_SIZE", op, name)
+        wk, n2 = mean_kib("WRITE_SIZE", op, name)
+        fb, wb = int(fk * 1024 * ff), int(wk * 1024 * wf)
+        out["kernels"][name] = {"op": op, "sources": files, "source_sha256": _source_hash(files),
+                                "fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "dispatches": [n1, n2],
+                                "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
+
+
 def wq_bytes(rows, cols):
     numel = rows * cols
     nb = -(-numel // 64)
@@ -726,7 +776,12 @@ def main():
                     choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "decode", "decode_large",
                              "decode_trace", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
+    ap.add_argument("--write-traffic", metavar="PMC_DIR", default=None,
+                    help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE counter runs in PMC_DIR and exit")
     a = ap.parse_args()
+    if a.write_traffic:
+        print(json.dumps(write_traffic(a.write_traffic), indent=1))
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the NF4 path here is built and timed on a single "
               "MI355X (no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
