@@ -526,6 +526,30 @@ def bench_blocksizes(dg, reps=4, rounds=5):
     return {"blocksize_variants": out}
 
 
+def bench_tiny(dg, reps=10):
+    """The tiny workload (W 256x256 fp32, X and dY 8x256): per-call latency of every call,
+    replayed from HIP graphs of 20 calls (latency-bound; reported, not a roofline figure)."""
+    import synth
+    d = torch.device("cuda:0")
+    t = synth.tiny()
+    W, X, dY = t["W"].to(d), t["X"].to(d), t["dY"].to(d)
+    N, K = W.shape
+    out = {}
+    for dq in (True, False):
+        q = dg.empty_qtensor(N, K, dq, d)
+        ws = torch.empty(dg.nf4_sizes(N, K, 64, dq)["workspace_bytes"], dtype=torch.uint8, device=d) if dq else None
+        tag = "" if dq else "_no_double_quant"
+        out["quantize" + tag] = time_graph(lambda: dg.nf4_quantize(W, double_quant=dq, out=q, workspace=ws), reps) * 1e3
+        if dq:
+            Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
+            Y = torch.empty((X.shape[0], N), dtype=torch.float32, device=d)
+            dX = torch.empty((dY.shape[0], K), dtype=torch.float32, device=d)
+            out["dequantize"] = time_graph(lambda: dg.nf4_dequantize(q, out=Wh), reps) * 1e3
+            out["fwd"] = time_graph(lambda: dg.nf4_matmul_fwd(X, q, out=Y), reps) * 1e3
+            out["bwd_dx"] = time_graph(lambda: dg.nf4_matmul_bwd_dx(dY, q, out=dX), reps) * 1e3
+    return {"tiny_us_per_call": out}
+
+
 def bench_read_stream(reps=5, gib=4):
     """The achievable HBM read bandwidth: a plain read stream (libnf4_bench) over a 4 GiB buffer
     (16x the 256 MB last-level cache), best of a few launch shapes."""
@@ -805,6 +829,7 @@ def main():
     if trace is not None:
         ops.update(trace)
     ops.update(bench_read_stream())
+    ops.update(bench_tiny(dg))
     if not a.no_large:
         ops.update(bench_large(dg))
     if not a.no_bulk:
