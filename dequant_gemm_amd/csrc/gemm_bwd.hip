@@ -625,6 +625,309 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   }
 }
+
+// ------------------------------------------------------------ one wave per SIMD
+//
+// The same backward with four waves, each owning 64 output columns over all
+// 256 rows of the tile (256 fp32 accumulators per lane, one wave per SIMD):
+// per 64-row step a lane dequantizes 64 columns of its weight row -- exactly
+// one 64-block, one table per 64 weights -- into a per-wave tile of 64 rows x
+// 64 columns, and each A fragment read from the dY tile feeds two MFMAs (the
+// two 32-column halves).  Against two waves of 32 columns per SIMD this halves
+// the A-fragment reads and the per-block tables per flop; the price is that
+// one wave must hide its own latencies.  Used for block size 64 without an
+// adapter term; the same dY staging, transposing reads and hand-over as the
+// kernel above.
+constexpr int NWAVE_W = 4;
+constexpr int BROW_W = 144;                  // weight-tile row: 128 bytes of bf16 + 16 of padding
+constexpr int BTILE_W = TN * BROW_W;         // per-wave weight tile: 64 rows x 64 bf16
+
+struct RowCodes64 {
+  uint4 w0, w1;   // 64 codes of this lane's weight row (one block)
+  AbsmaxRaw r;
+};
+
+template <bool DX_BF16, bool DQ, bool FP4>
+__global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_wide_kernel(
+    const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    AbsmaxSrc src, void *__restrict__ dX, int tiles_m, int tiles_k) {
+  __shared__ __attribute__((aligned(4096))) uint8_t as0[ATILE];
+  __shared__ __attribute__((aligned(4096))) uint8_t as1[ATILE];
+  __shared__ __attribute__((aligned(4096))) uint8_t as2[ATILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t bs[NWAVE_W * BTILE_W];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int tm, tk;
+  tile_of_main(blockIdx.x, tiles_m, tiles_k, tm, tk);
+  const int64_t m0 = (int64_t)tm * TM, k0 = (int64_t)tk * TK;
+  const float mu = DQ ? *src.mean : 0.f;
+  const int bl = lane & 31, kg = lane >> 5;
+
+  // this wave's 64 output columns (K % 64 == 0: all valid or all past K; past K
+  // they read columns K-64 .. K-1 and are never stored)
+  const int64_t kcol = k0 + 64 * wave;
+  const int64_t kc = kcol < K ? kcol : K - 64;
+  const uint8_t *wq = packed + (int64_t)lane * (K / 2) + kc / 2;
+  const int64_t blk0 = (int64_t)lane * (K / kBlock) + kc / kBlock;
+
+  // dY tile loads: wave w's load i (0..7) covers tile rows 8(8w + i) .. +7
+  const int64_t wrow0 = m0 + 64 * wave;
+  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 64 ? 64 : M - wrow0);
+  const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * N * 2));
+  const uint8_t *ywave = uniform_ptr(dY + (wrows > 0 ? wrow0 : 0) * N);
+  uint32_t yvoff[8];
+  int ylast = 0;
+  {
+    const int64_t lastn = N - (((N + TN - 1) / TN) - 1) * TN;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int ch = (lane & 7) ^ ((r >> 1) & 7);
+      yvoff[i] = (uint32_t)(r * N * 2) + ((uint32_t)ch << 4);
+      ylast |= (8 * ch < lastn) << i;
+    }
+  }
+  int aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = bl * AROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
+
+  uint8_t *bw = bs + wave * BTILE_W;
+  // transposing reads for slice sl, half h, column half c: as in the kernel
+  // above with 144-byte rows and the half's 64-byte offset
+  uint32_t btr;
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int rbase = 32 * (G >> 1) + (j >> 2);
+    const int chunk = 2 * (G & 1) + ((j & 3) >> 1);
+    btr = (uint32_t)(uintptr_t)bw + (uint32_t)(rbase * BROW_W + (chunk << 4) + 8 * (j & 1));
+  }
+  const int64_t ns = (N + TN - 1) / TN;
+  auto clamps = [&](int64_t s) { return s < ns ? s : ns - 1; };
+  auto yrsrc = [&](int64_t s) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(ywave + clamps(s) * (TN * 2)), (short)0,
+                                             wbytes, 0x00020000);
+  };
+  auto issue_y1 = [&](__amdgpu_buffer_rsrc_t rs, int64_t s, uint8_t *dst, int i) {
+    const bool in = clamps(s) < ns - 1 || ((ylast >> i) & 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (8 * wave + i) * 1024), 16,
+                                             in ? yvoff[i] : 0x80000000u, 0, 0, 0);
+  };
+  auto issue_codes = [&](int64_t s, RowCodes64 &c) {
+    const int64_t sc = clamps(s);
+    const int64_t n = sc * TN + lane;
+    const int64_t dn = n < N ? sc * TN : N - 1 - lane;
+    const uint4 *wp = reinterpret_cast<const uint4 *>(wq + dn * (K / 2));
+    c.w0 = wp[0];
+    c.w1 = wp[1];
+    c.r = load_raw<DQ>(src, blk0 + dn * (K / kBlock));
+  };
+  auto ahat_at = [&](int64_t s, const RowCodes64 &c) {
+    const float v = ahat_of(c.r, DQ, mu);
+    return (s < ns && s * TN + lane < N) ? v : 0.f;
+  };
+  // (inline assembly for the reason given in the kernel above; every result
+  // is consumed after an explicit lgkmcnt wait)
+  auto tr_read = [&](int sl, int h, int c) {
+    v4s v;
+    switch ((8 * sl + 4 * h) * BROW_W + 64 * c) {
+#define NF4_TR(B) case B: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:" #B : "=v"(v) : "v"(btr) : "memory"); break;
+      NF4_TR(0) NF4_TR(576) NF4_TR(1152) NF4_TR(1728) NF4_TR(2304) NF4_TR(2880) NF4_TR(3456) NF4_TR(4032)
+      NF4_TR(64) NF4_TR(640) NF4_TR(1216) NF4_TR(1792) NF4_TR(2368) NF4_TR(2944) NF4_TR(3520) NF4_TR(4096)
+#undef NF4_TR
+    }
+    return v;
+  };
+  auto write_row = [&](const uint32_t st[32]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<uint4 *>(bw + lane * BROW_W + (c << 4)) =
+          make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
+  };
+  auto dequant_word = [&](uint32_t wd, const Lut &t, uint32_t *out, int phase, Sel4 &sa, Sel4 &sb) {
+    if (phase == 0) select8(wd, sa, sb);
+    if (phase == 1) lookup4(sa, t, out[0], out[1]);
+    if (phase == 2) lookup4(sb, t, out[2], out[3]);
+  };
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][c][r] = 0.f;
+
+  uint4 a[8];
+  v4s b0[2][2], b1[2][2];   // B fragments [column half][n half] of the current and the next slice
+  uint32_t st[32];          // the next step's dequantized weight row, staged for the LDS write
+  RowCodes64 cs0, cs1, cs2;
+
+  // prologue: codes of steps 0-2 and dY tiles 0 and 1 in flight; step 0's row
+  // dequantized and written, its slice-0 B fragments read
+  {
+    RowCodes64 c0;
+    issue_codes(0, c0);
+    const __amdgpu_buffer_rsrc_t r0 = yrsrc(0), r1 = yrsrc(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_y1(r0, 0, as0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_y1(r1, 1, as1, i);
+    issue_codes(1, cs1);
+    issue_codes(2, cs2);
+    Lut t;
+    const float ah = ahat_at(0, c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lut_quarter<FP4>(ah, q, t);
+    const uint32_t wd[8] = {c0.w0.x, c0.w0.y, c0.w0.z, c0.w0.w, c0.w1.x, c0.w1.y, c0.w1.z, c0.w1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      Sel4 sa, sb;
+      select8(wd[c], sa, sb);
+      lookup4(sa, t, st[4 * c], st[4 * c + 1]);
+      lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
+    }
+    write_row(st);
+    b0[0][0] = tr_read(0, 0, 0);
+    b0[0][1] = tr_read(0, 1, 0);
+    b0[1][0] = tr_read(0, 0, 1);
+    b0[1][1] = tr_read(0, 1, 1);
+  }
+  // dY tile 0 landed (tile 1 and the codes of steps 1 and 2 may be in flight);
+  // the slice-0 B fragments read (lgkmcnt(0))
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + 2 * (DQ ? 4 : 3)) & ~(0xF << 8));
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(as0 + aoff[0] + i * 32 * AROW);
+
+  // One N-step as 32 groups of two MFMAs (slice j = groups 8j .. 8j+7; group g
+  // of a slice: M-tile g against both column halves):
+  //   A reads     after its MFMAs, group g refills a[g] for the next slice;
+  //               the next step's slice 0 after the hand-over, from `nx`
+  //   B reads     the next slice's four transposing reads in groups 0-3
+  //   dY loads    the tile two steps ahead into `ld`: groups 0, 3, ..., 21
+  //   dequant     the next step's table (groups 0, 1) and its eight code
+  //               words (groups 2-25), staged in registers; written to the
+  //               weight tile in group 26 (the step's last B reads completed
+  //               at group 24)
+  //   hand-over   before group 28: this wave's LDS traffic is complete and the
+  //               next dY tile has landed, barrier, codes three steps ahead,
+  //               the next step's slice-0 B reads
+  auto step = [&](int64_t s, uint8_t *rd, uint8_t *nx, uint8_t *ld, const RowCodes64 &cn, RowCodes64 &cfill) {
+    Sel4 sa, sb;
+    Lut t;
+    float ahn = 0.f;
+    const __amdgpu_buffer_rsrc_t rsl = yrsrc(s + 2);
+    const uint32_t wd[8] = {cn.w0.x, cn.w0.y, cn.w0.z, cn.w0.w, cn.w1.x, cn.w1.y, cn.w1.z, cn.w1.w};
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int slice = r / 8, g = r % 8;
+      v4s(*bc)[2] = (slice & 1) ? b1 : b0;
+      v4s(*bn)[2] = (slice & 1) ? b0 : b1;
+      if (r == 28) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(8) & ~(0xF << 8));   // vmcnt(8) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        sched_cut();
+        issue_codes(s + 3, cfill);
+        b0[0][0] = tr_read(0, 0, 0);
+        b0[0][1] = tr_read(0, 1, 0);
+        b0[1][0] = tr_read(0, 0, 1);
+        b0[1][1] = tr_read(0, 1, 1);
+        sched_cut();
+      }
+      if (g == 0) {
+        // this slice's B fragments: read in groups 0-3 of the previous slice
+        // (then four A reads) or after the hand-over (then eight A reads)
+        if (slice == 0)
+          __builtin_amdgcn_s_waitcnt(lgkm_imm(8));
+        else
+          __builtin_amdgcn_s_waitcnt(lgkm_imm(4));
+        sched_cut();
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, (uint4){(uint32_t)__builtin_bit_cast(uint64_t, bc[c][0]),
+                                                             (uint32_t)(__builtin_bit_cast(uint64_t, bc[c][0]) >> 32),
+                                                             (uint32_t)__builtin_bit_cast(uint64_t, bc[c][1]),
+                                                             (uint32_t)(__builtin_bit_cast(uint64_t, bc[c][1]) >> 32)});
+        acc[g][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[g]), bv, acc[g][c], 0, 0, 0);
+      }
+      if (slice < 3) {
+        a[g] = *reinterpret_cast<const uint4 *>(rd + aoff[slice + 1] + g * 32 * AROW);
+        if (g < 4) bn[g >> 1][g & 1] = tr_read(slice + 1, g & 1, g >> 1);
+      } else if (r >= 28) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * (r - 28) + u;
+          a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * AROW);
+        }
+      }
+      if (r % 3 == 0 && r <= 21) issue_y1(rsl, s + 2, ld, r / 3);
+      if (r == 0) {
+        ahn = ahat_at(s + 1, cn);
+        lut_quarter<FP4>(ahn, 0, t);
+        lut_quarter<FP4>(ahn, 1, t);
+      }
+      if (r == 1) {
+        lut_quarter<FP4>(ahn, 2, t);
+        lut_quarter<FP4>(ahn, 3, t);
+      }
+      if (r >= 2 && r <= 25) {
+        const int c = (r - 2) / 3, ph = (r - 2) % 3;
+        dequant_word(wd[c], t, st + 4 * c, ph, sa, sb);
+      }
+      if (r == 26) write_row(st);
+      sched_cut();
+    }
+  };
+  int64_t s = 0;
+  for (; s + 3 <= ns; s += 3) {
+    step(s, as0, as1, as2, cs1, cs0);
+    step(s + 1, as1, as2, as0, cs2, cs1);
+    step(s + 2, as2, as0, as1, cs0, cs2);
+  }
+  if (s < ns) step(s, as0, as1, as2, cs1, cs0);
+  if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
+  if (m0 + TM <= M && k0 + TK <= K && K < ((int64_t)1 << 27)) {
+    constexpr int ES = DX_BF16 ? 2 : 4;
+    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)K + bl) * ES;
+    uint8_t *xcol = reinterpret_cast<uint8_t *>(dX) + (m0 * K + kcol) * ES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          uint8_t *rowp = xcol + (int64_t)(32 * i + 8 * (r / 4) + (r % 4)) * K * ES + 32 * c * ES;
+          if (DX_BF16)
+            *reinterpret_cast<uint16_t *>(rowp + voff) = (uint16_t)(pack_bf16x2(acc[i][c][r], 0.f) & 0xffffu);
+          else
+            *reinterpret_cast<float *>(rowp + voff) = acc[i][c][r];
+        }
+      }
+    }
+  } else if (kcol < K) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
+          if (row < M) {
+            const int64_t off = row * K + kcol + 32 * c + bl;
+            if (DX_BF16)
+              reinterpret_cast<uint16_t *>(dX)[off] = (uint16_t)(pack_bf16x2(acc[i][c][r], 0.f) & 0xffffu);
+            else
+              reinterpret_cast<float *>(dX)[off] = acc[i][c][r];
+          }
+        }
+      }
+    }
+  }
+}
 }  // namespace tr_kernel
 
 }  // namespace
@@ -634,7 +937,18 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
                          hipStream_t stream) {
   const uint16_t *dY = reinterpret_cast<const uint16_t *>(dy);
   const bool has_lr = lr.r > 0;
-  if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
+  if (N % 8 == 0 && N < ((int64_t)1 << 24) && src.lbs == 6 && !has_lr) {
+    // block size 64, no adapter term: one wave per SIMD, 64 columns per wave
+    using namespace tr_kernel;
+    using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, void *, int, int);
+    static const K_t kern[2][2][2] = {{{bwd_dx_wide_kernel<false, false, false>, bwd_dx_wide_kernel<false, false, true>},
+                                       {bwd_dx_wide_kernel<false, true, false>, bwd_dx_wide_kernel<false, true, true>}},
+                                      {{bwd_dx_wide_kernel<true, false, false>, bwd_dx_wide_kernel<true, false, true>},
+                                       {bwd_dx_wide_kernel<true, true, false>, bwd_dx_wide_kernel<true, true, true>}}};
+    const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
+    hipLaunchKernelGGL(kern[dx_is_bf16 ? 1 : 0][src.dq ? 1 : 0][src.qt ? 1 : 0], dim3((unsigned)(tiles_m * tiles_k)),
+                       dim3(64 * NWAVE_W), 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
+  } else if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
     using namespace tr_kernel;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
