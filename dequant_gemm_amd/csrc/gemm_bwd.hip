@@ -804,11 +804,11 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   //   A reads     after its MFMAs, group g refills a[g] for the next slice;
   //               the next step's slice 0 after the hand-over, from `nx`
   //   B reads     the next slice's four transposing reads in groups 0-3
-  //   dY loads    the tile two steps ahead into `ld`: groups 0, 3, ..., 21
+  //   dY loads    the tile two steps ahead into `ld`: groups 0, 2, ..., 14
   //   dequant     the next step's table (groups 0, 1) and its eight code
   //               words (groups 2-25), staged in registers; written to the
-  //               weight tile in group 26 (the step's last B reads completed
-  //               at group 24)
+  //               weight tile two 16-byte chunks per group in groups 24-27
+  //               (the step's last B reads completed at group 24)
   //   hand-over   before group 28: this wave's LDS traffic is complete and the
   //               next dY tile has landed, barrier, codes three steps ahead,
   //               the next step's slice-0 B reads
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
           a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * AROW);
         }
       }
-      if (r % 3 == 0 && r <= 21) issue_y1(rsl, s + 2, ld, r / 3);
+      if (r % 2 == 0 && r <= 14) issue_y1(rsl, s + 2, ld, r / 2);
       if (r == 0) {
         ahn = ahat_at(s + 1, cn);
         lut_quarter<FP4>(ahn, 0, t);
@@ -875,7 +875,13 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
         const int c = (r - 2) / 3, ph = (r - 2) % 3;
         dequant_word(wd[c], t, st + 4 * c, ph, sa, sb);
       }
-      if (r == 26) write_row(st);
+      if (r >= 24 && r < 28) {
+        // the row two 16-byte chunks per group, after the step's last B reads
+#pragma unroll
+        for (int c = 2 * (r - 24); c < 2 * (r - 24) + 2; ++c)
+          *reinterpret_cast<uint4 *>(bw + lane * BROW_W + (c << 4)) =
+              make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
+      }
       sched_cut();
     }
   };
