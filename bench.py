@@ -79,7 +79,7 @@ def measured_traffic(kernel):
 
 # kernels whose HBM-side traffic is recorded: kernel name -> (profiling op, source files)
 TRAFFIC_KERNELS = {
-    "fwd_large_kernel": ("fwd", ["dequant_gemm_amd/csrc/gemm_fwd.hip", "dequant_gemm_amd/csrc/nf4_common.h"]),
+    "fwd_wide_kernel": ("fwd", ["dequant_gemm_amd/csrc/gemm_fwd.hip", "dequant_gemm_amd/csrc/nf4_common.h"]),
     "bwd_dx_wide_kernel": ("bwd_dx", ["dequant_gemm_amd/csrc/gemm_bwd.hip", "dequant_gemm_amd/csrc/nf4_common.h"]),
 }
 COPY_BYTES = 1 << 30   # the calibration copy of run_single_op("copy")
@@ -859,10 +859,10 @@ def main():
         "config": {"workload": "prefill: M=4096 (8x512 tokens), K=4096, N=11008, NF4 blocksize 64 "
                                "double-quant; step = quantize + fwd + bwd-dX",
                    "M": 4096, "K": 4096, "N": 11008, "blocksize": 64, "double_quant": True},
-        "roofline": {"kernel": "fwd_large_kernel" if dom == "fwd" else "bwd_dx_wide_kernel",
+        "roofline": {"kernel": "fwd_wide_kernel" if dom == "fwd" else "bwd_dx_wide_kernel",
                      "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("fwd_large_kernel" if dom == "fwd" else "bwd_dx_wide_kernel")},
+                     "traffic": measured_traffic("fwd_wide_kernel" if dom == "fwd" else "bwd_dx_wide_kernel")},
         "ops": {k: _rounded(v) for k, v in ops.items()},
     }
     if not a.no_cpu_baseline:

@@ -9,16 +9,23 @@
 // fp32 (or bf16) [M, N].  W^ is formed in registers as bf16 and fed to bf16
 // MFMA with fp32 accumulation.
 //
-// Two kernels, chosen by M:
-//   fwd_small_kernel  M <= 16, streaming-bound: one workgroup per 16 weight
-//                     rows, its eight waves split K; every weight byte is read
-//                     once, all of a lane's loads are issued together.
-//   fwd_large_kernel  M > 16, matrix-core-bound: 256x256 output tiles, eight
-//                     waves; X staged through LDS (three stages, filled by
-//                     buffer-to-LDS loads), each wave dequantizes its own 32
-//                     weight rows straight into MFMA operand registers (no LDS
-//                     round trip, no duplicate dequantization inside the
-//                     workgroup).
+// Kernels, chosen by M and the weight's layout:
+//   fwd_rows_kernel   M <= 16 over many weight rows: one 16-wave workgroup per
+//                     CU walks a run of 16-row groups with X in registers.
+//   fwd_small_kernel  M <= 16 otherwise, streaming-bound: one workgroup per 16
+//                     weight rows, its eight waves split K; every weight byte is
+//                     read once, all of a lane's loads are issued together.
+//   fwd_wide_kernel   M > 16, block size 64, no adapter term, K % 256 == 0:
+//                     256x256 output tiles, four waves of 64 weight rows (one
+//                     wave per SIMD), a lane dequantizing whole 64-blocks.
+//   fwd_large_kernel  M > 16 otherwise, matrix-core-bound: 256x256 output
+//                     tiles, eight waves; X staged through LDS (three stages,
+//                     filled by buffer-to-LDS loads), each wave dequantizes its
+//                     own 32 weight rows straight into MFMA operand registers
+//                     (no LDS round trip, no duplicate dequantization inside
+//                     the workgroup).
+#include <utility>
+
 #include "nf4_launch.h"
 
 namespace nf4 {
@@ -511,6 +518,17 @@ struct StepCodes {
 
 __device__ __forceinline__ void sched_cut() { __builtin_amdgcn_sched_barrier(0); }
 
+// f(std::integral_constant<int, i>{}) for i = 0 .. n-1, each a separate
+// instance: the index is a constant wherever f uses it, however large the body
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 template <typename T>
 __device__ __forceinline__ const uint8_t *uniform_ptr(const T *p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -802,6 +820,265 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 
+// ----------------------------------------------------------------- large M, one wave per SIMD
+//
+// The forward with four waves, each owning 64 output columns (two halves h of
+// 32: weight rows n0 + 64w + 32h + l%32) over all 256 rows of the tile: 256
+// fp32 accumulators per lane, one wave per SIMD, each A fragment feeding two
+// MFMAs.  K advances in double steps of 128 in which lane group kg = l/32
+// owns 64-block 2d + kg of both its weight rows, so a lane builds one table per
+// 64 weights of a row (the eight-wave kernel above: per 32).  MFMA slice j
+// (0..7) takes elements 8j .. 8j+7 of that block from both operands; the A
+// fragment of lane group kg comes from the X tile of its block, so a double
+// step reads two 64-K tiles at once: four LDS stages, one pair read while the
+// other loads.  A double step is 64 groups of two MFMAs (group g of a slice:
+// M-tile g against both halves); the other work:
+//   A reads     after its MFMAs, group g refills a[g] for the next slice; the
+//               next double step's slice 0 after the hand-over
+//   B words     the next slice's fragments (word j+1 of both rows) in groups
+//               0-5 of slice j < 7; the next double step's two tables once
+//               word 7 is done (slice 6 groups 6-7, slice 7 groups 0-1, in
+//               place), then its word 0 (slice 7 groups 2-7)
+//   X loads     the next double step's two tiles into the other pair of
+//               stages: groups 0, 2, ..., 30
+//   hand-over   before group 60: all loads and this wave's LDS reads complete,
+//               barrier, codes two double steps ahead (into the slot of this
+//               double step's own codes)
+// Used for block size 64 without an adapter term, K a multiple of 256 (double
+// steps in pairs: a loop body with a conditional second double step spills).
+constexpr int NWAVE_W = 4;
+
+struct DoubleCodes {
+  uint4 w[2][2];    // [row half][16-byte piece]: the 64 codes of each row's block
+  AbsmaxRaw r[2];   // the two blocks' absmax state
+};
+
+template <bool Y_BF16, bool DQ, bool FP4>
+__global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_wide_kernel(
+    const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    AbsmaxSrc src, void *__restrict__ Y, int tiles_m, int tiles_n) {
+  // two pairs of stages (tile 2d, then tile 2d + 1), one array per pair so
+  // that the compiler can tell the pair being read from the pair being loaded
+  // (a pointer chosen per lane between two arrays would make every LDS read
+  // wait for all loads in flight)
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0[2 * XTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1[2 * XTILE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const float mu = DQ ? *src.mean : 0.f;
+  const int bl = lane & 31, kg = lane >> 5;
+
+  // B operands: this lane's two weight rows; a column past N loads row N-1
+  // (its outputs are never stored)
+  const uint8_t *wq[2];
+  int64_t blk0[2], ncol[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ncol[h] = n0 + 64 * wave + 32 * h + bl;
+    const int64_t nc = ncol[h] < N ? ncol[h] : N - 1;
+    wq[h] = packed + nc * (K / 2) + kg * 32;   // block kg of each double step
+    blk0[h] = nc * (K / kBlock) + kg;
+  }
+
+  // X tile loads: a 64-K tile is 256 rows x 128 bytes; wave w's load i (0..7)
+  // covers tile rows 8(8w + i) .. +7, swizzled and bounded as in the kernel above
+  const int64_t wrow0 = m0 + 64 * wave;
+  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 64 ? 64 : M - wrow0);
+  const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * K * 2));
+  const uint8_t *xwave = uniform_ptr(X + (wrows > 0 ? wrow0 : 0) * K);
+  uint32_t xvoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    xvoff[i] = (uint32_t)(r * K * 2) + ((uint32_t)((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
+  // A fragments: lane l reads row 32i + l%32 of the tile of its block, logical
+  // chunk j of slice j, stored at chunk j ^ ((row/2) & 7)
+  int aoff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) aoff[j] = bl * XROW + ((j ^ ((bl >> 1) & 7)) << 4);
+
+  const int64_t nd = K / (2 * BK);
+  auto clampd = [&](int64_t d) { return d < nd ? d : nd - 1; };
+  auto xrsrc = [&](int64_t t) {   // the 64-K tile t
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + t * (BK * 2)), (short)0, wbytes,
+                                             0x00020000);
+  };
+  auto issue_x1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t *dst, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (8 * wave + i) * 1024), 16, xvoff[i], 0, 0, 0);
+  };
+  auto issue_codes = [&](int64_t d, DoubleCodes &c) {
+    const int64_t dc = clampd(d);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(wq[h] + dc * BK);
+      c.w[h][0] = p[0];
+      c.w[h][1] = p[1];
+      c.r[h] = load_raw<DQ>(src, blk0[h] + 2 * dc);
+    }
+  };
+  auto ahat_at = [&](int64_t d, const DoubleCodes &c, int h) { return d < nd ? ahat_of(c.r[h], DQ, mu) : 0.f; };
+  auto word = [&](const DoubleCodes &c, int h, int j) {
+    const uint4 &w = c.w[h][j >> 2];
+    return (j & 3) == 0 ? w.x : ((j & 3) == 1 ? w.y : ((j & 3) == 2 ? w.z : w.w));
+  };
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][h][r] = 0.f;
+
+  uint4 a[8];
+  uint32_t B0[2][4], B1[2][4];   // B fragments [row half] of the current and the next slice
+  Lut lut[2];
+  DoubleCodes cs0, cs1;          // double step d's codes sit in slot d % 2
+
+  // prologue: codes of double steps 0 and 1, the tiles of double step 0; its
+  // tables and slice-0 fragments
+  issue_codes(0, cs0);
+  {
+    const __amdgpu_buffer_rsrc_t r0 = xrsrc(0), r1 = xrsrc(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_x1(r0, xp0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_x1(r1, xp0 + XTILE, i);
+  }
+  issue_codes(1, cs1);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float ah = ahat_at(0, cs0, h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) make_lut_quarter<FP4>(ah, q, lut[h]);
+    Sel4 sa, sb;
+    select8(word(cs0, h, 0), sa, sb);
+    lookup4(sa, lut[h], B0[h][0], B0[h][1]);
+    lookup4(sb, lut[h], B0[h][2], B0[h][3]);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  sched_cut();
+  {
+    const uint8_t *base = xp0 + kg * XTILE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(base + aoff[0] + i * 32 * XROW);
+  }
+
+  // rdp: the pair read (tiles 2d, 2d+1); ldp: the pair loaded (2d+2, 2d+3)
+  auto dstep = [&](int64_t d, uint8_t *rdp, uint8_t *ldp, DoubleCodes &cc, const DoubleCodes &cn) {
+    Sel4 sa[2], sb[2];
+    float ahn[2] = {0.f, 0.f};
+    const uint8_t *rd = rdp + kg * XTILE;
+    const uint8_t *nx = ldp + kg * XTILE;
+    const int64_t t1 = 2 * clampd(d + 1);
+    const __amdgpu_buffer_rsrc_t rl0 = xrsrc(t1), rl1 = xrsrc(t1 + 1);
+    static_for<64>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      constexpr int slice = r / 8, g = r % 8;
+      uint32_t(*bc)[4] = (slice & 1) ? B1 : B0;
+      uint32_t(*bn)[4] = (slice & 1) ? B0 : B1;
+      if (r == 60) {
+        __builtin_amdgcn_s_waitcnt(0);   // the next tiles landed, this wave's LDS reads done
+        __builtin_amdgcn_s_barrier();
+        sched_cut();
+        issue_codes(d + 2, cc);
+        sched_cut();
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[g][h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[g]), as_bf16x8(bc[h]), acc[g][h], 0, 0, 0);
+      if (slice < 7) {
+        a[g] = *reinterpret_cast<const uint4 *>(rd + aoff[slice + 1] + g * 32 * XROW);
+      } else if (r >= 60) {
+        // the next double step's slice-0 fragments: a[i] after the hand-over and
+        // after its last MFMA here (group 56 + i)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if ((56 + i > 60 ? 56 + i : 60) == r) a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * XROW);
+      }
+      if (r % 2 == 0 && r <= 30) {
+        const int piece = r / 2;   // 0..7 tile 2d+2, 8..15 tile 2d+3
+        if (piece < 8)
+          issue_x1(rl0, ldp, piece);
+        else
+          issue_x1(rl1, ldp + XTILE, piece - 8);
+      }
+      // B words: word slice+1 of both rows for the next slice
+      if (slice < 7 && g < 6) {
+        const int h = g / 3, ph = g % 3;
+        if (ph == 0) select8(word(cc, h, slice + 1), sa[h], sb[h]);
+        if (ph == 1) lookup4(sa[h], lut[h], bn[h][0], bn[h][1]);
+        if (ph == 2) lookup4(sb[h], lut[h], bn[h][2], bn[h][3]);
+      }
+      // the next double step's tables (word 7's lookups are done in group 53)
+      if (r >= 54 && r <= 57) {
+        const int h = (r - 54) >> 1, q0 = 2 * ((r - 54) & 1);
+        if (q0 == 0) ahn[h] = ahat_at(d + 1, cn, h);
+        make_lut_quarter<FP4>(ahn[h], q0, lut[h]);
+        make_lut_quarter<FP4>(ahn[h], q0 + 1, lut[h]);
+      }
+      // and its word 0
+      if (r >= 58) {
+        const int q = r - 58, h = q / 3, ph = q % 3;
+        if (ph == 0) select8(word(cn, h, 0), sa[h], sb[h]);
+        if (ph == 1) lookup4(sa[h], lut[h], bn[h][0], bn[h][1]);
+        if (ph == 2) lookup4(sb[h], lut[h], bn[h][2], bn[h][3]);
+      }
+      sched_cut();
+    });
+  };
+  for (int64_t d = 0; d < nd; d += 2) {
+    dstep(d, xp0, xp1, cs0, cs1);
+    dstep(d + 1, xp1, xp0, cs1, cs0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
+  if (m0 + BM <= M && n0 + BN <= N && N < ((int64_t)1 << 27)) {
+    constexpr int ES = Y_BF16 ? 2 : 4;
+    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)N + bl) * ES;
+    uint8_t *ycol = reinterpret_cast<uint8_t *>(Y) + (m0 * N + n0 + 64 * wave) * ES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          uint8_t *rowp = ycol + (int64_t)(32 * i + 8 * (r / 4) + (r % 4)) * N * ES + 32 * h * ES;
+          if (Y_BF16)
+            *reinterpret_cast<uint16_t *>(rowp + voff) = (uint16_t)(pack_bf16x2(acc[i][h][r], 0.f) & 0xffffu);
+          else
+            *reinterpret_cast<float *>(rowp + voff) = acc[i][h][r];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (ncol[h] >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
+          if (row < M) {
+            const int64_t off = row * N + ncol[h];
+            if (Y_BF16)
+              reinterpret_cast<uint16_t *>(Y)[off] = (uint16_t)(pack_bf16x2(acc[i][h][r], 0.f) & 0xffffu);
+            else
+              reinterpret_cast<float *>(Y)[off] = acc[i][h][r];
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
@@ -848,6 +1125,16 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
     else
       hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr,
                          y);
+  } else if (src.lbs == 6 && lr.r == 0 && K % (4 * BK) == 0) {
+    // block size 64, no adapter term, K a multiple of 256: one wave per SIMD, 64 columns per wave
+    using W_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, void *, int, int);
+    static const W_t kern[2][2][2] = {{{fwd_wide_kernel<false, false, false>, fwd_wide_kernel<false, false, true>},
+                                       {fwd_wide_kernel<false, true, false>, fwd_wide_kernel<false, true, true>}},
+                                      {{fwd_wide_kernel<true, false, false>, fwd_wide_kernel<true, false, true>},
+                                       {fwd_wide_kernel<true, true, false>, fwd_wide_kernel<true, true, true>}}};
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern[y_is_bf16 ? 1 : 0][src.dq ? 1 : 0][src.qt ? 1 : 0], dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(64 * NWAVE_W), 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
   } else {
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
