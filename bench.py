@@ -762,6 +762,11 @@ def run_single_op(dg, op, steps, warmup):
         elif op == "dequantize":
             Wh = torch.empty((N, K), dtype=torch.bfloat16, device=d)
             fn = lambda i: dg.nf4_dequantize(q, out=Wh)
+        elif op == "dense_fwd":
+            # hipBLASLt's dense bf16 GEMM of the forward's shape (X [M, K] x W^T), for comparison
+            X = synth.prefill_x().to(d)
+            Wh = dg.nf4_dequantize(q)
+            fn = lambda i: torch.matmul(X, Wh.t())
         elif op == "dense_bwd_dx":
             # hipBLASLt's dense bf16 GEMM of the backward's shape (dY [M, N] x W^ [N, K]), for comparison
             dY = synth.prefill_dy().to(d)
@@ -802,7 +807,7 @@ def main():
     ap.add_argument("--no-decode-trace", action="store_true",
                     help="skip the profiler run that takes the decode kernels' own durations")
     ap.add_argument("--op", default=None,
-                    choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "dense_bwd_dx", "decode",
+                    choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "dense_fwd", "dense_bwd_dx", "decode",
                              "decode_large", "decode_trace", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", default=None,

@@ -11,11 +11,11 @@
 // (whose operands hold eight consecutive reduction indices per lane).
 //
 // Two kernels:
-//   bwd_dx_kernel          N % 8 == 0 (16-byte dY rows) and N < 2^24: dY
+//   bwd_dx_wide_kernel     N % 8 == 0 (16-byte dY rows) and N < 2^24: dY
 //                          through buffer-to-LDS loads, each wave dequantizes
-//                          its own weight columns row by row into a private
+//                          its own 64 weight columns row by row into a private
 //                          LDS tile and reads MFMA operands back with
-//                          transposing LDS reads.
+//                          transposing LDS reads; one wave per SIMD.
 //   bwd_dx_generic_kernel  any shape: dY staged through registers, the
 //                          weight tile written to LDS already transposed.
 #include "nf4_launch.h"
@@ -267,31 +267,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 namespace tr_kernel {
 // ------------------------------------------------------------ main kernel
 //
-// Workgroup tile 256 (M) x 256 (K), eight waves, two per SIMD; wave w owns the
-// 32 output columns k0 + 32w .. +31 over all 256 rows (8 MFMA 32x32x16 tiles
-// stacked along M).  The reduction runs over N in steps of 64.
+// Workgroup tile 256 (M) x 256 (K), four waves, one per SIMD; wave w owns the
+// 64 output columns k0 + 64w .. +63 (two halves c of 32) over all 256 rows:
+// 8 x 2 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane.  The reduction
+// runs over N in steps of 64.
 //
 // A operand (dY): 256 x 64 tiles reach LDS by buffer-to-LDS loads through
 // three stages, laid out and read exactly like the X tiles of the forward
-// kernel.
+// kernel; each A fragment feeds two MFMAs (the two column halves).
 //
-// B operand (W^, 64 rows n x the wave's 32 columns k): lane l dequantizes row
-// n = 64s + l of the wave's columns -- 32 consecutive codes of one block, one
-// LUT -- and writes the 32 bf16 values as one row of a per-wave LDS tile
-// (80-byte rows: 64 bytes of data and 16 of padding).  The MFMA wants eight
-// consecutive n of one column per lane; the transposing LDS read
-// ds_read_b64_tr_b16 delivers exactly that: within a 16-lane group, output
-// lane i element e is element i%4 of the 8 bytes addressed by source lane
-// 4e + i/4, so source lane j of group G addresses row r0 + 4h + j/4 and
-// columns 16(G%2) + 4(j%4) .. +3 (kg = G/2, h = which half of the 8 n), and
-// output lane i receives rows r0 + 4h .. +3 of column 16(G%2) + i; r0 is the
-// first of the eight n that lane group kg's A fragment holds in that slice.
+// B operand (W^, 64 rows n x the wave's 64 columns k): lane l dequantizes row
+// n = 64s + l of the wave's columns -- 64 consecutive codes: one block and one
+// table at block sizes of 64 and more, two at 32 -- and writes the 64 bf16
+// values as one row of a per-wave LDS tile.  The MFMA wants eight consecutive
+// n of one column per lane; the transposing LDS read ds_read_b64_tr_b16
+// delivers exactly that: within a 16-lane group, output lane i element e is
+// element i%4 of the 8 bytes addressed by source lane 4e + i/4, so source lane
+// j of group G addresses row r0 + 4h + j/4 and columns
+// 32c + 16(G%2) + 4(j%4) .. +3 (kg = G/2, h = which half of the 8 n, c = the
+// column half), and output lane i receives rows r0 + 4h .. +3 of column
+// 32c + 16(G%2) + i; r0 = 32kg + 8sl is the first of the eight n that lane
+// group kg's A fragment holds in slice sl.
+//
+// Against two waves of 32 columns per SIMD this halves the A-fragment reads
+// and the per-block tables per flop; the price is that one wave must hide its
+// own latencies.
 constexpr int TM = 256, TK = 256, TN = 64;
-constexpr int NWAVE = 8;
+constexpr int NWAVE_W = 4;
 constexpr int AROW = TN * 2;             // 128-byte dY rows in LDS
 constexpr int ATILE = TM * AROW;         // 32 KiB
-constexpr int BROW = 80;                 // weight-tile row: 64 bytes of bf16 + 16 bytes of padding
-constexpr int BTILE = TN * BROW;         // per-wave weight tile: 64 rows x 32 bf16
+constexpr int BROW_W = 144;              // weight-tile row: 128 bytes of bf16 + 16 of padding
+constexpr int BTILE_W = TN * BROW_W;     // per-wave weight tile: 64 rows x 64 bf16
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -311,11 +317,6 @@ __device__ __forceinline__ void tile_of_main(int bid, int tiles_m, int tiles_k, 
   tk = in_group / gsize;
 }
 
-struct RowCodes {
-  uint4 w;        // 32 codes of this lane's weight row
-  AbsmaxRaw r;
-};
-
 __device__ __forceinline__ void sched_cut() { __builtin_amdgcn_sched_barrier(0); }
 
 template <typename T>
@@ -334,323 +335,21 @@ __device__ __forceinline__ void lut_quarter(float ahat, int q, Lut &t) {
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
 
-template <bool DX_BF16, bool DQ, bool LR, bool GBS, bool FP4>
-__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dx_kernel(
+// A lane's weight state for one N-step: 64 codes of its weight row and the
+// absmax state of their block (blocks, at block size 32).
+template <bool BS32>
+struct RowCodesW {
+  uint4 w0, w1;
+  ChunkAbsmax<BS32> r;
+};
+
+template <bool DX_BF16, bool DQ, bool FP4, bool BS32, bool LR>
+__global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_wide_kernel(
     const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ dX, int tiles_m, int tiles_k) {
   // the dY stages first (larger alignment places them at the lowest LDS
   // addresses), so that their fragment reads fold the tile offsets into the
   // 16-bit immediate of the LDS read instead of forming each address
-  __shared__ __attribute__((aligned(4096))) uint8_t as0[ATILE];
-  __shared__ __attribute__((aligned(4096))) uint8_t as1[ATILE];
-  __shared__ __attribute__((aligned(4096))) uint8_t as2[ATILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t bs[NWAVE * BTILE];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  int tm, tk;
-  tile_of_main(blockIdx.x, tiles_m, tiles_k, tm, tk);
-  const int64_t m0 = (int64_t)tm * TM, k0 = (int64_t)tk * TK;
-  const float mu = DQ ? *src.mean : 0.f;
-  const int bl = lane & 31, kg = lane >> 5;
-
-  // this wave's 32 output columns (K % 64 == 0, so they are all valid or all
-  // past K; past K they read columns K-32 .. K-1 and are never stored)
-  const int64_t kcol = k0 + 32 * wave;
-  const int64_t kc = kcol < K ? kcol : K - 32;
-  // weight row of this lane in step s: n = 64s + lane
-  const uint8_t *wq = packed + (int64_t)lane * (K / 2) + kc / 2;
-  // the block of row n, columns kc .. kc+31: blk0 + (n - lane) K/64 (block size 64), else
-  // the flat index n K + kc shifted by log2(block size) -- never straddles a block
-  const int64_t blk0 = (int64_t)lane * (K / kBlock) + kc / kBlock;
-
-  // dY tile loads, as the forward kernel's X tiles: wave w's load i (0..3)
-  // covers tile rows 8(4w + i) .. +7; one descriptor per wave and step sized
-  // to its existing rows; a 16-byte chunk past N gets an offset beyond the
-  // descriptor and loads zeros.  (Requires N % 8 == 0 and N < 2^24.)
-  const int64_t wrow0 = m0 + 32 * wave;
-  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 32 ? 32 : M - wrow0);
-  const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * N * 2));
-  const uint8_t *ywave = uniform_ptr(dY + (wrows > 0 ? wrow0 : 0) * N);
-  uint32_t yvoff[4];
-  int ylast = 0;   // bit i: load i's chunk exists in the last step (N need not be a multiple of 64)
-  {
-    const int64_t lastn = N - (((N + TN - 1) / TN) - 1) * TN;   // valid n in the last step
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * i + (lane >> 3);
-      const int ch = (lane & 7) ^ ((r >> 1) & 7);
-      yvoff[i] = (uint32_t)(r * N * 2) + ((uint32_t)ch << 4);
-      ylast |= (8 * ch < lastn) << i;
-    }
-  }
-  int aoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) aoff[j] = bl * AROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
-
-  // per-wave weight tile: row n at n * 80 bytes (the padding keeps both the
-  // row writes and the transposing reads clear of most bank conflicts;
-  // measured against a 64-byte, XOR-swizzled layout)
-  uint8_t *bw = bs + wave * BTILE;
-  // transposing reads for slice sl, half h: source lane j of group G reads row
-  // 32kg + 8sl + 4h + j/4 (the n range the A fragment of lane group kg holds
-  // in slice sl), columns 16(G%2) + 4(j%4): 16-byte chunk 2(G%2) + (j%4)/2,
-  // byte 8 * ((j%4) & 1); the slice/half part of the row is an immediate.
-  uint32_t btr;
-  {
-    const int G = lane >> 4, j = lane & 15;
-    const int rbase = 32 * (G >> 1) + (j >> 2);
-    const int chunk = 2 * (G & 1) + ((j & 3) >> 1);
-    btr = (uint32_t)(uintptr_t)bw + (uint32_t)(rbase * BROW + (chunk << 4) + 8 * (j & 1));
-  }
-  const int64_t ns = (N + TN - 1) / TN;
-  auto clamps = [&](int64_t s) { return s < ns ? s : ns - 1; };
-  auto yrsrc = [&](int64_t s) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(ywave + clamps(s) * (TN * 2)), (short)0,
-                                             wbytes, 0x00020000);
-  };
-  auto issue_y1 = [&](__amdgpu_buffer_rsrc_t rs, int64_t s, uint8_t *dst, int i) {
-    const bool in = clamps(s) < ns - 1 || ((ylast >> i) & 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * wave + i) * 1024), 16,
-                                             in ? yvoff[i] : 0x80000000u, 0, 0, 0);
-  };
-  // a row past N loads row N-1's codes (in bounds) and gets a^ = 0
-  auto issue_codes = [&](int64_t s, RowCodes &c) {
-    const int64_t sc = clamps(s);
-    const int64_t n = sc * TN + lane;
-    const int64_t dn = n < N ? sc * TN : N - 1 - lane;     // row offset from this lane's base row
-    c.w = *reinterpret_cast<const uint4 *>(wq + dn * (K / 2));
-    c.r = load_raw<DQ>(src, GBS ? (((int64_t)lane + dn) * K + kc) >> src.lbs : blk0 + dn * (K / kBlock));
-  };
-  auto ahat_at = [&](int64_t s, const RowCodes &c) {
-    const float v = ahat_of(c.r, DQ, mu);
-    return (s < ns && s * TN + lane < N) ? v : 0.f;
-  };
-  // The transposing read is issued as inline assembly: the compiler's wait
-  // insertion cannot tell the intrinsic's LDS address from the dY tiles that
-  // buffer-to-LDS loads are filling and would wait for all of those loads
-  // before every such read.  Its results are waited for explicitly (an
-  // lgkmcnt wait) before the MFMA that consumes them.
-  auto tr_read = [&](int sl, int h) {
-    v4s v;
-    switch ((8 * sl + 4 * h) * BROW) {   // the row part as an immediate byte offset
-#define NF4_TR(B) case B: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:" #B : "=v"(v) : "v"(btr) : "memory"); break;
-      NF4_TR(0) NF4_TR(320) NF4_TR(640) NF4_TR(960) NF4_TR(1280) NF4_TR(1600) NF4_TR(1920) NF4_TR(2240)
-#undef NF4_TR
-    }
-    return v;
-  };
-  auto write_row = [&](const uint32_t st[16]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<uint4 *>(bw + lane * BROW + (c << 4)) =
-          make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
-  };
-
-  f32x16 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  uint4 a[8];
-  v4s b0[2], b1[2];      // B fragments (two 4 x bf16 halves each) of the current and next slice
-  uint32_t st[16];       // the next step's dequantized weight row, staged for the LDS write
-  RowCodes cs0, cs1, cs2;
-
-  // prologue: dY tiles 0 and 1 and the codes of steps 0 and 1 in flight;
-  // step 0's weight row dequantized and written, its first B fragment read
-  {
-    RowCodes c0;
-    issue_codes(0, c0);
-    const __amdgpu_buffer_rsrc_t r0 = yrsrc(0), r1 = yrsrc(1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_y1(r0, 0, as0, i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_y1(r1, 1, as1, i);
-    issue_codes(1, cs1);
-    issue_codes(2, cs2);
-    Lut t;
-    const float ah = ahat_at(0, c0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lut_quarter<FP4>(ah, q, t);
-    const uint32_t wd[4] = {c0.w.x, c0.w.y, c0.w.z, c0.w.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      Sel4 sa, sb;
-      select8(wd[c], sa, sb);
-      lookup4(sa, t, st[4 * c], st[4 * c + 1]);
-      lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
-    }
-    write_row(st);
-    b0[0] = tr_read(0, 0);
-    b0[1] = tr_read(0, 1);
-  }
-  // dY tile 0 landed; the first B fragment read (lgkmcnt(0))
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + 2 * (DQ ? 3 : 2)) & ~(0xF << 8));
-  __builtin_amdgcn_s_barrier();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(as0 + aoff[0] + i * 32 * AROW);
-
-  // One N-step as 16 groups of two MFMAs (slice j = groups 4j .. 4j+3):
-  //   A reads     as in the forward kernel (the group's two fragments again
-  //               for the next slice; the next step's slice 0 after the
-  //               hand-over, from `nx`)
-  //   B reads     the next slice's two transposing reads in the slice's
-  //               first two groups; the next step's slice 0 after the
-  //               hand-over (after this wave's write of the next tile)
-  //   dY loads    the tile two steps ahead into `ld`: groups 0, 4, 8, 12
-  //   dequant     the next step's LUT and its four code words in groups
-  //               0-11, staged in registers; written to the weight tile in
-  //               group 12 (its last reads were issued in slice 2)
-  //   hand-over   before group 14: this wave's LDS traffic is complete and
-  //               the next dY tile has landed, barrier, codes three steps
-  //               ahead (into the slot of this step's own codes: step s + i
-  //               sits in slot (s + i) % 3)
-  auto step = [&](int64_t s, uint8_t *rd, uint8_t *nx, uint8_t *ld, const RowCodes &cn, RowCodes &cfill) {
-    Sel4 sa, sb;
-    Lut t;
-    float ahn = 0.f;
-    const __amdgpu_buffer_rsrc_t rsl = yrsrc(s + 2);
-    const uint32_t wd[4] = {cn.w.x, cn.w.y, cn.w.z, cn.w.w};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int slice = r / 4, g = r % 4;
-      const v4s *bc = (slice & 1) ? b1 : b0;
-      v4s *bn = (slice & 1) ? b0 : b1;
-      if (r == 14) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4) & ~(0xF << 8));   // vmcnt(4) lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        sched_cut();
-        issue_codes(s + 3, cfill);
-        b0[0] = tr_read(0, 0);
-        b0[1] = tr_read(0, 1);
-        sched_cut();
-      }
-      if (g == 0) {
-        // the slice's B fragment: issued in groups 4j-4 and 4j-3 (slices 1-3,
-        // followed by four A reads) or after the previous hand-over (slice 0,
-        // followed by eight A reads)
-        if (slice == 0)
-          __builtin_amdgcn_s_waitcnt(lgkm_imm(8));
-        else
-          __builtin_amdgcn_s_waitcnt(lgkm_imm(4));
-        sched_cut();
-      }
-      {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, (uint4){(uint32_t)__builtin_bit_cast(uint64_t, bc[0]),
-                                                             (uint32_t)(__builtin_bit_cast(uint64_t, bc[0]) >> 32),
-                                                             (uint32_t)__builtin_bit_cast(uint64_t, bc[1]),
-                                                             (uint32_t)(__builtin_bit_cast(uint64_t, bc[1]) >> 32)});
-        acc[2 * g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[2 * g]), bv, acc[2 * g], 0, 0, 0);
-        acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[2 * g + 1]), bv, acc[2 * g + 1], 0, 0, 0);
-      }
-      if (slice < 3) {
-        const int off = aoff[slice + 1];
-        a[2 * g] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g) * 32 * AROW);
-        a[2 * g + 1] = *reinterpret_cast<const uint4 *>(rd + off + (2 * g + 1) * 32 * AROW);
-        if (g < 2) bn[g] = tr_read(slice + 1, g);
-      } else if (r >= 14) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * (r - 14) + u;
-          a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * AROW);
-        }
-      }
-      if (g == 0) issue_y1(rsl, s + 2, ld, slice);
-      // dequantization of the next step's weight row
-      if (r == 0) {
-        ahn = ahat_at(s + 1, cn);
-        lut_quarter<FP4>(ahn, 0, t);
-        lut_quarter<FP4>(ahn, 1, t);
-      }
-      if (r == 1) {
-        lut_quarter<FP4>(ahn, 2, t);
-        lut_quarter<FP4>(ahn, 3, t);
-      }
-      if (r >= 2 && r <= 13) {
-        const int c = (r - 2) / 3, ph = (r - 2) % 3;
-        if (ph == 0) select8(wd[c], sa, sb);
-        if (ph == 1) lookup4(sa, t, st[4 * c], st[4 * c + 1]);
-        if (ph == 2) lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
-      }
-      if (r == 13) write_row(st);
-      sched_cut();
-    }
-  };
-  // steps run in threes (one per LDS stage); the last one or two after the loop
-  int64_t s = 0;
-  for (; s + 3 <= ns; s += 3) {
-    step(s, as0, as1, as2, cs1, cs0);
-    step(s + 1, as1, as2, as0, cs2, cs1);
-    step(s + 2, as2, as0, as1, cs0, cs2);
-  }
-  if (s < ns) step(s, as0, as1, as2, cs1, cs0);
-  if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
-  __builtin_amdgcn_s_waitcnt(0);
-  if (LR) add_lowrank_32x8(acc, lr, m0, M, kc + bl, bl, kg, as0);
-
-  // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
-  const int64_t col = kcol + bl;
-  if (m0 + TM <= M && k0 + TK <= K && K < ((int64_t)1 << 27)) {
-    // a full tile: every store is a wave-uniform row address (scalar arithmetic) plus the
-    // lane's 32-bit byte offset (row 4kg, column l%32), with no per-store bounds test
-    constexpr int ES = DX_BF16 ? 2 : 4;
-    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)K + bl) * ES;
-    uint8_t *xcol = reinterpret_cast<uint8_t *>(dX) + (m0 * K + kcol) * ES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        uint8_t *rowp = xcol + (int64_t)(32 * i + 8 * (r / 4) + (r % 4)) * K * ES;
-        if (DX_BF16)
-          *reinterpret_cast<uint16_t *>(rowp + voff) = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
-        else
-          *reinterpret_cast<float *>(rowp + voff) = acc[i][r];
-      }
-    }
-  } else if (kcol < K) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
-        if (row < M) {
-          const int64_t off = row * K + col;
-          if (DX_BF16)
-            reinterpret_cast<uint16_t *>(dX)[off] = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
-          else
-            reinterpret_cast<float *>(dX)[off] = acc[i][r];
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------ one wave per SIMD
-//
-// The same backward with four waves, each owning 64 output columns over all
-// 256 rows of the tile (256 fp32 accumulators per lane, one wave per SIMD):
-// per 64-row step a lane dequantizes 64 columns of its weight row -- exactly
-// one 64-block, one table per 64 weights -- into a per-wave tile of 64 rows x
-// 64 columns, and each A fragment read from the dY tile feeds two MFMAs (the
-// two 32-column halves).  Against two waves of 32 columns per SIMD this halves
-// the A-fragment reads and the per-block tables per flop; the price is that
-// one wave must hide its own latencies.  Used for block size 64 without an
-// adapter term; the same dY staging, transposing reads and hand-over as the
-// kernel above.
-constexpr int NWAVE_W = 4;
-constexpr int BROW_W = 144;                  // weight-tile row: 128 bytes of bf16 + 16 of padding
-constexpr int BTILE_W = TN * BROW_W;         // per-wave weight tile: 64 rows x 64 bf16
-
-struct RowCodes64 {
-  uint4 w0, w1;   // 64 codes of this lane's weight row (one block)
-  AbsmaxRaw r;
-};
-
-template <bool DX_BF16, bool DQ, bool FP4>
-__global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dx_wide_kernel(
-    const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    AbsmaxSrc src, void *__restrict__ dX, int tiles_m, int tiles_k) {
   __shared__ __attribute__((aligned(4096))) uint8_t as0[ATILE];
   __shared__ __attribute__((aligned(4096))) uint8_t as1[ATILE];
   __shared__ __attribute__((aligned(4096))) uint8_t as2[ATILE];
@@ -667,16 +366,22 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   // they read columns K-64 .. K-1 and are never stored)
   const int64_t kcol = k0 + 64 * wave;
   const int64_t kc = kcol < K ? kcol : K - 64;
+  // weight row of this lane in step s: n = 64s + lane; the flat index of its
+  // first column, n K + kc, shifted by log2(block size) gives its block (64
+  // columns never straddle a block of 64 or more; at 32 they are two blocks)
   const uint8_t *wq = packed + (int64_t)lane * (K / 2) + kc / 2;
-  const int64_t blk0 = (int64_t)lane * (K / kBlock) + kc / kBlock;
+  const int64_t flat0 = (int64_t)lane * K + kc;
 
-  // dY tile loads: wave w's load i (0..7) covers tile rows 8(8w + i) .. +7
+  // dY tile loads, as the forward kernel's X tiles: wave w's load i (0..7)
+  // covers tile rows 8(8w + i) .. +7; one descriptor per wave and step sized
+  // to its existing rows; a 16-byte chunk past N gets an offset beyond the
+  // descriptor and loads zeros.  (Requires N % 8 == 0 and N < 2^24.)
   const int64_t wrow0 = m0 + 64 * wave;
   const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 64 ? 64 : M - wrow0);
   const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * N * 2));
   const uint8_t *ywave = uniform_ptr(dY + (wrows > 0 ? wrow0 : 0) * N);
   uint32_t yvoff[8];
-  int ylast = 0;
+  int ylast = 0;   // bit i: load i's chunk exists in the last step (N need not be a multiple of 64)
   {
     const int64_t lastn = N - (((N + TN - 1) / TN) - 1) * TN;
 #pragma unroll
@@ -691,9 +396,13 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
   for (int j = 0; j < 4; ++j) aoff[j] = bl * AROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
 
+  // per-wave weight tile: row n at n * 144 bytes (the padding keeps both the
+  // row writes and the transposing reads clear of most bank conflicts)
   uint8_t *bw = bs + wave * BTILE_W;
-  // transposing reads for slice sl, half h, column half c: as in the kernel
-  // above with 144-byte rows and the half's 64-byte offset
+  // transposing reads for slice sl, half h, column half c: source lane j of
+  // group G reads row 32kg + 8sl + 4h + j/4, columns 32c + 16(G%2) + 4(j%4):
+  // 16-byte chunk 4c + 2(G%2) + (j%4)/2, byte 8 * ((j%4) & 1); the slice, half
+  // and column-half parts of the address are an immediate
   uint32_t btr;
   {
     const int G = lane >> 4, j = lane & 15;
@@ -712,21 +421,25 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (8 * wave + i) * 1024), 16,
                                              in ? yvoff[i] : 0x80000000u, 0, 0, 0);
   };
-  auto issue_codes = [&](int64_t s, RowCodes64 &c) {
+  // a row past N loads row N-1's codes (in bounds) and gets a^ = 0
+  auto issue_codes = [&](int64_t s, RowCodesW<BS32> &c) {
     const int64_t sc = clamps(s);
     const int64_t n = sc * TN + lane;
-    const int64_t dn = n < N ? sc * TN : N - 1 - lane;
+    const int64_t dn = n < N ? sc * TN : N - 1 - lane;     // row offset from this lane's base row
     const uint4 *wp = reinterpret_cast<const uint4 *>(wq + dn * (K / 2));
     c.w0 = wp[0];
     c.w1 = wp[1];
-    c.r = load_raw<DQ>(src, blk0 + dn * (K / kBlock));
+    c.r.template load<DQ>(src, (flat0 + dn * K) >> src.lbs);
   };
-  auto ahat_at = [&](int64_t s, const RowCodes64 &c) {
-    const float v = ahat_of(c.r, DQ, mu);
+  auto ahat_at = [&](int64_t s, const RowCodesW<BS32> &c, int u) {
+    const float v = c.r.ahat(u, DQ, mu);
     return (s < ns && s * TN + lane < N) ? v : 0.f;
   };
-  // (inline assembly for the reason given in the kernel above; every result
-  // is consumed after an explicit lgkmcnt wait)
+  // The transposing read is issued as inline assembly: the compiler's wait
+  // insertion cannot tell the intrinsic's LDS address from the dY tiles that
+  // buffer-to-LDS loads are filling and would wait for all of those loads
+  // before every such read.  Its results are waited for explicitly (an
+  // lgkmcnt wait) before the MFMA that consumes them.
   auto tr_read = [&](int sl, int h, int c) {
     v4s v;
     switch ((8 * sl + 4 * h) * BROW_W + 64 * c) {
@@ -760,12 +473,12 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   uint4 a[8];
   v4s b0[2][2], b1[2][2];   // B fragments [column half][n half] of the current and the next slice
   uint32_t st[32];          // the next step's dequantized weight row, staged for the LDS write
-  RowCodes64 cs0, cs1, cs2;
+  RowCodesW<BS32> cs0, cs1, cs2;
 
   // prologue: codes of steps 0-2 and dY tiles 0 and 1 in flight; step 0's row
   // dequantized and written, its slice-0 B fragments read
   {
-    RowCodes64 c0;
+    RowCodesW<BS32> c0;
     issue_codes(0, c0);
     const __amdgpu_buffer_rsrc_t r0 = yrsrc(0), r1 = yrsrc(1);
 #pragma unroll
@@ -775,12 +488,17 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
     issue_codes(1, cs1);
     issue_codes(2, cs2);
     Lut t;
-    const float ah = ahat_at(0, c0);
+    const float ah = ahat_at(0, c0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) lut_quarter<FP4>(ah, q, t);
     const uint32_t wd[8] = {c0.w0.x, c0.w0.y, c0.w0.z, c0.w0.w, c0.w1.x, c0.w1.y, c0.w1.z, c0.w1.w};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+      if (BS32 && c == 4) {
+        const float ah1 = ahat_at(0, c0, 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lut_quarter<FP4>(ah1, q, t);
+      }
       Sel4 sa, sb;
       select8(wd[c], sa, sb);
       lookup4(sa, t, st[4 * c], st[4 * c + 1]);
@@ -806,24 +524,26 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   //   B reads     the next slice's four transposing reads in groups 0-3
   //   dY loads    the tile two steps ahead into `ld`: groups 0, 2, ..., 14
   //   dequant     the next step's table (groups 0, 1) and its eight code
-  //               words (groups 2-25), staged in registers; written to the
-  //               weight tile two 16-byte chunks per group in groups 24-27
-  //               (the step's last B reads completed at group 24)
+  //               words (groups 2-25), staged in registers; at block size 32
+  //               words 0-3 in groups 2-13, the second block's table in
+  //               groups 14-15 (in place) and words 4-7 in groups 16-27;
+  //               written to the weight tile two 16-byte chunks per group in
+  //               groups 24-27 (the step's last B reads completed at group 24)
   //   hand-over   before group 28: this wave's LDS traffic is complete and the
   //               next dY tile has landed, barrier, codes three steps ahead,
   //               the next step's slice-0 B reads
-  auto step = [&](int64_t s, uint8_t *rd, uint8_t *nx, uint8_t *ld, const RowCodes64 &cn, RowCodes64 &cfill) {
+  auto step = [&](int64_t s, uint8_t *rd, uint8_t *nx, uint8_t *ld, const RowCodesW<BS32> &cn, RowCodesW<BS32> &cfill) {
     Sel4 sa, sb;
     Lut t;
     float ahn = 0.f;
     const __amdgpu_buffer_rsrc_t rsl = yrsrc(s + 2);
     const uint32_t wd[8] = {cn.w0.x, cn.w0.y, cn.w0.z, cn.w0.w, cn.w1.x, cn.w1.y, cn.w1.z, cn.w1.w};
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const int slice = r / 8, g = r % 8;
+    static_for<32>([&](auto rcst) {
+      constexpr int r = decltype(rcst)::value;
+      constexpr int slice = r / 8, g = r % 8;
       v4s(*bc)[2] = (slice & 1) ? b1 : b0;
       v4s(*bn)[2] = (slice & 1) ? b0 : b1;
-      if (r == 28) {
+      if constexpr (r == 28) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(8) & ~(0xF << 8));   // vmcnt(8) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         sched_cut();
@@ -834,10 +554,10 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
         b0[1][1] = tr_read(0, 1, 1);
         sched_cut();
       }
-      if (g == 0) {
+      if constexpr (g == 0) {
         // this slice's B fragments: read in groups 0-3 of the previous slice
         // (then four A reads) or after the hand-over (then eight A reads)
-        if (slice == 0)
+        if constexpr (slice == 0)
           __builtin_amdgcn_s_waitcnt(lgkm_imm(8));
         else
           __builtin_amdgcn_s_waitcnt(lgkm_imm(4));
@@ -851,31 +571,44 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
                                                              (uint32_t)(__builtin_bit_cast(uint64_t, bc[c][1]) >> 32)});
         acc[g][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[g]), bv, acc[g][c], 0, 0, 0);
       }
-      if (slice < 3) {
+      if constexpr (slice < 3) {
         a[g] = *reinterpret_cast<const uint4 *>(rd + aoff[slice + 1] + g * 32 * AROW);
-        if (g < 4) bn[g >> 1][g & 1] = tr_read(slice + 1, g & 1, g >> 1);
-      } else if (r >= 28) {
+        if constexpr (g < 4) bn[g >> 1][g & 1] = tr_read(slice + 1, g & 1, g >> 1);
+      } else if constexpr (r >= 28) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = 2 * (r - 28) + u;
           a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * AROW);
         }
       }
-      if (r % 2 == 0 && r <= 14) issue_y1(rsl, s + 2, ld, r / 2);
-      if (r == 0) {
-        ahn = ahat_at(s + 1, cn);
+      if constexpr (r % 2 == 0 && r <= 14) issue_y1(rsl, s + 2, ld, r / 2);
+      if constexpr (r == 0) {
+        ahn = ahat_at(s + 1, cn, 0);
         lut_quarter<FP4>(ahn, 0, t);
         lut_quarter<FP4>(ahn, 1, t);
       }
-      if (r == 1) {
+      if constexpr (r == 1) {
         lut_quarter<FP4>(ahn, 2, t);
         lut_quarter<FP4>(ahn, 3, t);
       }
-      if (r >= 2 && r <= 25) {
+      if constexpr (!BS32 && r >= 2 && r <= 25) {
         const int c = (r - 2) / 3, ph = (r - 2) % 3;
         dequant_word(wd[c], t, st + 4 * c, ph, sa, sb);
       }
-      if (r >= 24 && r < 28) {
+      if constexpr (BS32 && r >= 2 && r <= 13) {
+        const int c = (r - 2) / 3, ph = (r - 2) % 3;
+        dequant_word(wd[c], t, st + 4 * c, ph, sa, sb);
+      }
+      if constexpr (BS32 && (r == 14 || r == 15)) {
+        if constexpr (r == 14) ahn = ahat_at(s + 1, cn, 1);
+        lut_quarter<FP4>(ahn, 2 * (r - 14), t);
+        lut_quarter<FP4>(ahn, 2 * (r - 14) + 1, t);
+      }
+      if constexpr (BS32 && r >= 16 && r <= 27) {
+        const int c = 4 + (r - 16) / 3, ph = (r - 16) % 3;
+        dequant_word(wd[c], t, st + 4 * c, ph, sa, sb);
+      }
+      if constexpr (r >= 24 && r < 28) {
         // the row two 16-byte chunks per group, after the step's last B reads
 #pragma unroll
         for (int c = 2 * (r - 24); c < 2 * (r - 24) + 2; ++c)
@@ -883,7 +616,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
               make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
       }
       sched_cut();
-    }
+    });
   };
   int64_t s = 0;
   for (; s + 3 <= ns; s += 3) {
@@ -894,6 +627,11 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   if (s < ns) step(s, as0, as1, as2, cs1, cs0);
   if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
   __builtin_amdgcn_s_waitcnt(0);
+  if (LR) {
+    const int64_t col[2] = {kc + bl, kc + 32 + bl};
+    // ranks in chunks of 48 (256 staged rows of 112 bytes in the first dY stage)
+    add_lowrank_wide<48>(acc, lr, m0, M, col, bl, kg, as0);
+  }
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   if (m0 + TM <= M && k0 + TK <= K && K < ((int64_t)1 << 27)) {
@@ -943,34 +681,22 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
                          hipStream_t stream) {
   const uint16_t *dY = reinterpret_cast<const uint16_t *>(dy);
   const bool has_lr = lr.r > 0;
-  if (N % 8 == 0 && N < ((int64_t)1 << 24) && src.lbs == 6 && !has_lr) {
-    // block size 64, no adapter term: one wave per SIMD, 64 columns per wave
-    using namespace tr_kernel;
-    using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, void *, int, int);
-    static const K_t kern[2][2][2] = {{{bwd_dx_wide_kernel<false, false, false>, bwd_dx_wide_kernel<false, false, true>},
-                                       {bwd_dx_wide_kernel<false, true, false>, bwd_dx_wide_kernel<false, true, true>}},
-                                      {{bwd_dx_wide_kernel<true, false, false>, bwd_dx_wide_kernel<true, false, true>},
-                                       {bwd_dx_wide_kernel<true, true, false>, bwd_dx_wide_kernel<true, true, true>}}};
-    const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
-    hipLaunchKernelGGL(kern[dx_is_bf16 ? 1 : 0][src.dq ? 1 : 0][src.qt ? 1 : 0], dim3((unsigned)(tiles_m * tiles_k)),
-                       dim3(64 * NWAVE_W), 0, stream, dY, M, N, K, packed, src, dx, tiles_m, tiles_k);
-  } else if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
+  if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
+    // 16-byte dY rows: buffer-to-LDS dY tiles, transposing weight reads, one wave per SIMD
     using namespace tr_kernel;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
                          int, int);
-#define NF4_BWD(GBS, FP4)                                                                                     \
-    {bwd_dx_kernel<false, false, false, GBS, FP4>, bwd_dx_kernel<false, false, true, GBS, FP4>,                \
-     bwd_dx_kernel<false, true, false, GBS, FP4>,  bwd_dx_kernel<false, true, true, GBS, FP4>,                 \
-     bwd_dx_kernel<true, false, false, GBS, FP4>,  bwd_dx_kernel<true, false, true, GBS, FP4>,                 \
-     bwd_dx_kernel<true, true, false, GBS, FP4>,   bwd_dx_kernel<true, true, true, GBS, FP4>}
-    static const K_t kern[2][2][8] = {{NF4_BWD(false, false), NF4_BWD(true, false)},
-                                      {NF4_BWD(false, true), NF4_BWD(true, true)}};
+#define NF4_BWD(XB, DQ, FP4) {{bwd_dx_wide_kernel<XB, DQ, FP4, false, false>, bwd_dx_wide_kernel<XB, DQ, FP4, false, true>}, \
+                              {bwd_dx_wide_kernel<XB, DQ, FP4, true, false>, bwd_dx_wide_kernel<XB, DQ, FP4, true, true>}}
+    static const K_t kern[2][2][2][2][2] = {{{NF4_BWD(false, false, false), NF4_BWD(false, false, true)},
+                                             {NF4_BWD(false, true, false), NF4_BWD(false, true, true)}},
+                                            {{NF4_BWD(true, false, false), NF4_BWD(true, false, true)},
+                                             {NF4_BWD(true, true, false), NF4_BWD(true, true, true)}}};
 #undef NF4_BWD
-    const int sel = (dx_is_bf16 ? 4 : 0) | (src.dq ? 2 : 0) | (has_lr ? 1 : 0);
     const int tiles_m = (int)((M + TM - 1) / TM), tiles_k = (int)((K + TK - 1) / TK);
-    const dim3 g((unsigned)(tiles_m * tiles_k)), b(64 * NWAVE);
-    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs != 6][sel], g, b, 0, stream, dY, M, N, K, packed, src, lr, dx,
-                       tiles_m, tiles_k);
+    hipLaunchKernelGGL(kern[dx_is_bf16 ? 1 : 0][src.dq ? 1 : 0][src.qt ? 1 : 0][src.lbs == 5 ? 1 : 0][has_lr ? 1 : 0],
+                       dim3((unsigned)(tiles_m * tiles_k)), dim3(64 * NWAVE_W), 0, stream, dY, M, N, K, packed, src,
+                       lr, dx, tiles_m, tiles_k);
   } else {
     using namespace generic;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,

@@ -15,17 +15,12 @@
 //   fwd_small_kernel  M <= 16 otherwise, streaming-bound: one workgroup per 16
 //                     weight rows, its eight waves split K; every weight byte is
 //                     read once, all of a lane's loads are issued together.
-//   fwd_wide_kernel   M > 16, block size 64, no adapter term, K % 256 == 0:
-//                     256x256 output tiles, four waves of 64 weight rows (one
-//                     wave per SIMD), a lane dequantizing whole 64-blocks.
-//   fwd_large_kernel  M > 16 otherwise, matrix-core-bound: 256x256 output
-//                     tiles, eight waves; X staged through LDS (three stages,
-//                     filled by buffer-to-LDS loads), each wave dequantizes its
-//                     own 32 weight rows straight into MFMA operand registers
-//                     (no LDS round trip, no duplicate dequantization inside
-//                     the workgroup).
-#include <utility>
-
+//   fwd_wide_kernel   M > 16, matrix-core-bound: 256x256 output tiles, four
+//                     waves of 64 weight rows (one wave per SIMD), X staged
+//                     through LDS by buffer-to-LDS loads; a lane dequantizes
+//                     whole 64-element chunks of its weight rows straight into
+//                     MFMA operand registers (no LDS round trip, no duplicate
+//                     dequantization inside the workgroup).
 #include "nf4_launch.h"
 
 namespace nf4 {
@@ -468,28 +463,43 @@ __global__ __launch_bounds__(64 * kRowsWaves) void fwd_rows_kernel(
 
 // ----------------------------------------------------------------- large M
 //
-// Workgroup tile 256 (M) x 256 (N), eight waves, two per SIMD; wave w owns the
-// 32 output columns n0 + 32w .. +31 over all 256 rows: 8 MFMA 32x32x16 tiles
-// stacked along M, 128 accumulator registers.  Each wave dequantizes only its
-// own columns (the weight never passes through LDS, and no column is
-// dequantized twice in a workgroup); each dequantized B fragment feeds 8
-// MFMAs.  While one wave of a SIMD waits on a load issue or a barrier, the
-// other keeps the matrix core busy.
+// Workgroup tile 256 (M) x 256 (N), four waves, one per SIMD; wave w owns the
+// 64 output columns n0 + 64w .. +63 (two halves h of 32: weight rows
+// n0 + 64w + 32h + l%32) over all 256 rows: 8 x 2 MFMA 32x32x16 tiles, 256
+// fp32 accumulators per lane.  Each wave dequantizes only its own weight rows
+// (the weight never passes through LDS, no row is dequantized twice in a
+// workgroup); each dequantized B fragment feeds 8 MFMAs and each A fragment
+// read from LDS feeds two.
 //
-// K advances in steps of 64 (one quantization block): per step a lane holds
-// one 16-byte code chunk (32 codes) and one LUT.  Lane group kg = l/32 owns K
-// range 32kg .. 32kg+31 of the step and MFMA slice j (0..3) takes elements
-// 8j .. 8j+7 of it from both operands (A and B only have to agree on the K
-// index of each slot).
-//
-// X tiles (256 rows x 64 K, 32 KiB) reach LDS by buffer-to-LDS loads through
-// three stages: the tile two steps ahead loads during a whole step.  The
-// barrier that hands a tile over sits in the middle of the last slice, so the
-// slice's second half covers the next step's first A-fragment reads.
+// K advances in double steps of 128 in which lane group kg = l/32 owns the
+// 64-element chunk 2d + kg of both its weight rows: one table per 64 weights
+// and row (two at block size 32, whose blocks split the chunk).  MFMA slice j
+// (0..7) takes elements 8j .. 8j+7 of that chunk from both operands (A and B
+// only have to agree on the K index of each slot); the A fragment of lane
+// group kg comes from the X tile of its chunk, so a double step reads two
+// 64-K tiles at once: four LDS stages, one pair read while the other loads.
+// A double step is 64 groups of two MFMAs (group g of a slice: M-tile g
+// against both halves); the other work:
+//   A reads     after its MFMAs, group g refills a[g] for the next slice; the
+//               next double step's slice 0 after the hand-over
+//   B words     the next slice's fragments (word j+1 of both rows) in groups
+//               0-5 of slice j < 7; at block size 32 the tables of the
+//               chunk's second block in groups 6-7 of slice 2 (in place,
+//               after word 3); the next double step's tables once word 7 is
+//               done (slice 6 groups 6-7, slice 7 groups 0-1), then its word 0
+//               (slice 7 groups 2-7)
+//   X loads     the next double step's two tiles into the other pair of
+//               stages: groups 0, 2, ..., 30
+//   hand-over   before group 60: all loads and this wave's LDS reads complete,
+//               barrier, codes two double steps ahead (into the slot of this
+//               double step's own codes)
+// Double steps run in pairs (a loop body with a conditional second double step
+// spills); chunks past K -- the second half of a last double step when K / 64
+// is odd, a padding double step -- get zero weights.
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NWAVE = 8;
 constexpr int XROW = BK * 2;                 // 128-byte LDS rows
 constexpr int XTILE = BM * XROW;             // 32 KiB
+constexpr int NWAVE_W = 4;
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
 // takes a contiguous run of tiles, then walk tiles in groups of 4 M-tiles so
@@ -510,24 +520,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
   tn = in_group / gsize;
 }
 
-// A lane's weight state for one K-step: 32 codes and the block's absmax state.
-struct StepCodes {
-  uint4 w;
-  AbsmaxRaw r;
-};
-
 __device__ __forceinline__ void sched_cut() { __builtin_amdgcn_sched_barrier(0); }
-
-// f(std::integral_constant<int, i>{}) for i = 0 .. n-1, each a separate
-// instance: the index is a constant wherever f uses it, however large the body
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
 
 template <typename T>
 __device__ __forceinline__ const uint8_t *uniform_ptr(const T *p) {
@@ -535,12 +528,6 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const T *p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ void mfma2(f32x16 &c0, f32x16 &c1, const uint4 &a0, const uint4 &a1, const uint32_t b[4]) {
-  const bf16x8 bv = as_bf16x8(b);
-  c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bv, c0, 0, 0, 0);
-  c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bv, c1, 0, 0, 0);
 }
 
 // Entries 4q .. 4q+3 of the LUT of bf16(level_i * a^) (one quarter, so that
@@ -553,310 +540,18 @@ __device__ __forceinline__ void make_lut_quarter(float ahat, int q, Lut &t) {
   t.hi[q] = perm(p1, p0, 0x07050301u);
 }
 
-// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
-
-// Interleave a scheduling region as `n` repetitions of: one MFMA, `nds` LDS
-// reads, `nv` VALU instructions and, every `vm_every`-th time, one vector
-// memory load.  A few vector-ALU instructions after each MFMA overlap the
-// matrix core almost completely; a burst after one MFMA does not, even with
-// a second wave on the SIMD.
-template <int n, int nds, int nv, int vm_every>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < n; ++i) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    if (nds) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_VALU, nv, 0);
-    if (vm_every && i % (vm_every ? vm_every : 1) == 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
-  }
-}
-
-template <bool Y_BF16, bool DQ, bool LR, bool GBS, bool FP4>
-__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_large_kernel(
-    const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    AbsmaxSrc src, LowRank lr, void *__restrict__ Y, int tiles_m, int tiles_n) {
-  // separate arrays (not one indexed by stage) so that the compiler can tell
-  // the tile being read from the tiles being loaded
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[XTILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs1[XTILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs2[XTILE];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const float mu = DQ ? *src.mean : 0.f;
-  const int bl = lane & 31, kg = lane >> 5;
-
-  // B operand: this lane's weight row; a column past N loads row N-1 (its
-  // outputs are never stored).
-  const int64_t ncol = n0 + 32 * wave + bl;
-  const int64_t nc = ncol < N ? ncol : N - 1;
-  const uint8_t *wq = packed + nc * (K / 2) + kg * 16;
-  // block of step k: blk0 + k (block size 64), else the flat index of the lane's
-  // 32-element chunk shifted by log2(block size) -- a chunk never straddles a block
-  const int64_t blk0 = nc * (K / kBlock);
-  const int64_t flat0 = nc * K + 32 * kg;
-
-  // X tile loads, buffer-to-LDS: wave w's load i (0..3) fills LDS bytes
-  // (4w + i) * 1024 .. +1023, i.e. tile rows 8(4w + i) .. +7; lane l takes row
-  // 8(4w + i) + l/8 and physical 16-byte chunk l%8, which holds logical chunk
-  // (l%8) ^ ((row/2) & 7).  One buffer descriptor per wave and step, based at
-  // the wave's first row and sized to its rows that exist: lanes of rows past
-  // M fall outside it and load zeros.  Offsets and sizes are 32-bit (K < 2^24,
-  // checked by the API); the descriptor fields are made explicitly
-  // wave-uniform since a descriptor lives in SGPRs.
-  const int64_t wrow0 = m0 + 32 * wave;
-  const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 32 ? 32 : M - wrow0);
-  const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * K * 2));
-  const uint8_t *xwave = uniform_ptr(X + (wrows > 0 ? wrow0 : 0) * K);
-  uint32_t xvoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * i + (lane >> 3);                             // row within the wave's 32
-    xvoff[i] = (uint32_t)(r * K * 2) + ((uint32_t)((lane & 7) ^ ((r >> 1) & 7)) << 4);
-  }
-  // A fragments: lane l reads row 32i + l%32, logical chunk 4kg + j of slice j,
-  // stored at chunk (4kg + j) ^ ((row/2) & 7) (the row's low five bits are l%32).
-  int aoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) aoff[j] = bl * XROW + (((4 * kg + j) ^ ((bl >> 1) & 7)) << 4);
-
-  const int64_t nk = K / BK;
-  auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
-  auto xrsrc = [&](int64_t kt) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + clampk(kt) * (BK * 2)), (short)0,
-                                             wbytes, 0x00020000);
-  };
-  auto issue_x1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t *dst, int i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * wave + i) * 1024), 16, xvoff[i], 0, 0, 0);
-  };
-  auto issue_codes = [&](int64_t kt, StepCodes &c) {
-    const int64_t k = clampk(kt);
-    c.w = *reinterpret_cast<const uint4 *>(wq + k * (BK / 2));
-    c.r = load_raw<DQ>(src, GBS ? (flat0 + k * BK) >> src.lbs : blk0 + k);
-  };
-  auto ahat_at = [&](int64_t kt, const StepCodes &c) { return kt < nk ? ahat_of(c.r, DQ, mu) : 0.f; };
-
-  f32x16 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  uint4 a[8];      // A fragments; each is refilled for the next slice right after its MFMA issues
-  // B fragments rotate through three buffers: step k's slices 0..3 take
-  // p0, p1, p2, p0 with (p0, p1, p2) = (k, k+1, k+2) mod 3, and step k+1's
-  // first word goes to p1, so every word can be dequantized a slice or more
-  // ahead into a buffer no MFMA is reading.
-  uint32_t bb0[4], bb1[4], bb2[4];
-  uint4 cw;        // codes of the current step
-  Lut lut;         // LUT of the current step
-  // codes of the next two steps, in flight: step kt + 1 + i sits in slot
-  // (kt + 1 + i) % 3, so that with three steps per loop iteration every
-  // slot keeps its registers (a loop-carried copy would wait for the load)
-  StepCodes cs0, cs1, cs2;
-
-  // prologue: the codes of steps 0 and 1 and tiles 0 and 1; all complete
-  // before the barrier (the compiler may reorder these loads, so the wait
-  // counts none of them as outstanding)
-  {
-    StepCodes c0;
-    issue_codes(0, c0);
-    const __amdgpu_buffer_rsrc_t r0 = xrsrc(0), r1 = xrsrc(1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_x1(r0, xs0, i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) issue_x1(r1, xs1, i);
-    issue_codes(1, cs1);
-    cw = c0.w;
-    const float ah = ahat_at(0, c0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) make_lut_quarter<FP4>(ah, q, lut);
-    Sel4 sa, sb;
-    select8(cw.x, sa, sb);
-    lookup4(sa, lut, bb0[0], bb0[1]);
-    lookup4(sb, lut, bb0[2], bb0[3]);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
-  sched_cut();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(xs0 + aoff[0] + i * 32 * XROW);
-
-  // One K-step: four slices of 8 MFMAs (one per 32-row tile), each a
-  // scheduling region whose other work is interleaved evenly between its
-  // MFMAs (about four vector-ALU instructions each):
-  //   slice j < 3   A fragments of slice j+1 (each refilled right after its
-  //                 MFMA); one load of the tile two steps ahead into `ld`
-  //                 (free since the previous hand-over)
-  //   dequant       slice 0: word 1 and word 2's selectors; slice 1: word
-  //                 2's lookups and half of word 3; slice 2: the rest of word
-  //                 3, the next step's a^ and three quarters of its LUT (in
-  //                 place, after word 3's last lookup); slice 3: the last
-  //                 quarter and the next step's first word
-  //   hand-over     after four MFMAs of slice 3: this wave's LDS reads and
-  //                 the next tile's loads complete (only the four loads of the
-  //                 tile two steps ahead may be outstanding), the barrier, the
-  //                 codes two steps ahead; the slice's last four MFMAs cover
-  //                 the reads of the next step's slice-0 fragments from `nx`
-  auto step = [&](int64_t kt, uint8_t *rd, uint8_t *nx, uint8_t *ld, const StepCodes &cn, StepCodes &cfill,
-                  uint32_t *p0, uint32_t *p1, uint32_t *p2) {
-    Sel4 sa, sb, sc, sd;
-    const __amdgpu_buffer_rsrc_t rsl = xrsrc(kt + 2);
-    // slice 0
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
-      a[i] = *reinterpret_cast<const uint4 *>(rd + aoff[1] + i * 32 * XROW);
-    }
-    issue_x1(rsl, ld, 0);
-    select8(cw.y, sa, sb);
-    lookup4(sa, lut, p1[0], p1[1]);
-    lookup4(sb, lut, p1[2], p1[3]);
-    select8(cw.z, sc, sd);
-    interleave<8, 1, 5, 8>();
-    sched_cut();
-    // slice 1
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p1), acc[i], 0, 0, 0);
-      a[i] = *reinterpret_cast<const uint4 *>(rd + aoff[2] + i * 32 * XROW);
-    }
-    issue_x1(rsl, ld, 1);
-    lookup4(sc, lut, p2[0], p2[1]);
-    lookup4(sd, lut, p2[2], p2[3]);
-    select8(cw.w, sa, sb);
-    lookup4(sa, lut, p0[0], p0[1]);
-    interleave<8, 1, 5, 8>();
-    sched_cut();
-    // slice 2
-    const float ahn = ahat_at(kt + 1, cn);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p2), acc[i], 0, 0, 0);
-      a[i] = *reinterpret_cast<const uint4 *>(rd + aoff[3] + i * 32 * XROW);
-    }
-    issue_x1(rsl, ld, 2);
-    lookup4(sb, lut, p0[2], p0[3]);
-    make_lut_quarter<FP4>(ahn, 0, lut);
-    make_lut_quarter<FP4>(ahn, 1, lut);
-    make_lut_quarter<FP4>(ahn, 2, lut);
-    interleave<8, 1, 5, 8>();
-    sched_cut();
-    // slice 3, first half
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
-    issue_x1(rsl, ld, 3);
-    make_lut_quarter<FP4>(ahn, 3, lut);
-    cw = cn.w;
-    select8(cw.x, sa, sb);
-    interleave<4, 0, 5, 4>();
-    sched_cut();
-    // hand-over
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4) & ~(0xF << 8));   // vmcnt(4) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    sched_cut();
-    issue_codes(kt + 2, cfill);
-    sched_cut();
-    // slice 3, second half
-#pragma unroll
-    for (int i = 4; i < 8; ++i)
-      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(p0), acc[i], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * XROW);
-    lookup4(sa, lut, p1[0], p1[1]);
-    lookup4(sb, lut, p1[2], p1[3]);
-    interleave<4, 2, 4, 0>();
-    sched_cut();
-  };
-  // steps run in threes (one per LDS stage, code slot and B-buffer rotation); the last one or two after the loop
-  int64_t kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
-    step(kt, xs0, xs1, xs2, cs1, cs2, bb0, bb1, bb2);
-    step(kt + 1, xs1, xs2, xs0, cs2, cs0, bb1, bb2, bb0);
-    step(kt + 2, xs2, xs0, xs1, cs0, cs1, bb2, bb0, bb1);
-  }
-  if (kt < nk) step(kt, xs0, xs1, xs2, cs1, cs2, bb0, bb1, bb2);
-  if (kt + 1 < nk) step(kt + 1, xs1, xs2, xs0, cs2, cs0, bb1, bb2, bb0);
-  __builtin_amdgcn_s_waitcnt(0);
-  if (LR) add_lowrank_32x8(acc, lr, m0, M, nc, bl, kg, xs0);
-
-  // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
-  if (m0 + BM <= M && n0 + BN <= N && N < ((int64_t)1 << 27)) {
-    // a full tile: every store is a wave-uniform row address (scalar arithmetic) plus the
-    // lane's 32-bit byte offset (row 4kg, column l%32), with no per-store bounds test
-    constexpr int ES = Y_BF16 ? 2 : 4;
-    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)N + bl) * ES;
-    uint8_t *ycol = reinterpret_cast<uint8_t *>(Y) + (m0 * N + n0 + 32 * wave) * ES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        uint8_t *rowp = ycol + (int64_t)(32 * i + 8 * (r / 4) + (r % 4)) * N * ES;
-        if (Y_BF16)
-          *reinterpret_cast<uint16_t *>(rowp + voff) = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
-        else
-          *reinterpret_cast<float *>(rowp + voff) = acc[i][r];
-      }
-    }
-  } else if (ncol < N) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
-        if (row < M) {
-          const int64_t off = row * N + ncol;
-          if (Y_BF16)
-            reinterpret_cast<uint16_t *>(Y)[off] = (uint16_t)(pack_bf16x2(acc[i][r], 0.f) & 0xffffu);
-          else
-            reinterpret_cast<float *>(Y)[off] = acc[i][r];
-        }
-      }
-    }
-  }
-}
-
-// ----------------------------------------------------------------- large M, one wave per SIMD
-//
-// The forward with four waves, each owning 64 output columns (two halves h of
-// 32: weight rows n0 + 64w + 32h + l%32) over all 256 rows of the tile: 256
-// fp32 accumulators per lane, one wave per SIMD, each A fragment feeding two
-// MFMAs.  K advances in double steps of 128 in which lane group kg = l/32
-// owns 64-block 2d + kg of both its weight rows, so a lane builds one table per
-// 64 weights of a row (the eight-wave kernel above: per 32).  MFMA slice j
-// (0..7) takes elements 8j .. 8j+7 of that block from both operands; the A
-// fragment of lane group kg comes from the X tile of its block, so a double
-// step reads two 64-K tiles at once: four LDS stages, one pair read while the
-// other loads.  A double step is 64 groups of two MFMAs (group g of a slice:
-// M-tile g against both halves); the other work:
-//   A reads     after its MFMAs, group g refills a[g] for the next slice; the
-//               next double step's slice 0 after the hand-over
-//   B words     the next slice's fragments (word j+1 of both rows) in groups
-//               0-5 of slice j < 7; the next double step's two tables once
-//               word 7 is done (slice 6 groups 6-7, slice 7 groups 0-1, in
-//               place), then its word 0 (slice 7 groups 2-7)
-//   X loads     the next double step's two tiles into the other pair of
-//               stages: groups 0, 2, ..., 30
-//   hand-over   before group 60: all loads and this wave's LDS reads complete,
-//               barrier, codes two double steps ahead (into the slot of this
-//               double step's own codes)
-// Used for block size 64 without an adapter term, K a multiple of 256 (double
-// steps in pairs: a loop body with a conditional second double step spills).
-constexpr int NWAVE_W = 4;
-
+// A lane's weight state for one double step: the codes of its chunk of both
+// rows and the absmax state of the chunk's block (blocks, at size 32).
+template <bool BS32>
 struct DoubleCodes {
-  uint4 w[2][2];    // [row half][16-byte piece]: the 64 codes of each row's block
-  AbsmaxRaw r[2];   // the two blocks' absmax state
+  uint4 w[2][2];             // [row half][16-byte piece]: the 64 codes of each row's chunk
+  ChunkAbsmax<BS32> r[2];
 };
 
-template <bool Y_BF16, bool DQ, bool FP4>
+template <bool Y_BF16, bool DQ, bool FP4, bool BS32, bool LR>
 __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_wide_kernel(
     const uint16_t *__restrict__ X, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    AbsmaxSrc src, void *__restrict__ Y, int tiles_m, int tiles_n) {
+    AbsmaxSrc src, LowRank lr, void *__restrict__ Y, int tiles_m, int tiles_n) {
   // two pairs of stages (tile 2d, then tile 2d + 1), one array per pair so
   // that the compiler can tell the pair being read from the pair being loaded
   // (a pointer chosen per lane between two arrays would make every LDS read
@@ -870,21 +565,30 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const float mu = DQ ? *src.mean : 0.f;
   const int bl = lane & 31, kg = lane >> 5;
+  const int64_t nb64 = K / BK;                          // 64-element chunks per row (K % 64 == 0)
+  const int64_t nd = (nb64 + 1) / 2;                    // double steps
+  const int64_t ndp = (nd + 1) & ~(int64_t)1;           // run in pairs
 
   // B operands: this lane's two weight rows; a column past N loads row N-1
   // (its outputs are never stored)
-  const uint8_t *wq[2];
-  int64_t blk0[2], ncol[2];
+  const uint8_t *wrow[2];
+  int64_t flat0[2], ncol[2], nclamp[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     ncol[h] = n0 + 64 * wave + 32 * h + bl;
-    const int64_t nc = ncol[h] < N ? ncol[h] : N - 1;
-    wq[h] = packed + nc * (K / 2) + kg * 32;   // block kg of each double step
-    blk0[h] = nc * (K / kBlock) + kg;
+    nclamp[h] = ncol[h] < N ? ncol[h] : N - 1;
+    wrow[h] = packed + nclamp[h] * (K / 2);
+    flat0[h] = nclamp[h] * K;   // flat index of the row's first element: blocks may span rows
   }
 
   // X tile loads: a 64-K tile is 256 rows x 128 bytes; wave w's load i (0..7)
-  // covers tile rows 8(8w + i) .. +7, swizzled and bounded as in the kernel above
+  // fills LDS bytes (8w + i) * 1024 .. +1023, i.e. tile rows 8(8w + i) .. +7;
+  // lane l takes row 8(8w + i) + l/8 and physical 16-byte chunk l%8, which
+  // holds logical chunk (l%8) ^ ((row/2) & 7).  One buffer descriptor per wave
+  // and tile, based at the wave's first row and sized to its rows that exist:
+  // lanes of rows past M fall outside it and load zeros.  Offsets and sizes
+  // are 32-bit (K < 2^24); the descriptor fields are made explicitly
+  // wave-uniform since a descriptor lives in SGPRs.
   const int64_t wrow0 = m0 + 64 * wave;
   const int64_t wrows = M - wrow0 < 0 ? 0 : (M - wrow0 > 64 ? 64 : M - wrow0);
   const int wbytes = __builtin_amdgcn_readfirstlane((int)(uint32_t)(wrows * K * 2));
@@ -895,33 +599,35 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
     const int r = 8 * i + (lane >> 3);
     xvoff[i] = (uint32_t)(r * K * 2) + ((uint32_t)((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
-  // A fragments: lane l reads row 32i + l%32 of the tile of its block, logical
+  // A fragments: lane l reads row 32i + l%32 of the tile of its chunk, logical
   // chunk j of slice j, stored at chunk j ^ ((row/2) & 7)
   int aoff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) aoff[j] = bl * XROW + ((j ^ ((bl >> 1) & 7)) << 4);
 
-  const int64_t nd = K / (2 * BK);
-  auto clampd = [&](int64_t d) { return d < nd ? d : nd - 1; };
-  auto xrsrc = [&](int64_t t) {   // the 64-K tile t
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + t * (BK * 2)), (short)0, wbytes,
+  auto xrsrc = [&](int64_t t) {   // the 64-K tile t; past K the last tile again (its weights are zero)
+    const int64_t tc = t < nb64 ? t : nb64 - 1;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xwave + tc * (BK * 2)), (short)0, wbytes,
                                              0x00020000);
   };
   auto issue_x1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t *dst, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (8 * wave + i) * 1024), 16, xvoff[i], 0, 0, 0);
   };
-  auto issue_codes = [&](int64_t d, DoubleCodes &c) {
-    const int64_t dc = clampd(d);
+  auto issue_codes = [&](int64_t d, DoubleCodes<BS32> &c) {
+    const int64_t j0 = 2 * d + kg;
+    const int64_t j = j0 < nb64 ? j0 : nb64 - 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(wq[h] + dc * BK);
+      const uint4 *p = reinterpret_cast<const uint4 *>(wrow[h] + j * (BK / 2));
       c.w[h][0] = p[0];
       c.w[h][1] = p[1];
-      c.r[h] = load_raw<DQ>(src, blk0[h] + 2 * dc);
+      c.r[h].template load<DQ>(src, (flat0[h] + j * BK) >> src.lbs);
     }
   };
-  auto ahat_at = [&](int64_t d, const DoubleCodes &c, int h) { return d < nd ? ahat_of(c.r[h], DQ, mu) : 0.f; };
-  auto word = [&](const DoubleCodes &c, int h, int j) {
+  auto ahat_at = [&](int64_t d, const DoubleCodes<BS32> &c, int h, int u) {
+    return 2 * d + kg < nb64 ? c.r[h].ahat(u, DQ, mu) : 0.f;
+  };
+  auto word = [&](const DoubleCodes<BS32> &c, int h, int j) {
     const uint4 &w = c.w[h][j >> 2];
     return (j & 3) == 0 ? w.x : ((j & 3) == 1 ? w.y : ((j & 3) == 2 ? w.z : w.w));
   };
@@ -937,7 +643,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   uint4 a[8];
   uint32_t B0[2][4], B1[2][4];   // B fragments [row half] of the current and the next slice
   Lut lut[2];
-  DoubleCodes cs0, cs1;          // double step d's codes sit in slot d % 2
+  DoubleCodes<BS32> cs0, cs1;      // double step d's codes sit in slot d % 2
 
   // prologue: codes of double steps 0 and 1, the tiles of double step 0; its
   // tables and slice-0 fragments
@@ -952,7 +658,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   issue_codes(1, cs1);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const float ah = ahat_at(0, cs0, h);
+    const float ah = ahat_at(0, cs0, h, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) make_lut_quarter<FP4>(ah, q, lut[h]);
     Sel4 sa, sb;
@@ -970,19 +676,18 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   }
 
   // rdp: the pair read (tiles 2d, 2d+1); ldp: the pair loaded (2d+2, 2d+3)
-  auto dstep = [&](int64_t d, uint8_t *rdp, uint8_t *ldp, DoubleCodes &cc, const DoubleCodes &cn) {
+  auto dstep = [&](int64_t d, uint8_t *rdp, uint8_t *ldp, DoubleCodes<BS32> &cc, const DoubleCodes<BS32> &cn) {
     Sel4 sa[2], sb[2];
     float ahn[2] = {0.f, 0.f};
     const uint8_t *rd = rdp + kg * XTILE;
     const uint8_t *nx = ldp + kg * XTILE;
-    const int64_t t1 = 2 * clampd(d + 1);
-    const __amdgpu_buffer_rsrc_t rl0 = xrsrc(t1), rl1 = xrsrc(t1 + 1);
+    const __amdgpu_buffer_rsrc_t rl0 = xrsrc(2 * d + 2), rl1 = xrsrc(2 * d + 3);
     static_for<64>([&](auto rc) {
       constexpr int r = decltype(rc)::value;
       constexpr int slice = r / 8, g = r % 8;
       uint32_t(*bc)[4] = (slice & 1) ? B1 : B0;
       uint32_t(*bn)[4] = (slice & 1) ? B0 : B1;
-      if (r == 60) {
+      if constexpr (r == 60) {
         __builtin_amdgcn_s_waitcnt(0);   // the next tiles landed, this wave's LDS reads done
         __builtin_amdgcn_s_barrier();
         sched_cut();
@@ -992,51 +697,60 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         acc[g][h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[g]), as_bf16x8(bc[h]), acc[g][h], 0, 0, 0);
-      if (slice < 7) {
+      if constexpr (slice < 7) {
         a[g] = *reinterpret_cast<const uint4 *>(rd + aoff[slice + 1] + g * 32 * XROW);
-      } else if (r >= 60) {
+      } else if constexpr (r >= 60) {
         // the next double step's slice-0 fragments: a[i] after the hand-over and
         // after its last MFMA here (group 56 + i)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if ((56 + i > 60 ? 56 + i : 60) == r) a[i] = *reinterpret_cast<const uint4 *>(nx + aoff[0] + i * 32 * XROW);
       }
-      if (r % 2 == 0 && r <= 30) {
-        const int piece = r / 2;   // 0..7 tile 2d+2, 8..15 tile 2d+3
-        if (piece < 8)
+      if constexpr (r % 2 == 0 && r <= 30) {
+        constexpr int piece = r / 2;   // 0..7 tile 2d+2, 8..15 tile 2d+3
+        if constexpr (piece < 8)
           issue_x1(rl0, ldp, piece);
         else
           issue_x1(rl1, ldp + XTILE, piece - 8);
       }
       // B words: word slice+1 of both rows for the next slice
-      if (slice < 7 && g < 6) {
-        const int h = g / 3, ph = g % 3;
-        if (ph == 0) select8(word(cc, h, slice + 1), sa[h], sb[h]);
-        if (ph == 1) lookup4(sa[h], lut[h], bn[h][0], bn[h][1]);
-        if (ph == 2) lookup4(sb[h], lut[h], bn[h][2], bn[h][3]);
+      if constexpr (slice < 7 && g < 6) {
+        constexpr int h = g / 3, ph = g % 3;
+        if constexpr (ph == 0) select8(word(cc, h, slice + 1), sa[h], sb[h]);
+        if constexpr (ph == 1) lookup4(sa[h], lut[h], bn[h][0], bn[h][1]);
+        if constexpr (ph == 2) lookup4(sb[h], lut[h], bn[h][2], bn[h][3]);
+      }
+      // block size 32: words 4-7 belong to the chunk's second block
+      if constexpr (BS32 && slice == 2 && g >= 6) {
+        constexpr int h = g - 6;
+        const float ab = ahat_at(d, cc, h, 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) make_lut_quarter<FP4>(ab, q, lut[h]);
       }
       // the next double step's tables (word 7's lookups are done in group 53)
-      if (r >= 54 && r <= 57) {
-        const int h = (r - 54) >> 1, q0 = 2 * ((r - 54) & 1);
-        if (q0 == 0) ahn[h] = ahat_at(d + 1, cn, h);
+      if constexpr (r >= 54 && r <= 57) {
+        constexpr int h = (r - 54) >> 1, q0 = 2 * ((r - 54) & 1);
+        if constexpr (q0 == 0) ahn[h] = ahat_at(d + 1, cn, h, 0);
         make_lut_quarter<FP4>(ahn[h], q0, lut[h]);
         make_lut_quarter<FP4>(ahn[h], q0 + 1, lut[h]);
       }
       // and its word 0
-      if (r >= 58) {
-        const int q = r - 58, h = q / 3, ph = q % 3;
-        if (ph == 0) select8(word(cn, h, 0), sa[h], sb[h]);
-        if (ph == 1) lookup4(sa[h], lut[h], bn[h][0], bn[h][1]);
-        if (ph == 2) lookup4(sb[h], lut[h], bn[h][2], bn[h][3]);
+      if constexpr (r >= 58) {
+        constexpr int q = r - 58, h = q / 3, ph = q % 3;
+        if constexpr (ph == 0) select8(word(cn, h, 0), sa[h], sb[h]);
+        if constexpr (ph == 1) lookup4(sa[h], lut[h], bn[h][0], bn[h][1]);
+        if constexpr (ph == 2) lookup4(sb[h], lut[h], bn[h][2], bn[h][3]);
       }
       sched_cut();
     });
   };
-  for (int64_t d = 0; d < nd; d += 2) {
+  for (int64_t d = 0; d < ndp; d += 2) {
     dstep(d, xp0, xp1, cs0, cs1);
     dstep(d + 1, xp1, xp0, cs1, cs0);
   }
   __builtin_amdgcn_s_waitcnt(0);
+  // the adapter term: ranks in chunks of 112 (256 staged rows of 240 bytes in the first pair of stages)
+  if (LR) add_lowrank_wide<112>(acc, lr, m0, M, nclamp, bl, kg, xp0);
 
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   if (m0 + BM <= M && n0 + BN <= N && N < ((int64_t)1 << 27)) {
@@ -1125,31 +839,21 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
     else
       hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs == 5][sel], g, b, 0, stream, X, (int)M, N, K, packed, src, lr,
                          y);
-  } else if (src.lbs == 6 && lr.r == 0 && K % (4 * BK) == 0) {
-    // block size 64, no adapter term, K a multiple of 256: one wave per SIMD, 64 columns per wave
-    using W_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, void *, int, int);
-    static const W_t kern[2][2][2] = {{{fwd_wide_kernel<false, false, false>, fwd_wide_kernel<false, false, true>},
-                                       {fwd_wide_kernel<false, true, false>, fwd_wide_kernel<false, true, true>}},
-                                      {{fwd_wide_kernel<true, false, false>, fwd_wide_kernel<true, false, true>},
-                                       {fwd_wide_kernel<true, true, false>, fwd_wide_kernel<true, true, true>}}};
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    hipLaunchKernelGGL(kern[y_is_bf16 ? 1 : 0][src.dq ? 1 : 0][src.qt ? 1 : 0], dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(64 * NWAVE_W), 0, stream, X, M, N, K, packed, src, y, tiles_m, tiles_n);
   } else {
-    using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,
-                         int, int);
-#define NF4_LARGE(GBS, FP4)                                                                                   \
-    {fwd_large_kernel<false, false, false, GBS, FP4>, fwd_large_kernel<false, false, true, GBS, FP4>,          \
-     fwd_large_kernel<false, true, false, GBS, FP4>,  fwd_large_kernel<false, true, true, GBS, FP4>,           \
-     fwd_large_kernel<true, false, false, GBS, FP4>,  fwd_large_kernel<true, false, true, GBS, FP4>,           \
-     fwd_large_kernel<true, true, false, GBS, FP4>,   fwd_large_kernel<true, true, true, GBS, FP4>}
-    static const K_t kern[2][2][8] = {{NF4_LARGE(false, false), NF4_LARGE(true, false)},
-                                      {NF4_LARGE(false, true), NF4_LARGE(true, true)}};
-#undef NF4_LARGE
+    // M > 16: 256x256 tiles, one wave per SIMD
+    using W_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *, int,
+                         int);
+#define NF4_WIDE(YB, DQ, FP4) {{fwd_wide_kernel<YB, DQ, FP4, false, false>, fwd_wide_kernel<YB, DQ, FP4, false, true>}, \
+                               {fwd_wide_kernel<YB, DQ, FP4, true, false>, fwd_wide_kernel<YB, DQ, FP4, true, true>}}
+    static const W_t kern[2][2][2][2][2] = {{{NF4_WIDE(false, false, false), NF4_WIDE(false, false, true)},
+                                             {NF4_WIDE(false, true, false), NF4_WIDE(false, true, true)}},
+                                            {{NF4_WIDE(true, false, false), NF4_WIDE(true, false, true)},
+                                             {NF4_WIDE(true, true, false), NF4_WIDE(true, true, true)}}};
+#undef NF4_WIDE
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const dim3 g((unsigned)(tiles_m * tiles_n)), b(64 * NWAVE);
-    hipLaunchKernelGGL(kern[src.qt ? 1 : 0][src.lbs != 6][sel], g, b, 0, stream, X, M, N, K, packed, src, lr, y,
-                       tiles_m, tiles_n);
+    hipLaunchKernelGGL(kern[y_is_bf16 ? 1 : 0][src.dq ? 1 : 0][src.qt ? 1 : 0][src.lbs == 5 ? 1 : 0][lr.r > 0 ? 1 : 0],
+                       dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * NWAVE_W), 0, stream, X, M, N, K, packed, src, lr,
+                       y, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }

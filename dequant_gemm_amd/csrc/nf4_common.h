@@ -13,7 +13,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace nf4 {
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. n-1, each a separate
+// instance: the index is a constant wherever f uses it, however large the body
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -154,6 +168,57 @@ __device__ __forceinline__ float ahat_of(const AbsmaxRaw &r, int dq, float mu) {
   return dq ? __fadd_rn(__fmul_rn((float)r.q, r.v), mu) : r.v;
 }
 
+// The state of two adjacent blocks 2i and 2i+1 (one 64-element chunk at block
+// size 32), loaded as one access: the two int8 absmax values as 16 bits (the
+// pair never straddles a group of 256, so one scale serves both) or the two
+// fp32 absmax values as 8 bytes.  Kept packed until used: unpacking right
+// after the load would wait for it there.
+struct AbsmaxRaw2 {
+  float v0, v1;   // fp32 absmax values (no double quantization), or the group scale in v0
+  uint32_t q2;    // the two int8 absmax values, block 2i in the low byte
+};
+
+template <bool DQ>
+__device__ __forceinline__ AbsmaxRaw2 load_raw2(const AbsmaxSrc &s, int64_t blk) {   // blk even
+  AbsmaxRaw2 r;
+  if (DQ) {
+    r.q2 = *reinterpret_cast<const uint16_t *>(s.q + blk);
+    r.v0 = s.scale[blk >> 8];
+    r.v1 = r.v0;
+  } else {
+    const float2 a = *reinterpret_cast<const float2 *>(s.absmax + blk);
+    r.v0 = a.x;
+    r.v1 = a.y;
+    r.q2 = 0;
+  }
+  return r;
+}
+
+// a^ of block 2i + u
+__device__ __forceinline__ float ahat2_of(const AbsmaxRaw2 &r, int u, int dq, float mu) {
+  if (!dq) return u ? r.v1 : r.v0;
+  const int q = (int)(int8_t)(uint8_t)(u ? (r.q2 >> 8) : r.q2);
+  return __fadd_rn(__fmul_rn((float)q, r.v0), mu);
+}
+
+// The per-chunk absmax state of a 64-element chunk: one block, or two at size 32.
+template <bool BS32>
+struct ChunkAbsmax;
+template <>
+struct ChunkAbsmax<false> {
+  AbsmaxRaw r;
+  template <bool DQ>
+  __device__ __forceinline__ void load(const AbsmaxSrc &s, int64_t blk) { r = load_raw<DQ>(s, blk); }
+  __device__ __forceinline__ float ahat(int, int dq, float mu) const { return ahat_of(r, dq, mu); }
+};
+template <>
+struct ChunkAbsmax<true> {
+  AbsmaxRaw2 r;
+  template <bool DQ>
+  __device__ __forceinline__ void load(const AbsmaxSrc &s, int64_t blk) { r = load_raw2<DQ>(s, blk); }
+  __device__ __forceinline__ float ahat(int u, int dq, float mu) const { return ahat2_of(r, u, dq, mu); }
+};
+
 // ------------------------------------------------------------------ low-rank adapter term
 //
 // "bitsandbytes" page, 4-bit/LoRA paragraph: a frozen 4-bit base weight with
@@ -168,57 +233,65 @@ struct LowRank {
   int r;
 };
 
-// For the 32x32x16 kernels with eight waves (512 threads), each owning 32 output columns of
-// the workgroup's 256 rows: adds U V^T to a wave's 8 stacked 32-row tiles of
-// the columns starting at col0 (lane l: row l%32 of each tile and column
-// col0 + l%32; lane group kg = l/32 takes ranks 16s + 8kg .. +7 of slice s
-// from both operands).  Every wave needs the same 256 rows of U, so the
-// workgroup stages them in LDS (`buf`, 32 KiB that no wave still reads), a
-// chunk of kLrChunk ranks at a time; each wave reads its 32 rows of V from
-// memory.  Rows past M read row M-1 and the column must already be clamped to
-// an existing one: those outputs are never stored.  All waves of the
-// workgroup must call this together (it synchronises them).
-constexpr int kLrChunk = 48;                      // ranks per LDS chunk
-constexpr int kLrRow = 2 * kLrChunk + 16;         // bytes per staged row (16 of padding against bank conflicts)
-
-__device__ __forceinline__ void add_lowrank_32x8(f32x16 acc[8], const LowRank &lr, int64_t m0, int64_t M,
-                                                 int64_t col, int bl, int kg, uint8_t *buf) {
-  static_assert(256 * kLrRow <= 32768, "staged U chunk exceeds the LDS buffer");
-  const uint16_t *vrow = lr.v + col * lr.r + 8 * kg;
-  for (int r0 = 0; r0 < lr.r; r0 += kLrChunk) {
-    const int rc = lr.r - r0 < kLrChunk ? lr.r - r0 : kLrChunk;   // a multiple of 16
-    const int cpr = rc / 8;                                        // 16-byte chunks per row
-    __syncthreads();                                               // the buffer is free
-    {
-      // 256 * cpr <= 1536 chunks over the 512 threads: all loads, then all stores
-      constexpr int kPer = 256 * (kLrChunk / 8) / 512;
-      uint4 v[kPer];
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int c = threadIdx.x + 512 * k;
-        const int row = c / cpr, ch = c - row * cpr;
-        const int64_t grow = m0 + row < M ? m0 + row : M - 1;
-        if (c < 256 * cpr) v[k] = *reinterpret_cast<const uint4 *>(lr.u + grow * lr.r + r0 + 8 * ch);
+// For the 32x32x16 kernels with four waves (256 threads), each owning 64
+// output columns as two halves of 32 over the workgroup's 256 rows: adds U V^T
+// to a wave's 8 x 2 tiles, half h at the columns col[h] (lane l: row l%32 of
+// each 32-row tile, column col[h] of half h; lane group kg = l/32 takes ranks
+// 16s + 8kg .. +7 of slice s from both operands).  Every wave needs the same
+// 256 rows of U, so the workgroup stages them in LDS (`buf`, 256 rows of
+// 2 CH + 16 bytes that no wave still reads), a chunk of CH ranks (a multiple
+// of 16) at a time; each A fragment read from it feeds both halves.  The V
+// fragments of a whole chunk are loaded before its U rows are staged, so that
+// their latencies overlap.  Rows past M read row M-1 and the columns must
+// already be clamped to existing ones: those outputs are never stored.  All
+// waves of the workgroup must call this together (it synchronises them).
+template <int CH>
+__device__ __forceinline__ void add_lowrank_wide(f32x16 acc[8][2], const LowRank &lr, int64_t m0, int64_t M,
+                                                 const int64_t col[2], int bl, int kg, uint8_t *buf) {
+  static_assert(CH % 16 == 0, "chunks of whole MFMA slices");
+  constexpr int ROW = 2 * CH + 16;   // bytes per staged row (16 of padding against bank conflicts)
+  const uint16_t *vrow0 = lr.v + col[0] * lr.r + 8 * kg;
+  const uint16_t *vrow1 = lr.v + col[1] * lr.r + 8 * kg;
+  for (int r0 = 0; r0 < lr.r; r0 += CH) {
+    const int rc = lr.r - r0 < CH ? lr.r - r0 : CH;   // a multiple of 16
+    const int cpr = rc / 8;                            // 16-byte chunks per row
+    uint4 bv0[CH / 16], bv1[CH / 16];
+    static_for<CH / 16>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if (16 * s < rc) {
+        bv0[s] = *reinterpret_cast<const uint4 *>(vrow0 + r0 + 16 * s);
+        bv1[s] = *reinterpret_cast<const uint4 *>(vrow1 + r0 + 16 * s);
       }
+    });
+    __syncthreads();   // the buffer is free
+    // U rows into the buffer (global and LDS accesses never alias: the loads
+    // need not wait for the stores)
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int c = threadIdx.x + 512 * k;
-        const int row = c / cpr, ch = c - row * cpr;
-        if (c < 256 * cpr) *reinterpret_cast<uint4 *>(buf + row * kLrRow + 16 * ch) = v[k];
-      }
+    for (int k = 0; k < CH / 8; ++k) {
+      const int c = threadIdx.x + 256 * k;
+      const int row = c / cpr, ch = c - row * cpr;
+      const int64_t grow = m0 + row < M ? m0 + row : M - 1;
+      if (c < 256 * cpr)
+        *reinterpret_cast<uint4 *>(buf + row * ROW + 16 * ch) =
+            *reinterpret_cast<const uint4 *>(lr.u + grow * lr.r + r0 + 8 * ch);
     }
     __syncthreads();
-    for (int s = 0; s < rc / 16; ++s) {
-      const uint4 bv = *reinterpret_cast<const uint4 *>(vrow + r0 + 16 * s);
-      uint4 av[8];
+    static_for<CH / 16>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if (16 * s < rc) {
+        uint4 av[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        av[i] = *reinterpret_cast<const uint4 *>(buf + (32 * i + bl) * kLrRow + 16 * (2 * s + kg));
+        for (int i = 0; i < 8; ++i)
+          av[i] = *reinterpret_cast<const uint4 *>(buf + (32 * i + bl) * ROW + 16 * (2 * s + kg));
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
-                                                         __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
-    }
+        for (int i = 0; i < 8; ++i) {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                              __builtin_bit_cast(bf16x8, bv0[s]), acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                              __builtin_bit_cast(bf16x8, bv1[s]), acc[i][1], 0, 0, 0);
+        }
+      }
+    });
   }
 }
 

@@ -121,9 +121,25 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t m, const 
 //   magnitude index(|n|) = base_j + (|n| > thr_j)
 // (strictly above: a tie goes to the smaller magnitude, the lower code).  The
 // sign is applied after; zero of either sign takes code 0 (+0).
+//
+// The comparison itself needs no quotient.  For q = |x| / a and an fp32
+// threshold t, fl(q) > t exactly when q lies above the midpoint tm between t
+// and the next float (or on it, when t's significand is odd: the tie rounds to
+// the even neighbour).  With tm2 = tm (t even) or a double just below tm (t
+// odd: no fp32 |x| lies between a * tm2 and a * tm), the decision is
+// fma(-a, tm2, |x|) > 0 in fp64: the fused product-difference is rounded
+// once, which keeps its sign exact.  Bit-exact ratios such as 5/24 = 160/768
+// are common among bf16 weights and land on thresholds; this decides them
+// without the IEEE division.
 constexpr int kFp4Cells = 25;
 
-__device__ void build_cells_fp4(Cell *tab) {
+struct Fp4Cell {
+  double tm2;   // decision point (+inf if the cell holds no threshold)
+  float thr;    // the threshold itself, for exact quotients
+  int base;     // magnitude index of the cell's lower edge
+};
+
+__device__ void build_cells_fp4(Fp4Cell *tab) {
   for (int j = threadIdx.x; j < kFp4Cells; j += blockDim.x) {
     const float lo = ((float)j - 0.5f) * (1.0f / 24.0f);
     const float hi = ((float)j + 0.5f) * (1.0f / 24.0f);
@@ -137,51 +153,54 @@ __device__ void build_cells_fp4(Cell *tab) {
       else if (t < hi)
         thr = t;
     }
-    Cell c;
+    Fp4Cell c;
     c.thr = thr;
     c.base = base;
+    c.tm2 = __builtin_inf();
+    if (thr != __builtin_inff()) {
+      const uint32_t tb = __float_as_uint(thr);
+      const double tm = 0.5 * ((double)thr + (double)__uint_as_float(tb + 1u));   // exact in fp64
+      c.tm2 = (tb & 1u) ? tm * (1.0 - 0x1p-40) : tm;
+    }
     tab[j] = c;
   }
 }
 
-__device__ __forceinline__ int classify_fp4(float n, const Cell *tab, bool &near) {
+// Magnitude-and-sign code of an exact quotient n.
+__device__ __forceinline__ int classify_fp4(float n, const Fp4Cell *tab) {
   const float an = fabsf(n);
   int j = (int)(an * 24.0f + 0.5f);
   j = j > kFp4Cells - 1 ? kFp4Cells - 1 : j;
-  const Cell c = tab[j];
-  near = near_thr(an, c.thr);
+  const Fp4Cell c = tab[j];
   const int mi = c.base + (an > c.thr ? 1 : 0);
   return (n < 0.f && mi > 0) ? 8 + mi : mi;
 }
 
 // FP4 codes of eight values of one block with absmax bits `m` (finite,
-// non-zero): one reciprocal per block (n' within 2^-22 relative of the exact
-// quotient); each value within 2^-20 relative of its cell's threshold, and
-// every value of a block whose reciprocal is not a normal float, is redone
-// with the IEEE division.  (With bf16 weights the quotient lands exactly on
-// the threshold 1/8 for a few elements in a thousand, so the redo is per
-// element.)
-__device__ __forceinline__ uint32_t encode8_fp4(const float x[8], uint32_t m, const Cell *cells) {
+// non-zero).  One reciprocal per block locates each value's cell (n' within
+// 2^-22 relative of the quotient: the cell may be the neighbour of the exact
+// one only near a cell edge, where both give the same index); the threshold
+// decision is the exact fp64 test above.  A block whose reciprocal is not a
+// normal float takes the IEEE division.
+__device__ __forceinline__ uint32_t encode8_fp4(const float x[8], uint32_t m, const Fp4Cell *cells) {
   const float a = __uint_as_float(m);
+  const bool fast = m >= 0x01000000u && m < 0x7e000000u;   // 2^-125 <= a < 2^125
   int code[8];
-  bool near[8];
-  const bool fast = m >= 0x01000000u && m < 0x7e000000u;
-  const float r = __builtin_amdgcn_rcpf(a);
-  bool any = false;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    code[i] = classify_fp4(x[i] * r, cells, near[i]);
-    near[i] = near[i] || !fast;
-    any = any || near[i];
-  }
-  if (any) {                // rare: one branch around the per-element redo
+  if (fast) {
+    const float r = __builtin_amdgcn_rcpf(a);
+    const double na = -(double)a;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (near[i]) {
-        bool unused;
-        code[i] = classify_fp4(x[i] / a, cells, unused);
-      }
+      const float ax = fabsf(x[i]);
+      int j = (int)(ax * r * 24.0f + 0.5f);
+      j = j > kFp4Cells - 1 ? kFp4Cells - 1 : j;
+      const Fp4Cell c = cells[j];
+      const int mi = c.base + (__fma_rn(na, c.tm2, (double)ax) > 0.0 ? 1 : 0);
+      code[i] = (x[i] < 0.f && mi > 0) ? 8 + mi : mi;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = classify_fp4(x[i] / a, cells);
   }
   uint32_t word = 0;
 #pragma unroll
@@ -212,7 +231,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_blocks_kernel(
   constexpr int BS = 8 * LPB;        // weights per block
   constexpr int BPI = kQuantThreads / LPB;     // blocks per workgroup and iteration
   constexpr int kWaves = kQuantThreads / 64;
-  __shared__ Cell cells[129];
+  __shared__ __attribute__((aligned(16))) uint8_t celltab[129 * sizeof(Cell)];   // NF4: 129 Cells, FP4: 25 Fp4Cells
+  static_assert(kFp4Cells * sizeof(Fp4Cell) <= sizeof(celltab), "FP4 cell table exceeds its buffer");
+  Cell *cells = reinterpret_cast<Cell *>(celltab);
+  Fp4Cell *cells4 = reinterpret_cast<Fp4Cell *>(celltab);
   __shared__ unsigned long long lbuck[256];
   __shared__ unsigned long long lslot[kMeanSlots];
   __shared__ uint32_t wmax[kWaves];
@@ -238,7 +260,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_blocks_kernel(
   uint4 cu = make_uint4(0, 0, 0, 0), cv = cu;
   if (blk < nfull) load(blk, cu, cv);   // in flight while the level table is built
   if (FP4)
-    build_cells_fp4(cells);
+    build_cells_fp4(cells4);
   else
     build_cells(cells);
   if (DQ) {
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_blocks_kernel(
     } else if (m == 0) {
       word = kZeroWord;  // all-zero block
     } else {
-      word = FP4 ? encode8_fp4(x, m, cells) : encode8(x, m, cells);
+      word = FP4 ? encode8_fp4(x, m, cells4) : encode8(x, m, cells);
     }
     *reinterpret_cast<uint32_t *>(packed + blk * (BS / 2) + part * 4) = word;
     if (part == 0) {
@@ -326,7 +348,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_blocks_kernel(
     if (m != 0 && m < 0x7f800000u) {
       bool unused = false;
       const float n = x / __uint_as_float(m);
-      code = FP4 ? classify_fp4(n, cells, unused) : classify(n, cells, unused);
+      code = FP4 ? classify_fp4(n, cells4) : classify(n, cells, unused);
     }
     if (!valid) code = 0;
     const int upper = __shfl_down(code, 1);
