@@ -40,6 +40,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // wave's loads are issued before any of its arithmetic.
 
 constexpr int kSmallCols = 16;
+constexpr int kSmallRows = 16;     // X rows per grid row (the MFMA's 16 A rows)
+// Above 16 rows the launcher keeps this kernel (one grid row per 16 rows, each
+// dequantizing the whole weight again) while (grid rows) x N is at most
+// kSmallChunkBudget.  Its time grows with the grid rows (about N K / 3e12 s
+// each, the dequantization's VALU rate), while the 256x256 kernel below 256
+// rows takes one round of tiles, about K x 20 ns, on a mostly idle chip;
+// measured crossovers: 14 grid rows at N = 4096, 4-5 at 11008, 2 at 28672.
+constexpr int64_t kSmallChunkBudget = 14 * 4096;
 constexpr int kSmallWaves = 8;
 constexpr int kNonTemporal = 2;    // buffer-load cache policy: bit 1 = nt (streaming)
 constexpr size_t kSmallXldsBytes = 131456;   // X staged in LDS: at most 16 rows of 4096 (+16 bytes), a zero pad
@@ -49,6 +57,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     const uint16_t *__restrict__ X, int M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     AbsmaxSrc src, LowRank lr, void *__restrict__ Y) {
   __shared__ f32x4 red[kSmallWaves - 1][64];
+  {
+    // more than 16 rows: grid row y takes rows 16y .. 16y + 15 of X (and of U and Y)
+    const int m0 = kSmallRows * (int)blockIdx.y;
+    X += (int64_t)m0 * K;
+    lr.u += (int64_t)m0 * lr.r;
+    Y = reinterpret_cast<uint8_t *>(Y) + (int64_t)m0 * N * (Y_BF16 ? 2 : 4);
+    M = M - m0 < kSmallRows ? M - m0 : kSmallRows;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * kSmallCols;
@@ -816,7 +832,8 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
     hipLaunchKernelGGL(rows[K <= 4096 ? 0 : 1][src.qt ? 1 : 0][src.dq ? 1 : 0][src.lbs == 5 ? 1 : 0], dim3(grid),
                        dim3(64 * kRowsWaves), 0, stream, X, (int)M, N, K, packed, src, lr, y, y_is_bf16 ? 1 : 0, base,
                        extra);
-  } else if (M <= 16) {
+  } else if (M <= 16 || ((M + kSmallRows - 1) / kSmallRows) * N <= kSmallChunkBudget) {
+    // a few rows: the streaming kernel, one grid row per 16 rows of X
     using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *);
 #define NF4_SMALL(BS32, FP4, XL)                                                                              \
     {fwd_small_kernel<false, false, false, BS32, FP4, XL>, fwd_small_kernel<false, false, true, BS32, FP4, XL>, \
@@ -827,11 +844,13 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
                                       {NF4_SMALL(false, true, false), NF4_SMALL(true, true, false)}};
     static const K_t kern_xlds[2][8] = {NF4_SMALL(false, false, true), NF4_SMALL(false, true, true)};
 #undef NF4_SMALL
-    const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols)), b(64 * kSmallWaves);
+    const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols), (unsigned)((M + kSmallRows - 1) / kSmallRows)),
+        b(64 * kSmallWaves);
     // X staged in LDS (M >= 4, block sizes of 64 or more): it must fit, K must be a
     // multiple of 512, and every wave must own at least one superchunk of 256
     const int64_t nsc = (K + 255) / 256, per = (nsc + kSmallWaves - 1) / kSmallWaves;
-    const size_t xbytes = (size_t)M * (size_t)(2 * K + 16) + 128;
+    const int64_t mrows = M < kSmallRows ? M : kSmallRows;   // X rows a workgroup stages
+    const size_t xbytes = (size_t)mrows * (size_t)(2 * K + 16) + 128;
     const bool xlds = M >= 4 && src.lbs != 5 && K % 512 == 0 && (kSmallWaves - 1) * per < nsc &&
                       xbytes <= kSmallXldsBytes;
     if (xlds)

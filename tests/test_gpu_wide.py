@@ -1,8 +1,9 @@
 """GPU parity: the one-wave-per-SIMD GEMM kernels at their edges.
 
 "Zenbit" page, zenbit.pallas_nf4 bullet: the forward Y = X W^T and the
-backward dX = dY W^ with the weight dequantized on chip.  For M > 16 the
-forward runs four waves of 64 output columns whose lanes each own a whole
+backward dX = dY W^ with the weight dequantized on chip.  When the 16-row
+grid rows of the streaming kernel times N exceed 14 * 4096 the forward runs
+four waves of 64 output columns whose lanes each own a whole
 64-element chunk of a weight row per 128-K double step; the backward (N % 8
 == 0) runs four waves of 64 output columns that dequantize 64-column weight
 rows into a per-wave LDS tile.  "bitsandbytes" page, double-quantization
@@ -44,10 +45,10 @@ def _case(M, N, K, seed, dq=True, qt="nf4", bs=64):
 @pytest.mark.parametrize("dq", [True, False])
 def test_every_instantiation_on_a_cut_tile(dq, qt, bs):
     # M = 300: the second row tile has 44 rows (one wave's worth, the other three
-    # waves load zeros); N = 328: the second column tile has one full wave, one
+    # waves load zeros); N = 3400: the last column tile has one full wave, one
     # wave of 8 columns and two waves past N; K = 768: three pairs of double
-    # steps.  The backward of the same weight (N % 8 == 0) on dY [300, 328].
-    M, N, K = 300, 328, 768
+    # steps.  The backward of the same weight (N % 8 == 0) on dY [300, 3400].
+    M, N, K = 300, 3400, 768
     note(f"wide fwd/bwd dq={dq} {qt} bs={bs} {M}x{N}x{K}")
     dg, q, X, wh = _case(M, N, K, 1000 + 10 * dq + (qt == "fp4") + bs, dq, qt, bs)
     dY = synth.normal((M, N), 1.0, 1100 + bs)
@@ -66,13 +67,14 @@ def test_every_instantiation_on_a_cut_tile(dq, qt, bs):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (256, 256, 256),     # one whole tile, one pair of double steps
-    (512, 768, 512),     # whole tiles in both directions
-    (257, 65, 1024),     # one row and one column past a tile
-    (17, 1000, 2304),    # a single partial row tile; nine pairs
-    (600, 300, 384),     # three double steps and a padding one
-    (40, 200, 64),       # K = 64: one chunk, lane group 1 and the second double step all padding
-    (300, 129, 320),     # five chunks: the third double step's second half is padding
+    (256, 4096, 256),    # one whole row of tiles, one pair of double steps
+    (512, 2048, 512),    # whole tiles in both directions
+    (257, 3585, 1024),   # one row and one column past a tile
+    (17, 28800, 256),    # a single partial row tile
+    (300, 3100, 2304),   # nine pairs
+    (600, 1600, 384),    # three double steps and a padding one
+    (300, 3100, 64),     # K = 64: one chunk, lane group 1 and the second double step all padding
+    (300, 3073, 320),    # five chunks: the third double step's second half is padding
 ])
 def test_shapes(M, N, K):
     note(f"wide fwd {M}x{N}x{K}")
@@ -86,7 +88,7 @@ def test_shapes(M, N, K):
 @pytest.mark.parametrize("bs", [128, 256])
 def test_large_block_sizes(bs):
     """Block sizes above 64: one block per 64-element chunk, blocks spanning rows (K = 320)."""
-    M, N, K = 280, 200, 320
+    M, N, K = 280, 3300, 320
     note(f"wide fwd/bwd bs={bs}")
     dg, q, X, wh = _case(M, N, K, 1300 + bs, True, "nf4", bs)
     dY = synth.normal((M, N), 1.0, 1301 + bs)
@@ -101,7 +103,7 @@ def test_large_block_sizes(bs):
 @pytest.mark.parametrize("bs,r", [(64, 48), (32, 128)])
 def test_adapter_term_on_cut_tiles(bs, r):
     """The adapter term added in the same accumulators: ragged tiles, ranks over one staged chunk."""
-    M, N, K = 300, 264, 320
+    M, N, K = 300, 3080, 320
     note(f"wide fwd/bwd + adapter bs={bs} r={r}")
     dg, q, X, wh = _case(M, N, K, 1500 + bs + r, True, "nf4", bs)
     U = synth.normal((M, r), 1.0, 1501 + r)
@@ -125,7 +127,7 @@ def test_adapter_term_on_cut_tiles(bs, r):
 
 def test_identity_rows_reproduce_the_weight():
     """X = rows of I: each output row is a dequantized weight column, exactly (K = 512)."""
-    N, K = 320, 512
+    N, K = 3100, 512
     dg, q, _, wh = _case(64, N, K, 4321)
     X = torch.eye(K, dtype=torch.bfloat16)[100:400].contiguous()
     Y = dg.nf4_matmul_fwd(X.to(dev()), q)
