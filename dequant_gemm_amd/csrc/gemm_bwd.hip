@@ -366,6 +366,12 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   // they read columns K-64 .. K-1 and are never stored)
   const int64_t kcol = k0 + 64 * wave;
   const int64_t kc = kcol < K ? kcol : K - 64;
+  // The weight rows are dequantized with the even/odd selectors (two byte
+  // permutes fewer per eight codes): the eight values of each code word go to
+  // the tile in the column order 0, 2, 4, 6, 1, 3, 5, 7, so tile column q holds
+  // weight column 8 (q / 8) + 2 (q % 4) + (q % 8) / 4, and lane l's results
+  // (tile column l % 32 of each half) belong to that column.
+  const int bcol = (bl & ~7) | ((bl & 3) << 1) | ((bl >> 2) & 1);
   // weight row of this lane in step s: n = 64s + lane; the flat index of its
   // first column, n K + kc, shifted by log2(block size) gives its block (64
   // columns never straddle a block of 64 or more; at 32 they are two blocks)
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
           make_uint4(st[4 * c], st[4 * c + 1], st[4 * c + 2], st[4 * c + 3]);
   };
   auto dequant_word = [&](uint32_t wd, const Lut &t, uint32_t *out, int phase, Sel4 &sa, Sel4 &sb) {
-    if (phase == 0) select8(wd, sa, sb);
+    if (phase == 0) select8_even_odd(wd, sa, sb);
     if (phase == 1) lookup4(sa, t, out[0], out[1]);
     if (phase == 2) lookup4(sb, t, out[2], out[3]);
   };
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
         for (int q = 0; q < 4; ++q) lut_quarter<FP4>(ah1, q, t);
       }
       Sel4 sa, sb;
-      select8(wd[c], sa, sb);
+      select8_even_odd(wd[c], sa, sb);
       lookup4(sa, t, st[4 * c], st[4 * c + 1]);
       lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
     }
@@ -628,7 +634,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   if (s + 1 < ns) step(s + 1, as1, as2, as0, cs2, cs1);
   __builtin_amdgcn_s_waitcnt(0);
   if (LR) {
-    const int64_t col[2] = {kc + bl, kc + 32 + bl};
+    const int64_t col[2] = {kc + bcol, kc + 32 + bcol};
     // ranks in chunks of 48 (256 staged rows of 112 bytes in the first dY stage)
     add_lowrank_wide<48>(acc, lr, m0, M, col, bl, kg, as0);
   }
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   // epilogue: lane l, register r of a 32x32 tile holds row 8(r/4)+4(l/32)+r%4, column l%32
   if (m0 + TM <= M && k0 + TK <= K && K < ((int64_t)1 << 27)) {
     constexpr int ES = DX_BF16 ? 2 : 4;
-    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)K + bl) * ES;
+    const uint32_t voff = (uint32_t)((4 * kg) * (uint32_t)K + bcol) * ES;
     uint8_t *xcol = reinterpret_cast<uint8_t *>(dX) + (m0 * K + kcol) * ES;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -661,7 +667,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
         for (int r = 0; r < 16; ++r) {
           const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * kg + (r % 4);
           if (row < M) {
-            const int64_t off = row * K + kcol + 32 * c + bl;
+            const int64_t off = row * K + kcol + 32 * c + bcol;
             if (DX_BF16)
               reinterpret_cast<uint16_t *>(dX)[off] = (uint16_t)(pack_bf16x2(acc[i][c][r], 0.f) & 0xffffu);
             else
