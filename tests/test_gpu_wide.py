@@ -75,6 +75,7 @@ def test_every_instantiation_on_a_cut_tile(dq, qt, bs):
     (600, 1600, 384),    # three double steps and a padding one
     (300, 3100, 64),     # K = 64: one chunk, lane group 1 and the second double step all padding
     (300, 3073, 320),    # five chunks: the third double step's second half is padding
+    (300, 33000, 256),   # 2 x 129 tiles: more tiles than CUs (a second round of workgroups, cut tiles)
 ])
 def test_shapes(M, N, K):
     note(f"wide fwd {M}x{N}x{K}")
