@@ -736,6 +736,21 @@ def run_single_op(dg, op, steps, warmup):
             torch.cuda.synchronize()
         print(json.dumps({"op": op, "calls_per_m": warmup + steps}), flush=True)
         return
+    elif op in ("large_fwd", "large_bwd_dx"):
+        # the 8192 x 8192 x 28672 GEMMs on the Student-t weight, inputs drawn on the device as in bench_large
+        M, K, N = synth.LARGE_M, synth.LARGE_K, synth.LARGE_N
+        torch.manual_seed(4000)
+        W = (torch.distributions.StudentT(torch.tensor(4.0, device=d)).sample((N, K)) * 0.02).float().contiguous()
+        q = dg.nf4_quantize(W)
+        del W
+        if op == "large_fwd":
+            X = _device_normal((M, K), 1.0, 4001, d)
+            Y = torch.empty((M, N), dtype=torch.float32, device=d)
+            fn = lambda i: dg.nf4_matmul_fwd(X, q, out=Y)
+        else:
+            dY = _device_normal((M, N), 0.01, 4002, d)
+            dX = torch.empty((M, K), dtype=torch.float32, device=d)
+            fn = lambda i: dg.nf4_matmul_bwd_dx(dY, q, out=dX)
     elif op == "decode":
         K, N = synth.DECODE_K, synth.DECODE_N
         qs = [dg.nf4_quantize(w.to(d)) for w in synth.parallel(synth.decode_weight, range(16))]
@@ -808,7 +823,7 @@ def main():
                     help="skip the profiler run that takes the decode kernels' own durations")
     ap.add_argument("--op", default=None,
                     choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "dense_fwd", "dense_bwd_dx", "decode",
-                             "decode_large", "decode_trace", "copy"],
+                             "decode_large", "decode_trace", "large_fwd", "large_bwd_dx", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE counter runs in PMC_DIR and exit")

@@ -511,6 +511,9 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
       lookup4(sb, t, st[4 * c + 2], st[4 * c + 3]);
     }
     write_row(st);
+    // the row has landed before it is read back (the transposing reads are not
+    // ordered behind this wave's earlier LDS writes by anything else here)
+    __builtin_amdgcn_s_waitcnt(lgkm_imm(0));
     b0[0][0] = tr_read(0, 0, 0);
     b0[0][1] = tr_read(0, 1, 0);
     b0[1][0] = tr_read(0, 0, 1);
@@ -554,10 +557,16 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
         __builtin_amdgcn_s_barrier();
         sched_cut();
         issue_codes(s + 3, cfill);
-        b0[0][0] = tr_read(0, 0, 0);
-        b0[0][1] = tr_read(0, 1, 0);
-        b0[1][0] = tr_read(0, 0, 1);
-        b0[1][1] = tr_read(0, 1, 1);
+        // the next step's slice-0 fragments, only if there is a next step: the
+        // compiler takes an inline-asm load's result as written at once, so a
+        // result nothing consumes would leave its registers free for reuse while
+        // the load is still in flight
+        if (s + 1 < ns) {
+          b0[0][0] = tr_read(0, 0, 0);
+          b0[0][1] = tr_read(0, 1, 0);
+          b0[1][0] = tr_read(0, 0, 1);
+          b0[1][1] = tr_read(0, 1, 1);
+        }
         sched_cut();
       }
       if constexpr (g == 0) {
