@@ -751,11 +751,13 @@ def run_single_op(dg, op, steps, warmup):
             dY = _device_normal((M, N), 0.01, 4002, d)
             dX = torch.empty((M, K), dtype=torch.float32, device=d)
             fn = lambda i: dg.nf4_matmul_bwd_dx(dY, q, out=dX)
-    elif op == "decode":
+    elif op in ("decode", "decode_m1"):
+        # decode forward on 16 rotating quantized 4096 x 4096 weights, M = 16 (decode) or 1 (decode_m1)
         K, N = synth.DECODE_K, synth.DECODE_N
+        Md = 16 if op == "decode" else 1
         qs = [dg.nf4_quantize(w.to(d)) for w in synth.parallel(synth.decode_weight, range(16))]
-        X = synth.decode_x(16).to(d)
-        Y = torch.empty((16, N), dtype=torch.float32, device=d)
+        X = synth.decode_x(Md).to(d)
+        Y = torch.empty((Md, N), dtype=torch.float32, device=d)
         fn = lambda i: dg.nf4_matmul_fwd(X, qs[i % len(qs)], out=Y)
     else:
         M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
@@ -823,7 +825,7 @@ def main():
                     help="skip the profiler run that takes the decode kernels' own durations")
     ap.add_argument("--op", default=None,
                     choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "dense_fwd", "dense_bwd_dx", "decode",
-                             "decode_large", "decode_trace", "large_fwd", "large_bwd_dx", "copy"],
+                             "decode_m1", "decode_large", "decode_trace", "large_fwd", "large_bwd_dx", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE counter runs in PMC_DIR and exit")
