@@ -519,9 +519,12 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
     b0[1][0] = tr_read(0, 0, 1);
     b0[1][1] = tr_read(0, 1, 1);
   }
-  // dY tile 0 landed (tile 1 and the codes of steps 1 and 2 may be in flight);
-  // the slice-0 B fragments read (lgkmcnt(0))
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + 2 * (DQ ? 4 : 3)) & ~(0xF << 8));
+  // every load landed, dY tiles 0 and 1 included; the slice-0 B fragments read
+  // (lgkmcnt(0)).  The wait is for all vector-memory operations: a count that
+  // leaves later loads in flight does not order the buffer-to-LDS loads before
+  // them (measured: a wait that let the last eight loads run on let tiles be read
+  // before they had landed)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~(0xF << 8));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4 *>(as0 + aoff[0] + i * 32 * AROW);
@@ -538,9 +541,10 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
   //               groups 14-15 (in place) and words 4-7 in groups 16-27;
   //               written to the weight tile two 16-byte chunks per group in
   //               groups 24-27 (the step's last B reads completed at group 24)
-  //   hand-over   before group 28: this wave's LDS traffic is complete and the
-  //               next dY tile has landed, barrier, codes three steps ahead,
-  //               the next step's slice-0 B reads
+  //   hand-over   before group 28: this wave's LDS traffic is complete and all
+  //               its loads have landed (the next dY tile among them; the tile
+  //               two steps ahead was issued in groups 0-14), barrier, codes
+  //               three steps ahead, the next step's slice-0 B reads
   auto step = [&](int64_t s, uint8_t *rd, uint8_t *nx, uint8_t *ld, const RowCodesW<BS32> &cn, RowCodesW<BS32> &cfill) {
     Sel4 sa, sb;
     Lut t;
@@ -553,7 +557,7 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
       v4s(*bc)[2] = (slice & 1) ? b1 : b0;
       v4s(*bn)[2] = (slice & 1) ? b0 : b1;
       if constexpr (r == 28) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(8) & ~(0xF << 8));   // vmcnt(8) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~(0xF << 8));   // vmcnt(0) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         sched_cut();
         issue_codes(s + 3, cfill);

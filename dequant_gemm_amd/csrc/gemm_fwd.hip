@@ -51,6 +51,7 @@ constexpr int64_t kSmallChunkBudget = 14 * 4096;
 constexpr int kSmallWaves = 8;
 constexpr int kNonTemporal = 2;    // buffer-load cache policy: bit 1 = nt (streaming)
 constexpr size_t kSmallXldsBytes = 131456;   // X staged in LDS: at most 16 rows of 4096 (+16 bytes), a zero pad
+constexpr int kSmallXldsRows = 13;           // X staged in LDS from this many rows on
 
 template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4, bool XLDS>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
@@ -132,11 +133,16 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   // XLDS: X [M, K] staged in LDS by buffer-to-LDS loads issued before any
   // weight load (row m at m * (2K + 16) bytes, padded against bank
   // conflicts), one 1 KiB piece per wave instruction; fragments are then read
-  // from LDS by the lanes whose X row exists.  Against per-lane X loads from
-  // L2 (each instruction touching 64 different 128-byte lines) this took a
-  // 4096x4096 call from 5.83 / 7.88 to 5.66 / 7.16 us at M = 4 / 16.  The
-  // launcher uses it only when every wave owns at least one superchunk (the
-  // hand-over barrier is inside the first iteration) and K % 512 == 0.
+  // from LDS by the lanes whose X row exists.  The loads have landed only
+  // after a wait for every vector-memory operation, the weight loads issued
+  // after them included (a count that leaves those in flight does not order
+  // buffer-to-LDS loads before them), so the first chunk's arithmetic waits
+  // for the second chunk's codes.  Against per-lane X loads from L2 (each
+  // instruction touching 64 different 128-byte lines) staging is faster from
+  // about 13 rows on: 4096x4096 calls, per-lane / staged, 5.93 / 6.52 us at
+  // M = 4, 7.31 / 7.39 at M = 12, 8.00 / 7.66 at M = 16.  The launcher uses it
+  // from M = 13, when every wave owns at least one superchunk (the hand-over
+  // barrier is inside the first iteration) and K % 512 == 0.
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   const uint32_t xstride = (uint32_t)(K * 2 + 16);
   const uint32_t xzero = (uint32_t)M * xstride;     // 128 zero bytes after the M rows
@@ -186,10 +192,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
     }
     if (XLDS) {
       if (sc == s0) {
-        // the X pieces were issued before this iteration's weight loads: two
-        // chunks of two code loads and the absmax state (1 or 2 loads per block)
-        constexpr int kAfterX = 2 * (2 + (DQ ? 2 : 1) * (BS32 ? 2 : 1));
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterX));
+        // the X pieces landed: a wait for all vector-memory operations (a count
+        // that leaves the later weight loads in flight does not order the
+        // buffer-to-LDS loads before them)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_waitcnt(lgkm_imm(0));      // the zero pad's stores
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -846,12 +852,12 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
 #undef NF4_SMALL
     const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols), (unsigned)((M + kSmallRows - 1) / kSmallRows)),
         b(64 * kSmallWaves);
-    // X staged in LDS (M >= 4, block sizes of 64 or more): it must fit, K must be a
+    // X staged in LDS (M >= 13, block sizes of 64 or more): it must fit, K must be a
     // multiple of 512, and every wave must own at least one superchunk of 256
     const int64_t nsc = (K + 255) / 256, per = (nsc + kSmallWaves - 1) / kSmallWaves;
     const int64_t mrows = M < kSmallRows ? M : kSmallRows;   // X rows a workgroup stages
     const size_t xbytes = (size_t)mrows * (size_t)(2 * K + 16) + 128;
-    const bool xlds = M >= 4 && src.lbs != 5 && K % 512 == 0 && (kSmallWaves - 1) * per < nsc &&
+    const bool xlds = M >= kSmallXldsRows && src.lbs != 5 && K % 512 == 0 && (kSmallWaves - 1) * per < nsc &&
                       xbytes <= kSmallXldsBytes;
     if (xlds)
       hipLaunchKernelGGL(kern_xlds[src.qt ? 1 : 0][sel], g, b, xbytes, stream, X, (int)M, N, K, packed, src, lr, y);
