@@ -12,10 +12,12 @@
 // Kernels, chosen by M and the weight's layout:
 //   fwd_rows_kernel   M <= 16 over many weight rows: one 16-wave workgroup per
 //                     CU walks a run of 16-row groups with X in registers.
-//   fwd_small_kernel  M <= 16 otherwise, streaming-bound: one workgroup per 16
-//                     weight rows, its eight waves split K; every weight byte is
-//                     read once, all of a lane's loads are issued together.
-//   fwd_wide_kernel   M > 16, matrix-core-bound: 256x256 output tiles, four
+//   fwd_small_kernel  M <= 16 otherwise, and larger M while its 16-row grid
+//                     rows times N stay small, streaming-bound: one workgroup
+//                     per 16 weight rows (per grid row), its eight waves split
+//                     K; every weight byte is read once per grid row, all of a
+//                     lane's loads are issued together.
+//   fwd_wide_kernel   otherwise, matrix-core-bound: 256x256 output tiles, four
 //                     waves of 64 weight rows (one wave per SIMD), X staged
 //                     through LDS by buffer-to-LDS loads; a lane dequantizes
 //                     whole 64-element chunks of its weight rows straight into
