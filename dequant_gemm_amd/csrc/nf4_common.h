@@ -263,18 +263,37 @@ __device__ __forceinline__ void add_lowrank_wide(f32x16 acc[8][2], const LowRank
         bv1[s] = *reinterpret_cast<const uint4 *>(vrow1 + r0 + 16 * s);
       }
     });
-    __syncthreads();   // the buffer is free
-    // U rows into the buffer (global and LDS accesses never alias: the loads
-    // need not wait for the stores)
-#pragma unroll
-    for (int k = 0; k < CH / 8; ++k) {
-      const int c = threadIdx.x + 256 * k;
-      const int row = c / cpr, ch = c - row * cpr;
-      const int64_t grow = m0 + row < M ? m0 + row : M - 1;
-      if (c < 256 * cpr)
-        *reinterpret_cast<uint4 *>(buf + row * ROW + 16 * ch) =
-            *reinterpret_cast<const uint4 *>(lr.u + grow * lr.r + r0 + 8 * ch);
+    // U rows into the buffer: piece c = threadIdx.x + 256 k (k < cpr, a
+    // condition the whole workgroup shares) is row c / cpr, 16-byte chunk
+    // c % cpr.  Every load is issued before the first store, so that the loads'
+    // latencies overlap (with a store after each load, each waited for its own).
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 up[CH / 8];
+    uint32_t poff[CH / 8];   // the pieces' byte offsets in the buffer
+    {
+      const int q = 256 / cpr, rm = 256 - q * cpr;      // 256 threads = q rows + rm chunks
+      int row = (int)threadIdx.x / cpr, ch = (int)threadIdx.x - row * cpr;
+      static_for<CH / 8>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        poff[k] = (uint32_t)(row * ROW + 16 * ch);
+        // (a piece past the chunk loads U's first 16 bytes instead, never stored:
+        // no branch around the load)
+        const int64_t grow = m0 + row < M ? m0 + row : M - 1;
+        const int64_t eoff = k < cpr ? grow * lr.r + r0 + 8 * ch : 0;
+        up[k] = *reinterpret_cast<const u32x4 *>(lr.u + eoff);
+        row += q;
+        ch += rm;
+        if (ch >= cpr) {
+          ch -= cpr;
+          ++row;
+        }
+      });
     }
+    __syncthreads();   // the buffer is free
+    static_for<CH / 8>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if (k < cpr) *reinterpret_cast<u32x4 *>(buf + poff[k]) = up[k];
+    });
     __syncthreads();
     static_for<CH / 16>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
