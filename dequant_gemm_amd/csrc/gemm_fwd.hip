@@ -53,7 +53,7 @@ constexpr int64_t kSmallChunkBudget = 14 * 4096;
 constexpr int kSmallWaves = 8;
 constexpr int kNonTemporal = 2;    // buffer-load cache policy: bit 1 = nt (streaming)
 constexpr size_t kSmallXldsBytes = 131456;   // X staged in LDS: at most 16 rows of 4096 (+16 bytes), a zero pad
-constexpr int kSmallXldsRows = 13;           // X staged in LDS from this many rows on
+constexpr int kSmallXldsRows = 11;           // X staged in LDS from this many rows on
 
 template <bool Y_BF16, bool DQ, bool LR, bool BS32, bool FP4, bool XLDS>
 __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
@@ -141,21 +141,34 @@ __global__ __launch_bounds__(64 * kSmallWaves) void fwd_small_kernel(
   // buffer-to-LDS loads before them), so the first chunk's arithmetic waits
   // for the second chunk's codes.  Against per-lane X loads from L2 (each
   // instruction touching 64 different 128-byte lines) staging is faster from
-  // about 13 rows on: 4096x4096 calls, per-lane / staged, 5.93 / 6.52 us at
-  // M = 4, 7.31 / 7.39 at M = 12, 8.00 / 7.66 at M = 16.  The launcher uses it
-  // from M = 13, when every wave owns at least one superchunk (the hand-over
-  // barrier is inside the first iteration) and K % 512 == 0.
+  // about 11 rows on: 4096x4096 calls, per-lane / staged, 5.92 / 6.48 us at
+  // M = 4, 6.59 / 6.72 at 8, 6.86 / 6.82 at 10, 7.33 / 6.93 at 12.  The launcher
+  // uses it from M = 11, when every wave owns at least one superchunk (the
+  // hand-over barrier is inside the first iteration) and K % 512 == 0.
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   const uint32_t xstride = (uint32_t)(K * 2 + 16);
   const uint32_t xzero = (uint32_t)M * xstride;     // 128 zero bytes after the M rows
   if (XLDS) {
     if (threadIdx.x < 8) *reinterpret_cast<uint4 *>(xs + xzero + 16 * threadIdx.x) = make_uint4(0u, 0u, 0u, 0u);
+    // Piece c0 = 64 w + 512 i (while c0 < M cpr) is row c0 / cpr, 16-byte chunk
+    // c0 % cpr; both are kept as wave-uniform counters (scalar registers), so a
+    // lane's offset is the constant 16 l and the rest is the scalar offset: no
+    // per-lane division or 64-bit multiply ahead of the weight loads.
     const int cpr = (int)(K / 8);                   // 16-byte pieces per X row, a multiple of 64
-    const int total = M * cpr;
-    for (int c0 = 64 * wave; c0 < total; c0 += 64 * kSmallWaves) {
-      const int m = c0 / cpr, ch0 = c0 - m * cpr;
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    int m = 0, ch0 = 64 * wv;
+    while (ch0 >= cpr) {
+      ch0 -= cpr;
+      ++m;
+    }
+    while (m < M) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void *)(xs + m * xstride + 16 * ch0), 16,
-                                               (uint32_t)((m * K + (int64_t)(ch0 + lane) * 8) * 2), 0, 0, 0);
+                                               16u * (uint32_t)lane, (uint32_t)(m * (int)K * 2 + 16 * ch0), 0, 0);
+      ch0 += 64 * kSmallWaves;
+      while (ch0 >= cpr) {
+        ch0 -= cpr;
+        ++m;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -854,7 +867,7 @@ hipError_t launch_fwd(const void *x, int64_t M, int64_t N, int64_t K, const uint
 #undef NF4_SMALL
     const dim3 g((unsigned)((N + kSmallCols - 1) / kSmallCols), (unsigned)((M + kSmallRows - 1) / kSmallRows)),
         b(64 * kSmallWaves);
-    // X staged in LDS (M >= 13, block sizes of 64 or more): it must fit, K must be a
+    // X staged in LDS (M >= 11, block sizes of 64 or more): it must fit, K must be a
     // multiple of 512, and every wave must own at least one superchunk of 256
     const int64_t nsc = (K + 255) / 256, per = (nsc + kSmallWaves - 1) / kSmallWaves;
     const int64_t mrows = M < kSmallRows ? M : kSmallRows;   // X rows a workgroup stages

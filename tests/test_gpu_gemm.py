@@ -143,6 +143,25 @@ def test_decode_full(M):
     assert_gemm_within_bound(Y, O.matmul_fwd(x, wh), O.fwd_bound(x, wh), f"decode M={M}")
 
 
+@pytest.mark.parametrize("N,K", [(1000, 2048), (520, 4096)])
+def test_small_m_every_row_count(N, K):
+    """M = 1 .. 16 on one weight: the small-M forward reads X per lane below 11 rows and from
+    the copy staged in LDS from 11 rows on; K = 2048 puts two rows of X in one copy round of
+    the eight waves (a wave's first piece in the second row), K = 4096 one."""
+    dg = lib()
+    d = dev()
+    W = synth.normal((N, K), 0.02, 7 * N + K, torch.bfloat16)
+    q = dg.nf4_quantize(W.to(d))
+    wh = _oracle_what(W).astype(np.float64)
+    for M in range(1, 17):
+        note(f"small-M fwd M={M} N={N} K={K}")
+        X = synth.normal((M, K), 1.0, 100 * M + K)
+        Y = dg.nf4_matmul_fwd(X.to(d), q)
+        torch.cuda.synchronize()
+        x = X.float().numpy()
+        assert_gemm_within_bound(Y, O.matmul_fwd(x, wh), O.fwd_bound(x, wh), f"small M={M} N={N} K={K}")
+
+
 @pytest.fixture(scope="module")
 def prefill():
     dg = lib()
