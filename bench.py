@@ -16,7 +16,8 @@ timings (HIP events around every launch of a second pass of as many steps), the
 dequantizer, the rank-64 adapter variants of both GEMMs, the decode-shape
 forward (M = 1, 4, 16 on a rotating pool of 512 quantized 4096x4096 weights,
 replayed from a HIP graph so host launch overhead does not count; and each
-dispatch's own duration from a rocprofv3 kernel trace of a child process), a
+dispatch's own duration from a rocprofv3 kernel trace of a child process), the
+backward dX = dY W^ at the same row counts over the same pool, a
 plain HBM read stream (the achievable bandwidth), the
 outlier-heavy large shape (M = K = 8192, N = 28672, fp32 Student-t weight), the
 32-layer bulk quantize/dequantize round trip, the prefill workload at block sizes
@@ -309,6 +310,24 @@ def bench_decode(dg, pool=512, reps=10):
                                "frac_hbm": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                                "TFLOP/s": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
         del g
+        # the backward dX = dY W^ at the same row counts over the same pool (context:
+        # a small-batch backward, one workgroup per 32 output columns streaming the weight)
+        dY = _device_normal((M, N), 1.0, 1200 + M, d)
+        dX = torch.empty((M, K), dtype=torch.float32, device=d)
+        for qq in qs:
+            dg.nf4_matmul_bwd_dx(dY, qq, out=dX)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for qq in qs:
+                dg.nf4_matmul_bwd_dx(dY, qq, out=dX)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_events(g.replay, reps) / pool
+        b = M * N * 2 + wq_bytes(N, K) + M * K * 4
+        out[f"decode_bwd_dx_m{M}"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
+                                      "frac_hbm": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del g, dY, dX
     # Context: the per-call floor of this measurement -- a one-element kernel replayed
     # the same way (one launch per pool entry).  No kernel can take less per call here.
     t = torch.zeros(1, device=d)
@@ -759,6 +778,13 @@ def run_single_op(dg, op, steps, warmup):
         X = synth.decode_x(Md).to(d)
         Y = torch.empty((Md, N), dtype=torch.float32, device=d)
         fn = lambda i: dg.nf4_matmul_fwd(X, qs[i % len(qs)], out=Y)
+    elif op == "decode_bwd":
+        # the backward dX = dY W^ on 16 rotating quantized 4096 x 4096 weights, M = 16
+        K, N = synth.DECODE_K, synth.DECODE_N
+        qs = [dg.nf4_quantize(w.to(d)) for w in synth.parallel(synth.decode_weight, range(16))]
+        dY = synth.normal((16, N), 1.0, 1216).to(d)
+        dX = torch.empty((16, K), dtype=torch.float32, device=d)
+        fn = lambda i: dg.nf4_matmul_bwd_dx(dY, qs[i % len(qs)], out=dX)
     else:
         M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
         W = synth.prefill_weight().to(d)
@@ -824,7 +850,7 @@ def main():
     ap.add_argument("--no-decode-trace", action="store_true",
                     help="skip the profiler run that takes the decode kernels' own durations")
     ap.add_argument("--op", default=None,
-                    choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "dense_fwd", "dense_bwd_dx", "decode",
+                    choices=["fwd", "bwd_dx", "fwd_bs32", "bwd_dx_bs32", "quantize", "dequantize", "dense_fwd", "dense_bwd_dx", "decode", "decode_bwd",
                              "decode_m1", "decode_large", "decode_trace", "large_fwd", "large_bwd_dx", "copy"],
                     help="run only this operation, --steps times (profiler runs); prints its own JSON line")
     ap.add_argument("--write-traffic", metavar="PMC_DIR", default=None,

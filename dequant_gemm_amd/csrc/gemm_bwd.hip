@@ -10,8 +10,11 @@
 // dequantized weight has to change orientation before it can feed the MFMA
 // (whose operands hold eight consecutive reduction indices per lane).
 //
-// Two kernels:
-//   bwd_dx_wide_kernel     N % 8 == 0 (16-byte dY rows) and N < 2^24: dY
+// Three kernels:
+//   bwd_dx_small_kernel    at most 16 rows of dY, N % 8 == 0 and N < 2^24: one
+//                          workgroup per 64 output columns streams the whole
+//                          weight chunk, 16 waves taking 64-row steps in turn.
+//   bwd_dx_wide_kernel     otherwise, N % 8 == 0 (16-byte dY rows) and N < 2^24: dY
 //                          through buffer-to-LDS loads, each wave dequantizes
 //                          its own 64 weight columns row by row into a private
 //                          LDS tile and reads MFMA operands back with
@@ -693,6 +696,190 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
 }
 }  // namespace tr_kernel
 
+// ------------------------------------------------------------ small-M kernel
+//
+// For at most 16 rows of dY the 256x256 kernels above would leave 15/16 of
+// every MFMA idle and launch one workgroup per 256 output columns; here the
+// work is the weight stream.  Workgroup b owns the 64 output columns
+// k0 = 64b .. +63 (one 64-element chunk of every weight row) over all N rows
+// of the reduction; its 16 waves (four per SIMD) take steps of 64 weight rows
+// in turn (wave w: steps w, w + 16, ...).  In a step lane l dequantizes row
+// 64s + l of the chunk -- one table per 64 weights (two at block size 32) --
+// and writes the 64 bf16 values as one row of the wave's own LDS tile; the
+// transposing read ds_read_b64_tr_b16 then hands each lane eight consecutive
+// rows of one column (within a 16-lane group, output lane i element e is
+// element i%4 of the 8 bytes addressed by lane 4e + i/4), the B operand of
+// MFMA 16x16x32 whose A operand is dY (lane l: row l%16, the same eight
+// reduction indices 8(l/16) .. +7 of a 32-row half).  Rows of dY past M and
+// reduction indices past N load zeros (buffer descriptor), so the weight rows
+// past N (read clamped to the last row) add exact zeros.  The next step's
+// codes, absmax state and dY fragments are loaded before the current step is
+// dequantized.  At the end the 16 waves' partial sums meet in LDS and each
+// thread adds one output element's 16 parts in wave order (deterministic).
+namespace small {
+
+constexpr int SW = 16;                  // waves per workgroup, four per SIMD
+constexpr int SR = 64;                  // weight rows per wave step, one per lane
+constexpr int kMaxRows = 16;            // rows of dY (the MFMA's 16 A rows)
+constexpr int64_t kSmallWideBands = 129;   // 64-column bands from this many on (else 32: K/32 <= 256 workgroups)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// CW output columns per workgroup (32 or 64): a lane's CW codes of one weight
+// row lie in one block, or in two at block size 32 with CW = 64 (BS32).
+template <int CW, bool BS32>
+struct StepIn {
+  uint4 c[CW / 32];        // the lane's CW codes
+  ChunkAbsmax<BS32> ab;    // their block's absmax state
+  uint4 a[2];              // dY fragments of the two 32-row halves
+};
+
+template <int CW, bool DQ, bool BS32, bool FP4, bool LR>
+__global__ __launch_bounds__(64 * SW) void bwd_dx_small_kernel(const uint16_t *__restrict__ dY, int M, int64_t N,
+                                                               int64_t K, const uint8_t *__restrict__ packed,
+                                                               AbsmaxSrc src, LowRank lr, void *__restrict__ dX,
+                                                               int dx_bf16) {
+  static_assert(CW == 32 || CW == 64, "32 or 64 columns per workgroup");
+  static_assert(!BS32 || CW == 64, "a 32-column chunk lies in one block at every block size");
+  constexpr int NJ = CW / 16;           // MFMA column groups
+  constexpr int SROW = 2 * CW + 16;     // LDS tile row: CW bf16 + 16 bytes of padding
+  constexpr int STILE = SR * SROW;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[SW * STILE > SW * NJ * 64 * 16 ? SW * STILE : SW * NJ * 64 * 16];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, kg = lane >> 4;
+  // bands sharing a 128-byte line of codes go to workgroups of one XCD
+  // (consecutive workgroups are dealt to the eight XCDs in turn)
+  int band = blockIdx.x;
+  {
+    const int nb = gridDim.x, q = nb / 8, r = nb % 8, x = band % 8, i = band / 8;
+    band = x * q + (x < r ? x : r) + i;
+  }
+  const uint32_t k0 = (uint32_t)band * CW;
+  const float mu = DQ ? *src.mean : 0.f;
+  uint8_t *tile = tiles + wave * STILE;
+  // 32-bit offsets throughout (the launcher keeps N K below 2^32 and K below
+  // 2^24, so row offsets are 24-bit products).  Codes from the workgroup's
+  // column band on; dY [M, N] (at most 16 x 2^24 elements): lanes whose row
+  // lies past M, and reduction indices past N, get offsets beyond the
+  // descriptor (zeros).
+  const uint32_t rowb = (uint32_t)(K / 2), Nu = (uint32_t)N, Ku = (uint32_t)K;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(packed + k0 / 2), (short)0, (int)(Nu * rowb - k0 / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(dY), (short)0,
+                                                                       (int)((uint32_t)M * Nu * 2u), 0x00020000);
+  const uint32_t yrow = col < M ? (uint32_t)col * Nu * 2u : 0x80000000u;
+  const int nsteps = (int)((N + SR - 1) / SR);
+
+  auto load_step = [&](int s, StepIn<CW, BS32> &in) {
+    s = s < nsteps ? s : nsteps - 1;   // past the last step: a repeat, never used
+    const uint32_t n = (uint32_t)s * SR + (uint32_t)lane;
+    const uint32_t nc = n < Nu ? n : Nu - 1;
+    const uint32_t co = __umul24(nc, rowb);
+#pragma unroll
+    for (int u = 0; u < CW / 32; ++u)
+      in.c[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(crs, co + 16u * u, 0, 0));
+    in.ab.template load<DQ>(src, (int64_t)((__umul24(nc, Ku) + k0) >> src.lbs));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t na = (uint32_t)s * SR + 32u * h + 8u * kg;   // N % 8 == 0: all eight indices in or out
+      const uint32_t off = na < Nu ? yrow + na * 2u : 0x80000000u;
+      in.a[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(yrs, off, 0, 0));
+    }
+  };
+
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](const StepIn<CW, BS32> &in) {
+    const Lut t0 = make_lut<FP4>(in.ab.ahat(0, DQ, mu));
+    Lut t1;
+    if (BS32) t1 = make_lut<FP4>(in.ab.ahat(1, DQ, mu));
+    uint4 row[CW / 8];
+#pragma unroll
+    for (int j = 0; j < CW / 8; ++j) {
+      const uint4 &cw = in.c[j / 4];
+      const uint32_t word = (j % 4 == 0) ? cw.x : (j % 4 == 1) ? cw.y : (j % 4 == 2) ? cw.z : cw.w;
+      const Lut &tj = (BS32 && j >= 4) ? t1 : t0;
+      Sel4 sa, sb;
+      select8(word, sa, sb);
+      lookup4(sa, tj, row[j].x, row[j].y);
+      lookup4(sb, tj, row[j].z, row[j].w);
+    }
+    // the previous step's reads of the tile have returned before it is rewritten,
+    // and the new row is in place before any lane reads it transposed
+    __builtin_amdgcn_s_waitcnt(lgkm_imm(0));
+#pragma unroll
+    for (int j = 0; j < CW / 8; ++j) *reinterpret_cast<uint4 *>(tile + lane * SROW + 16 * j) = row[j];
+    __builtin_amdgcn_s_waitcnt(lgkm_imm(0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        // lane 4e + q of the group addresses row 32h + 8kg + e (+4) and columns 16j + 4q .. +3
+        const uint8_t *a = tile + (32 * h + 8 * kg + (col >> 2)) * SROW + (16 * j + 4 * (col & 3)) * 2;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)a);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(a + 4 * SROW));
+        const v4s b8[2] = {lo, hi};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(in.a[h]), __builtin_bit_cast(bf16x8, b8),
+                                                         acc[j], 0, 0, 0);
+      }
+    }
+  };
+
+  StepIn<CW, BS32> A, B;
+  load_step(wave, A);
+  for (int s = wave; s < nsteps; s += 2 * SW) {
+    load_step(s + SW, B);
+    process(A);
+    load_step(s + 2 * SW, A);
+    if (s + SW < nsteps) process(B);
+  }
+
+  if (LR) {
+    // adapter term V A^T (lr.u = V [M, r], lr.v = A^T [K, r]): rank slices of 32
+    // dealt to the waves; lane group kg takes ranks 32s + 8kg .. +7 (zeros past r)
+    for (int s = wave; 32 * s < lr.r; s += SW) {
+      const int rk = 32 * s + 8 * kg;
+      uint4 av = make_uint4(0u, 0u, 0u, 0u);
+      if (rk < lr.r && col < M) av = *reinterpret_cast<const uint4 *>(lr.u + (int64_t)col * lr.r + rk);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        uint4 bv = make_uint4(0u, 0u, 0u, 0u);
+        if (rk < lr.r) bv = *reinterpret_cast<const uint4 *>(lr.v + (int64_t)(k0 + 16 * j + col) * lr.r + rk);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // the waves' parts through LDS (the tiles are free once every wave is here):
+  // part (w, j) of lane l at f32x4 index (NJ w + j) * 64 + l
+  __syncthreads();
+  f32x4 *red = reinterpret_cast<f32x4 *>(tiles);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) red[(NJ * wave + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  // thread t < 256 NJ: lane l = t % 64, column group j = (t / 64) % NJ, register
+  // i = t / (64 NJ); element (row 4(l/16) + i, column k0 + 16j + l%16)
+  if (threadIdx.x < 256 * NJ) {
+    const int l = threadIdx.x & 63, j = (threadIdx.x >> 6) % NJ, i = (threadIdx.x >> 6) / NJ;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < SW; ++w) sum += red[(NJ * w + j) * 64 + l][i];
+    const int m = 4 * (l >> 4) + i;
+    if (m < M) {
+      const int64_t off = (int64_t)m * K + (int64_t)(k0 + 16 * j + (l & 15));
+      if (dx_bf16)
+        reinterpret_cast<uint16_t *>(dX)[off] = (uint16_t)(pack_bf16x2(sum, 0.f) & 0xffffu);
+      else
+        reinterpret_cast<float *>(dX)[off] = sum;
+    }
+  }
+}
+
+}  // namespace small
+
 }  // namespace
 
 hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
@@ -700,7 +887,25 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
                          hipStream_t stream) {
   const uint16_t *dY = reinterpret_cast<const uint16_t *>(dy);
   const bool has_lr = lr.r > 0;
-  if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
+  if (M >= 1 && M <= small::kMaxRows && N > 0 && N % 8 == 0 && N < ((int64_t)1 << 24) && K < ((int64_t)1 << 24) &&
+      N * K < ((int64_t)1 << 32)) {
+    // at most 16 rows of dY: the weight stream, one workgroup per 64 output columns
+    using namespace small;
+    using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *, int);
+#define NF4_BWDS(CW, DQ, BS32, FP4) {bwd_dx_small_kernel<CW, DQ, BS32, FP4, false>, bwd_dx_small_kernel<CW, DQ, BS32, FP4, true>}
+    static const K_t kern64[2][2][2][2] = {{{NF4_BWDS(64, false, false, false), NF4_BWDS(64, false, false, true)},
+                                            {NF4_BWDS(64, false, true, false), NF4_BWDS(64, false, true, true)}},
+                                           {{NF4_BWDS(64, true, false, false), NF4_BWDS(64, true, false, true)},
+                                            {NF4_BWDS(64, true, true, false), NF4_BWDS(64, true, true, true)}}};
+    static const K_t kern32[2][2][2] = {{NF4_BWDS(32, false, false, false), NF4_BWDS(32, false, false, true)},
+                                        {NF4_BWDS(32, true, false, false), NF4_BWDS(32, true, false, true)}};
+#undef NF4_BWDS
+    const int cw = K / 64 >= kSmallWideBands ? 64 : 32;
+    const K_t f = cw == 64 ? kern64[src.dq ? 1 : 0][src.lbs == 5 ? 1 : 0][src.qt ? 1 : 0][has_lr ? 1 : 0]
+                           : kern32[src.dq ? 1 : 0][src.qt ? 1 : 0][has_lr ? 1 : 0];
+    hipLaunchKernelGGL(f, dim3((unsigned)(K / cw)), dim3(64 * SW), 0, stream, dY, (int)M, N, K, packed, src, lr, dx,
+                       dx_is_bf16);
+  } else if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
     // 16-byte dY rows: buffer-to-LDS dY tiles, transposing weight reads, one wave per SIMD
     using namespace tr_kernel;
     using K_t = void (*)(const uint16_t *, int64_t, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *,

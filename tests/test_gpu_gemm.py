@@ -162,6 +162,30 @@ def test_small_m_every_row_count(N, K):
         assert_gemm_within_bound(Y, O.matmul_fwd(x, wh), O.fwd_bound(x, wh), f"small M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K", [(1000, 2048), (8, 64), (4104, 192)])
+def test_small_m_backward_every_row_count(N, K):
+    """M = 1 .. 16 rows of dY on one weight: the small-M backward (one workgroup per 64 output
+    columns, 64-row steps over N dealt to 16 waves); N = 1000 and 4104 end in a partial step and
+    leave some waves without a step, N = 8 is a single partial step, K = 64 a single workgroup."""
+    dg = lib()
+    d = dev()
+    W = synth.normal((N, K), 0.02, 3 * N + K, torch.bfloat16)
+    q = dg.nf4_quantize(W.to(d))
+    wh = _oracle_what(W).astype(np.float64)
+    for M in range(1, 17):
+        note(f"small-M bwd M={M} N={N} K={K}")
+        dY = synth.normal((M, N), 1.0, 200 * M + N)
+        dYd = dY.to(d)
+        dX = dg.nf4_matmul_bwd_dx(dYd, q)
+        dX16 = dg.nf4_matmul_bwd_dx(dYd, q, torch.bfloat16)
+        again = dg.nf4_matmul_bwd_dx(dYd, q)
+        torch.cuda.synchronize()
+        assert torch.equal(dX, again), "deterministic"
+        assert np.array_equal(bf16_bits(dX16), O.f32_to_bf16_bits(dX.cpu().numpy()))
+        dy = dY.float().numpy()
+        assert_gemm_within_bound(dX, O.matmul_bwd_dx(dy, wh), O.bwd_dx_bound(dy, wh), f"small bwd M={M} N={N} K={K}")
+
+
 @pytest.fixture(scope="module")
 def prefill():
     dg = lib()
