@@ -11,9 +11,10 @@
 // (whose operands hold eight consecutive reduction indices per lane).
 //
 // Three kernels:
-//   bwd_dx_small_kernel    at most 16 rows of dY, N % 8 == 0 and N < 2^24: one
-//                          workgroup per 64 output columns streams the whole
-//                          weight chunk, 16 waves taking 64-row steps in turn.
+//   bwd_dx_small_kernel    up to 16 rows of dY (more as grid rows of 16 while
+//                          cheaper), N % 8 == 0 and N < 2^24: one workgroup per
+//                          32 or 64 output columns streams the whole weight
+//                          band, 16 waves taking 64-row steps in turn.
 //   bwd_dx_wide_kernel     otherwise, N % 8 == 0 (16-byte dY rows) and N < 2^24: dY
 //                          through buffer-to-LDS loads, each wave dequantizes
 //                          its own 64 weight columns row by row into a private
@@ -720,7 +721,8 @@ namespace small {
 
 constexpr int SW = 16;                  // waves per workgroup, four per SIMD
 constexpr int SR = 64;                  // weight rows per wave step, one per lane
-constexpr int kMaxRows = 16;            // rows of dY (the MFMA's 16 A rows)
+constexpr int kMaxRows = 16;            // rows of dY per grid row (the MFMA's 16 A rows)
+constexpr int kMaxGridRows = 16;        // grid rows considered (M up to 256, one M tile of the 256x256 kernel)
 constexpr int64_t kSmallWideBands = 129;   // 64-column bands from this many on (else 32: K/32 <= 256 workgroups)
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -746,6 +748,14 @@ __global__ __launch_bounds__(64 * SW) void bwd_dx_small_kernel(const uint16_t *_
   constexpr int SROW = 2 * CW + 16;     // LDS tile row: CW bf16 + 16 bytes of padding
   constexpr int STILE = SR * SROW;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[SW * STILE > SW * NJ * 64 * 16 ? SW * STILE : SW * NJ * 64 * 16];
+  {
+    // more than 16 rows: grid row y takes rows 16y .. 16y + 15 of dY (and of V and dX)
+    const int m0 = kMaxRows * (int)blockIdx.y;
+    dY += (int64_t)m0 * N;
+    lr.u += (int64_t)m0 * lr.r;
+    dX = reinterpret_cast<uint8_t *>(dX) + (int64_t)m0 * K * (dx_bf16 ? 2 : 4);
+    M = M - m0 < kMaxRows ? M - m0 : kMaxRows;
+  }
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
   // bands sharing a 128-byte line of codes go to workgroups of one XCD
@@ -887,9 +897,21 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
                          hipStream_t stream) {
   const uint16_t *dY = reinterpret_cast<const uint16_t *>(dy);
   const bool has_lr = lr.r > 0;
-  if (M >= 1 && M <= small::kMaxRows && N > 0 && N % 8 == 0 && N < ((int64_t)1 << 24) && K < ((int64_t)1 << 24) &&
-      N * K < ((int64_t)1 << 32)) {
-    // at most 16 rows of dY: the weight stream, one workgroup per 64 output columns
+  const bool small_fits = M >= 1 && M <= small::kMaxGridRows * small::kMaxRows && N > 0 && N % 8 == 0 &&
+                          N < ((int64_t)1 << 24) && K < ((int64_t)1 << 24) && N * K < ((int64_t)1 << 32);
+  const int cw = K / 64 >= small::kSmallWideBands ? 64 : 32;
+  bool use_small = small_fits && M <= small::kMaxRows;
+  if (small_fits && !use_small) {
+    // more rows: each grid row of 16 re-streams the weight.  Both kernels' times grow
+    // with N; per 256 workgroups (one round on the chip) the small kernel measured
+    // ~12 us (32-column bands) or ~20 us (64) per 4096 rows, the 256x256 kernel (one
+    // M tile below 257 rows) ~95 us per round of its K/256 tiles.
+    const int64_t rounds_small = ((K / cw) * ((M + small::kMaxRows - 1) / small::kMaxRows) + 255) / 256;
+    const int64_t rounds_wide = ((K + 255) / 256 + 255) / 256;
+    use_small = rounds_small * (cw == 64 ? 5 : 3) <= rounds_wide * 23;
+  }
+  if (use_small) {
+    // the weight stream, one workgroup per 32 or 64 output columns and grid row
     using namespace small;
     using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *, int);
 #define NF4_BWDS(CW, DQ, BS32, FP4) {bwd_dx_small_kernel<CW, DQ, BS32, FP4, false>, bwd_dx_small_kernel<CW, DQ, BS32, FP4, true>}
@@ -900,11 +922,10 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
     static const K_t kern32[2][2][2] = {{NF4_BWDS(32, false, false, false), NF4_BWDS(32, false, false, true)},
                                         {NF4_BWDS(32, true, false, false), NF4_BWDS(32, true, false, true)}};
 #undef NF4_BWDS
-    const int cw = K / 64 >= kSmallWideBands ? 64 : 32;
     const K_t f = cw == 64 ? kern64[src.dq ? 1 : 0][src.lbs == 5 ? 1 : 0][src.qt ? 1 : 0][has_lr ? 1 : 0]
                            : kern32[src.dq ? 1 : 0][src.qt ? 1 : 0][has_lr ? 1 : 0];
-    hipLaunchKernelGGL(f, dim3((unsigned)(K / cw)), dim3(64 * SW), 0, stream, dY, (int)M, N, K, packed, src, lr, dx,
-                       dx_is_bf16);
+    hipLaunchKernelGGL(f, dim3((unsigned)(K / cw), (unsigned)((M + kMaxRows - 1) / kMaxRows)), dim3(64 * SW), 0,
+                       stream, dY, (int)M, N, K, packed, src, lr, dx, dx_is_bf16);
   } else if (N % 8 == 0 && N < ((int64_t)1 << 24)) {
     // 16-byte dY rows: buffer-to-LDS dY tiles, transposing weight reads, one wave per SIMD
     using namespace tr_kernel;

@@ -186,6 +186,31 @@ def test_small_m_backward_every_row_count(N, K):
         assert_gemm_within_bound(dX, O.matmul_bwd_dx(dy, wh), O.bwd_dx_bound(dy, wh), f"small bwd M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 1000, 2048), (33, 520, 4096), (100, 1000, 2048), (224, 264, 4096),
+                                   (40, 4104, 11008)])
+def test_small_m_backward_grid_rows(M, N, K):
+    """Above 16 rows of dY the small-M backward gives each 16 rows a grid row of their own while
+    its estimated time stays below the 256x256 kernel's (a last grid row of one row at 17 and
+    33, 64-column bands at K = 11008); every element against the oracle, bf16 the one rounding
+    of fp32, reruns bitwise identical."""
+    note(f"small-M bwd grid rows M={M} N={N} K={K}")
+    dg = lib()
+    d = dev()
+    W = synth.normal((N, K), 0.02, 5 * M + N, torch.bfloat16)
+    dY = synth.normal((M, N), 1.0, 7 * M + K)
+    q = dg.nf4_quantize(W.to(d))
+    dYd = dY.to(d)
+    dX = dg.nf4_matmul_bwd_dx(dYd, q)
+    dX16 = dg.nf4_matmul_bwd_dx(dYd, q, torch.bfloat16)
+    again = dg.nf4_matmul_bwd_dx(dYd, q)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, again)
+    assert np.array_equal(bf16_bits(dX16), O.f32_to_bf16_bits(dX.cpu().numpy()))
+    wh = _oracle_what(W).astype(np.float64)
+    dy = dY.float().numpy()
+    assert_gemm_within_bound(dX, O.matmul_bwd_dx(dy, wh), O.bwd_dx_bound(dy, wh), f"grid rows bwd M={M} N={N} K={K}")
+
+
 @pytest.fixture(scope="module")
 def prefill():
     dg = lib()
