@@ -701,22 +701,25 @@ __global__ __launch_bounds__(64 * NWAVE_W) __attribute__((amdgpu_waves_per_eu(1,
 //
 // For at most 16 rows of dY the 256x256 kernels above would leave 15/16 of
 // every MFMA idle and launch one workgroup per 256 output columns; here the
-// work is the weight stream.  Workgroup b owns the 64 output columns
-// k0 = 64b .. +63 (one 64-element chunk of every weight row) over all N rows
-// of the reduction; its 16 waves (four per SIMD) take steps of 64 weight rows
-// in turn (wave w: steps w, w + 16, ...).  In a step lane l dequantizes row
-// 64s + l of the chunk -- one table per 64 weights (two at block size 32) --
-// and writes the 64 bf16 values as one row of the wave's own LDS tile; the
-// transposing read ds_read_b64_tr_b16 then hands each lane eight consecutive
-// rows of one column (within a 16-lane group, output lane i element e is
-// element i%4 of the 8 bytes addressed by lane 4e + i/4), the B operand of
-// MFMA 16x16x32 whose A operand is dY (lane l: row l%16, the same eight
-// reduction indices 8(l/16) .. +7 of a 32-row half).  Rows of dY past M and
-// reduction indices past N load zeros (buffer descriptor), so the weight rows
-// past N (read clamped to the last row) add exact zeros.  The next step's
-// codes, absmax state and dY fragments are loaded before the current step is
-// dequantized.  At the end the 16 waves' partial sums meet in LDS and each
-// thread adds one output element's 16 parts in wave order (deterministic).
+// work is the weight stream.  Workgroup b owns a band of CW output columns
+// (CW = 32, or 64 when there are enough bands to fill the chip) over all N
+// rows of the reduction, and grid row y the dY rows 16y .. 16y + 15 (more
+// rows than 16: the weight is streamed once per grid row); bands that share a
+// 128-byte line of codes run on one XCD.  The 16 waves (four per SIMD) take
+// steps of 64 weight rows in turn (wave w: steps w, w + 16, ...).  In a step
+// lane l dequantizes row 64s + l of the band -- one table per row (two at
+// block size 32 with CW = 64) -- and writes the CW bf16 values as one row of
+// the wave's own LDS tile; the transposing read ds_read_b64_tr_b16 then hands
+// each lane eight consecutive rows of one column (within a 16-lane group,
+// output lane i element e is element i%4 of the 8 bytes addressed by lane
+// 4e + i/4), the B operand of MFMA 16x16x32 whose A operand is dY (lane l:
+// row l%16, the same eight reduction indices 8(l/16) .. +7 of a 32-row half).
+// Rows of dY past M and reduction indices past N load zeros (buffer
+// descriptor), so the weight rows past N (read clamped to the last row) add
+// exact zeros.  The next step's codes, absmax state and dY fragments are
+// loaded before the current step is dequantized.  At the end the 16 waves'
+// partial sums meet in LDS and each thread adds one output element's 16 parts
+// in wave order (deterministic, and no workspace).
 namespace small {
 
 constexpr int SW = 16;                  // waves per workgroup, four per SIMD
