@@ -726,7 +726,11 @@ constexpr int SW = 16;                  // waves per workgroup, four per SIMD
 constexpr int SR = 64;                  // weight rows per wave step, one per lane
 constexpr int kMaxRows = 16;            // rows of dY per grid row (the MFMA's 16 A rows)
 constexpr int kMaxGridRows = 16;        // grid rows considered (M up to 256, one M tile of the 256x256 kernel)
-constexpr int64_t kSmallWideBands = 129;   // 64-column bands from this many on (else 32: K/32 <= 256 workgroups)
+// Measured time of one round of up to 256 workgroups per 4096 weight rows, in
+// tenths of a microsecond, for a band width (64 or 32 columns), or for the
+// 256x256 kernel (0: one round of its K/256 tiles).  16-column bands took 15 us
+// a round, more than 32-column bands at every shape, and are not used.
+constexpr int64_t band_cost(int cw) { return cw == 64 ? 165 : cw == 32 ? 140 : 950; }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -902,19 +906,26 @@ hipError_t launch_bwd_dx(const void *dy, int64_t M, int64_t N, int64_t K, const 
   const bool has_lr = lr.r > 0;
   const bool small_fits = M >= 1 && M <= small::kMaxGridRows * small::kMaxRows && N > 0 && N % 8 == 0 &&
                           N < ((int64_t)1 << 24) && K < ((int64_t)1 << 24) && N * K < ((int64_t)1 << 32);
-  const int cw = K / 64 >= small::kSmallWideBands ? 64 : 32;
+  // Band width: the one with the least estimated time, rounds of 256 workgroups
+  // times the per-round cost (a partly filled round costs about a full one).
+  const int64_t grid_rows = (M + small::kMaxRows - 1) / small::kMaxRows;
+  int cw = 64;
+  int64_t est = 0;
+  for (const int c : {64, 32}) {
+    const int64_t e = ((K / c) * grid_rows + 255) / 256 * small::band_cost(c);
+    if (c == 64 || e < est) {
+      cw = c;
+      est = e;
+    }
+  }
   bool use_small = small_fits && M <= small::kMaxRows;
   if (small_fits && !use_small) {
-    // more rows: each grid row of 16 re-streams the weight.  Both kernels' times grow
-    // with N; per 256 workgroups (one round on the chip) the small kernel measured
-    // ~12 us (32-column bands) or ~20 us (64) per 4096 rows, the 256x256 kernel (one
-    // M tile below 257 rows) ~95 us per round of its K/256 tiles.
-    const int64_t rounds_small = ((K / cw) * ((M + small::kMaxRows - 1) / small::kMaxRows) + 255) / 256;
+    // more rows: each grid row of 16 re-streams the weight
     const int64_t rounds_wide = ((K + 255) / 256 + 255) / 256;
-    use_small = rounds_small * (cw == 64 ? 5 : 3) <= rounds_wide * 23;
+    use_small = est <= rounds_wide * small::band_cost(0);
   }
   if (use_small) {
-    // the weight stream, one workgroup per 32 or 64 output columns and grid row
+    // the weight stream, one workgroup per band of 32 or 64 output columns and grid row
     using namespace small;
     using K_t = void (*)(const uint16_t *, int, int64_t, int64_t, const uint8_t *, AbsmaxSrc, LowRank, void *, int);
 #define NF4_BWDS(CW, DQ, BS32, FP4) {bwd_dx_small_kernel<CW, DQ, BS32, FP4, false>, bwd_dx_small_kernel<CW, DQ, BS32, FP4, true>}
